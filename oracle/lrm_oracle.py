@@ -1,0 +1,299 @@
+"""CPU oracle of the LRMoE backward hot path, in float64.
+
+TEST INFRASTRUCTURE ONLY.  This package is the independent reference that the GPU library is
+checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it; the GPU product path never calls, links or executes anything here, and
+this package imports nothing from the GPU library.
+
+Sources (cited by page title and section/equation):
+  [LRMoE]  "LRMoE: Demand-Side Load Re-Calibration for Efficient MoE Training on
+           Memory-Constrained Nodes" (Hu et al., arXiv 2610.37720): Sec. 3.1 design overview,
+           Sec. 3.2 Load Recalibration Metric (Prop. 3.1, Eq. (1)-(3)), Sec. 3.3 layerwise load
+           calibration (Algorithm 1, Fig. 4), Sec. 3.4 repacking GEMM, Appendix 7.1 (Eq. (4)-(12)),
+           Appendix 7.2 (Prop. 7.1, Eq. (13)-(16)).
+  [EPMath] "Expert Parallel Math Deep": "Routing as an expectation over a batch" (counts, sum of
+           n_i = T*k) and "Capacity and the exact drop-rate formula" (C = CF*T*k/E).
+
+Every function computes the plain definition: fp64 arithmetic on the exact stored input values
+(bf16 inputs are given as uint16 bit patterns and widened exactly).  Readings where the pages
+leave a step open:
+  * pair index p = t*k + j, slot j in descending-logit order; token t = p // k;
+  * the forward layout of the saved activations phi is expert-major with p ascending inside each
+    expert (the "consistent pair order" of Sec. 3.1/3.3);
+  * quota policy q_e = n_e (full retention) or min(n_e, floor(num*L / (den*E_loc)), cap) in
+    integer arithmetic, where L is the number of local routed pairs (the pages leave the
+    quota-allocation policy open, Sec. 3.2; this is the capacity form of [EPMath]);
+  * selection is decided on float32 scores (the precision the GPU stores), ranking by score
+    descending and then pair index ascending; kept rows are written in ascending forward-row
+    order;
+  * the compacted weighted cotangent is delta = RNE_dtype(fl32(alpha * g)): one IEEE float32
+    product, then round-to-nearest-even to the storage type (Appendix 7.1, Eq. (5) allows exposing
+    delta instead of g, applying alpha only once);
+  * dW and dphi are produced in float64 here (fp32 on the GPU).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ------------------------------------------------------------------------------------------------
+# element types
+# ------------------------------------------------------------------------------------------------
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 values of stored elements (dtype "f32" or "bf16" given as uint16 bits)."""
+    if dtype == "f32":
+        return np.asarray(a, np.float32).astype(np.float64)
+    if dtype == "bf16":
+        bits = np.asarray(a, np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even); returns uint16 bits.
+
+    bf16 keeps the upper 16 bits of the float32 pattern.  Adding 0x7FFF plus the lowest kept bit
+    and truncating rounds the dropped 16 bits to nearest with ties to the even kept value; a carry
+    out of the mantissa correctly increments the exponent (up to infinity).  Finite inputs only.
+    """
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+# ------------------------------------------------------------------------------------------------
+# a1: routed counts and forward layout
+# ------------------------------------------------------------------------------------------------
+
+
+def routed_counts(topk_idx: np.ndarray, E: int) -> np.ndarray:
+    """n_e = |P_e|, the number of routed pairs of every expert e in [0, E).
+
+    [LRMoE] Algorithm 1, step 1 (N_{l,e} <- |P_{l,e}|); [EPMath] "Routing as an expectation over
+    a batch": each token makes k dispatches, so the counts sum to T*k.
+    """
+    idx = np.asarray(topk_idx).reshape(-1).astype(np.int64)
+    if idx.size and (idx.min() < 0 or idx.max() >= E):
+        raise ValueError("expert id out of range")
+    n = np.zeros(E, np.int64)
+    np.add.at(n, idx, 1)
+    return n
+
+
+def forward_layout(topk_idx: np.ndarray, e_lo: int, E_loc: int):
+    """Forward dispatch layout of the local pairs.
+
+    Returns (row_pair, fwd_off): row_pair lists, expert by expert for e in [e_lo, e_lo+E_loc),
+    the pair indices routed to e in ascending order ([LRMoE] Sec. 3.1 and 3.3: rows are kept in a
+    consistent pair order, grouped by expert); fwd_off[i] is the first row of local expert i and
+    fwd_off[E_loc] = L.
+    """
+    idx = np.asarray(topk_idx).reshape(-1)
+    segs, off = [], [0]
+    for e in range(e_lo, e_lo + E_loc):
+        ps = np.flatnonzero(idx == e).astype(np.int64)        # ascending pair index
+        segs.append(ps)
+        off.append(off[-1] + ps.size)
+    row_pair = np.concatenate(segs) if segs else np.zeros(0, np.int64)
+    return row_pair, np.asarray(off, np.int64)
+
+
+# ------------------------------------------------------------------------------------------------
+# a2: quotas and compacted offsets
+# ------------------------------------------------------------------------------------------------
+
+
+def plan_quotas(n_loc: np.ndarray, policy: dict):
+    """Retention quotas q_e and compacted-segment offsets.
+
+    [LRMoE] Sec. 3.1/3.3: quotas satisfy 0 <= K_e <= N_e and are fixed for the invocation;
+    "starting with full retention" means K_e = N_e.  The cap form follows [EPMath] "Capacity and
+    the exact drop-rate formula": an expert keeps min(n_e, C) rows with C = CF * (mean load),
+    here C = floor(num*L / (den*E_loc)) computed exactly in integers, optionally also capped at an
+    absolute cap.  cmp_off is the exclusive prefix sum of q with the total appended, so segment e
+    occupies rows [cmp_off[e], cmp_off[e+1]) ([LRMoE] Fig. 4: counts R=[3,1,2] give offsets
+    [0,3,4,6]).
+    """
+    n = [int(v) for v in np.asarray(n_loc).reshape(-1)]
+    E_loc = len(n)
+    L = sum(n)
+    if policy.get("full", 0):
+        q = list(n)
+    else:
+        num, den = int(policy["rho_num"]), int(policy["rho_den"])
+        if den <= 0 or num < 0:
+            raise ValueError("bad retention fraction")
+        c = (num * L) // (den * E_loc) if E_loc > 0 else 0
+        cap = int(policy.get("cap_abs", -1))
+        q = [min(v, c) if cap < 0 else min(v, c, cap) for v in n]
+    off = [0]
+    for v in q:
+        off.append(off[-1] + v)
+    return np.asarray(q, np.int64), np.asarray(off, np.int64)
+
+
+# ------------------------------------------------------------------------------------------------
+# a3: Load Recalibration Metric
+# ------------------------------------------------------------------------------------------------
+
+
+def lrm_scores(topk_w, g, phi, row_pair, k: int, dtype: str, chunk: int = 65536) -> np.ndarray:
+    """R_r = alpha_p^2 * ||g_t||_2^2 * ||phi_r||_2^2 for every local forward row r, in float64.
+
+    [LRMoE] Sec. 3.2, Prop. 3.1, Eq. (3) (and Algorithm 1, step 13): the squared Frobenius norm of
+    the pair's FC2 weight-gradient contribution G_u = (alpha_u g_t) phi_u^T, factorised with the
+    rank-one identity of Appendix 7.1, Eq. (11)-(12).  p = row_pair[r], t = p // k.
+    """
+    row_pair = np.asarray(row_pair, np.int64)
+    a = np.asarray(topk_w, np.float32).astype(np.float64)[row_pair]
+    t = row_pair // k
+    gsq = np.empty(g.shape[0], np.float64)
+    for s in range(0, g.shape[0], chunk):
+        gw = widen(g[s:s + chunk], dtype)
+        gsq[s:s + chunk] = (gw * gw).sum(axis=1)
+    psq = np.empty(row_pair.shape[0], np.float64)
+    for s in range(0, row_pair.shape[0], chunk):
+        pw = widen(phi[s:s + chunk], dtype)
+        psq[s:s + chunk] = (pw * pw).sum(axis=1)
+    return a * a * gsq[t] * psq
+
+
+# ------------------------------------------------------------------------------------------------
+# a4: per-expert top-q selection
+# ------------------------------------------------------------------------------------------------
+
+
+def select_top_quota(score32: np.ndarray, fwd_off, quota, row_pair) -> np.ndarray:
+    """Forward rows kept by per-expert TopK(q_e), ascending within each expert, experts in order.
+
+    [LRMoE] Algorithm 1, step 14 and Sec. 3.3: within each logical expert keep the q_e
+    highest-scoring pairs; Appendix 7.2, Prop. 7.1: keeping the largest scores is optimal, and ties
+    at the boundary admit several optimal sets.  The set is made unique by ranking on
+    (score descending, pair index ascending).  Scores are the float32 values the decision is taken
+    on.
+    """
+    s = np.asarray(score32, np.float32).astype(np.float64)
+    row_pair = np.asarray(row_pair, np.int64)
+    out = []
+    for e in range(len(quota)):
+        r0, r1 = int(fwd_off[e]), int(fwd_off[e + 1])
+        q = int(quota[e])
+        if q < 0 or q > r1 - r0:
+            raise ValueError("quota outside [0, n_e]")
+        rows = np.arange(r0, r1, dtype=np.int64)
+        order = np.lexsort((row_pair[rows], -s[rows]))      # primary: -score; then pair index
+        out.append(np.sort(rows[order[:q]]))
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+# ------------------------------------------------------------------------------------------------
+# a5: physical compaction
+# ------------------------------------------------------------------------------------------------
+
+
+def compact(sel_row, row_pair, topk_w, g, phi, k: int, dtype: str):
+    """Gather the retained rows into contiguous expert-major buffers.
+
+    [LRMoE] Sec. 3.3/3.4 and Fig. 4 (mask -> pack -> counts/offsets): retained gradient rows and
+    their matching saved activations are packed in pair order.  Row i of the output belongs to the
+    forward row r = sel_row[i] with pair p = row_pair[r] and token t = p // k:
+        Gc[i]   = RNE_dtype(fl32(alpha_p * g_t))     (delta_u of Appendix 7.1, Eq. (5))
+        Phic[i] = phi[r]                             (exact copy)
+        sel_pair[i] = p
+    Returns (Gc, Phic, sel_pair) in the storage type (bf16 as uint16 bits).
+    """
+    sel_row = np.asarray(sel_row, np.int64)
+    p = np.asarray(row_pair, np.int64)[sel_row]
+    t = p // k
+    a32 = np.asarray(topk_w, np.float32)[p][:, None]
+    if dtype == "f32":
+        Gc = (a32 * np.asarray(g, np.float32)[t]).astype(np.float32)      # one fp32 product
+    else:
+        g32 = (np.asarray(g, np.uint16)[t].astype(np.uint32) << 16).view(np.float32)
+        Gc = f32_to_bf16_rne(a32 * g32)
+    Phic = np.asarray(phi)[sel_row].copy()
+    return Gc, Phic, p
+
+
+# ------------------------------------------------------------------------------------------------
+# a6 / a7: grouped FC2 gradients over the retained rows
+# ------------------------------------------------------------------------------------------------
+
+
+def grouped_dw(Gc, Phic, cmp_off, dtype: str) -> np.ndarray:
+    """dW_e = sum over retained rows i of expert e of delta_i phi_i^T  (shape [E_loc, h, d]).
+
+    [LRMoE] Sec. 3.2, Eq. (1) and Appendix 7.1, Eq. (8)-(9): the protected (FC2) weight gradient
+    is the sum of the retained pairs' rank-one contributions; an expert with no retained row gets
+    an all-zero gradient.
+    """
+    D = widen(Gc, dtype)
+    P = widen(Phic, dtype)
+    E_loc = len(cmp_off) - 1
+    dW = np.zeros((E_loc, D.shape[1], P.shape[1]), np.float64)
+    for e in range(E_loc):
+        s, t = int(cmp_off[e]), int(cmp_off[e + 1])
+        if t > s:
+            dW[e] = D[s:t].T @ P[s:t]
+    return dW
+
+
+def grouped_dx(Gc, W, cmp_off, dtype: str) -> np.ndarray:
+    """dphi_i = W_e^T delta_i for every retained row i of expert e (shape [K, d]).
+
+    [LRMoE] Appendix 7.1, Eq. (4)-(7): W_e in R^{d_out x d_in} maps phi_u to the expert output
+    y_u = alpha_u W_e phi_u, so the cotangent of phi_u is W_e^T (alpha_u g_t) = W_e^T delta_u;
+    Sec. 3.3: the retained count is the row dimension of the input-gradient product.
+    """
+    D = widen(Gc, dtype)
+    E_loc = len(cmp_off) - 1
+    out = np.zeros((D.shape[0], W.shape[2]), np.float64)
+    for e in range(E_loc):
+        s, t = int(cmp_off[e]), int(cmp_off[e + 1])
+        if t > s:
+            out[s:t] = D[s:t] @ widen(W[e], dtype)       # row i: sum_j delta_ij W_e[j, :]
+    return out
+
+
+def dw_rows(Gc, Phic, cmp_off, e: int, rows_h, dtype: str) -> np.ndarray:
+    """Rows ``rows_h`` (FC2 output indices) of dW_e, as grouped_dw computes them, in float64."""
+    s, t = int(cmp_off[e]), int(cmp_off[e + 1])
+    rows_h = np.asarray(rows_h, np.int64)
+    if t == s:
+        return np.zeros((rows_h.size, Phic.shape[1]), np.float64)
+    return widen(Gc[s:t][:, rows_h], dtype).T @ widen(Phic[s:t], dtype)
+
+
+def dx_rows(Gc, W, cmp_off, rows_i, dtype: str) -> np.ndarray:
+    """Rows ``rows_i`` (compacted row indices) of dphi, as grouped_dx computes them, in float64."""
+    rows_i = np.asarray(rows_i, np.int64)
+    off = np.asarray(cmp_off, np.int64)
+    e_of = np.searchsorted(off, rows_i, side="right") - 1
+    out = np.zeros((rows_i.size, W.shape[2]), np.float64)
+    for j, (i, e) in enumerate(zip(rows_i, e_of)):
+        out[j] = widen(Gc[i], dtype) @ widen(W[e], dtype)
+    return out
+
+
+# ------------------------------------------------------------------------------------------------
+# whole path
+# ------------------------------------------------------------------------------------------------
+
+
+def run(topk_idx, topk_w, g, phi, W, *, T, k, E, e_lo, E_loc, dtype, policy,
+        gemms: bool = True) -> dict:
+    """Run every step of the path on the CPU and return all intermediate results."""
+    n = routed_counts(topk_idx, E)
+    row_pair, fwd_off = forward_layout(topk_idx, e_lo, E_loc)
+    quota, cmp_off = plan_quotas(n[e_lo:e_lo + E_loc], policy)
+    R = lrm_scores(topk_w, g, phi, row_pair, k, dtype)
+    score32 = R.astype(np.float32)
+    sel_row = select_top_quota(score32, fwd_off, quota, row_pair)
+    Gc, Phic, sel_pair = compact(sel_row, row_pair, topk_w, g, phi, k, dtype)
+    out = dict(counts=n, row_pair=row_pair, fwd_off=fwd_off, quota=quota, cmp_off=cmp_off,
+               score64=R, score32=score32, sel_row=sel_row, Gc=Gc, Phic=Phic, sel_pair=sel_pair)
+    if gemms:
+        out["dW"] = grouped_dw(Gc, Phic, cmp_off, dtype)
+        out["dphi"] = grouped_dx(Gc, W, cmp_off, dtype)
+    return out
