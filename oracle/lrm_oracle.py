@@ -55,11 +55,13 @@ def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
 
     bf16 keeps the upper 16 bits of the float32 pattern.  Adding 0x7FFF plus the lowest kept bit
     and truncating rounds the dropped 16 bits to nearest with ties to the even kept value; a carry
-    out of the mantissa correctly increments the exponent (up to infinity).  Finite inputs only.
+    out of the mantissa correctly increments the exponent (up to infinity).  Finite inputs only
+    (the largest finite pattern 0xFF7FFFFF plus 0x8000 still fits in 32 bits).
     """
-    u = np.ascontiguousarray(x, np.float32).view(np.uint32).astype(np.uint64)
-    u = u + 0x7FFF + ((u >> 16) & 1)
-    return (u >> 16).astype(np.uint16)
+    u = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    one, half = np.uint32(1), np.uint32(0x7FFF)
+    u = u + half + ((u >> np.uint32(16)) & one)
+    return (u >> np.uint32(16)).astype(np.uint16)
 
 
 # ------------------------------------------------------------------------------------------------
@@ -192,7 +194,7 @@ def select_top_quota(score32: np.ndarray, fwd_off, quota, row_pair) -> np.ndarra
 # ------------------------------------------------------------------------------------------------
 
 
-def compact(sel_row, row_pair, topk_w, g, phi, k: int, dtype: str):
+def compact(sel_row, row_pair, topk_w, g, phi, k: int, dtype: str, chunk: int = 8192):
     """Gather the retained rows into contiguous expert-major buffers.
 
     [LRMoE] Sec. 3.3/3.4 and Fig. 4 (mask -> pack -> counts/offsets): retained gradient rows and
@@ -207,11 +209,14 @@ def compact(sel_row, row_pair, topk_w, g, phi, k: int, dtype: str):
     p = np.asarray(row_pair, np.int64)[sel_row]
     t = p // k
     a32 = np.asarray(topk_w, np.float32)[p][:, None]
-    if dtype == "f32":
-        Gc = (a32 * np.asarray(g, np.float32)[t]).astype(np.float32)      # one fp32 product
-    else:
-        g32 = (np.asarray(g, np.uint16)[t].astype(np.uint32) << 16).view(np.float32)
-        Gc = f32_to_bf16_rne(a32 * g32)
+    Gc = np.empty((sel_row.size, g.shape[1]), np.float32 if dtype == "f32" else np.uint16)
+    for s in range(0, sel_row.size, chunk):        # row blocks only bound the temporaries
+        rows = slice(s, s + chunk)
+        if dtype == "f32":
+            Gc[rows] = a32[rows] * np.asarray(g, np.float32)[t[rows]]       # one fp32 product
+        else:
+            g32 = (np.asarray(g, np.uint16)[t[rows]].astype(np.uint32) << 16).view(np.float32)
+            Gc[rows] = f32_to_bf16_rne(a32[rows] * g32)
     Phic = np.asarray(phi)[sel_row].copy()
     return Gc, Phic, p
 
