@@ -1,0 +1,154 @@
+// Host side of the C ABI declared in include/lrm.h: argument validation, workspace layout and
+// kernel launches.  No allocation, no synchronisation (except lrm_read_device_error).
+#include <stdint.h>
+
+#include "lrm_internal.hpp"
+
+using lrm::WsLayout;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+lrm_status check_problem(const lrm_problem* p) {
+  if (!p) return LRM_ERR_INVALID_ARGUMENT;
+  if (p->T <= 0 || p->k <= 0 || p->E <= 0 || p->E_loc <= 0 || p->h <= 0 || p->d <= 0)
+    return LRM_ERR_INVALID_ARGUMENT;
+  if (p->k > p->E || p->e_lo < 0 || (int64_t)p->e_lo + p->E_loc > p->E)
+    return LRM_ERR_INVALID_ARGUMENT;
+  if (p->L_cap <= 0 || p->K_cap <= 0) return LRM_ERR_INVALID_ARGUMENT;
+  if ((int64_t)p->T * p->k > INT32_MAX) return LRM_ERR_UNSUPPORTED;
+  if (p->dtype != LRM_F32 && p->dtype != LRM_BF16) return LRM_ERR_UNSUPPORTED;
+  if (p->h % 8 != 0 || p->d % 8 != 0) return LRM_ERR_UNSUPPORTED;
+  if (p->E > 4096 || p->E_loc > 1024) return LRM_ERR_UNSUPPORTED;
+  return LRM_OK;
+}
+
+lrm_status check_ws(const lrm_problem* p, const void* ws, size_t ws_bytes, WsLayout* wl) {
+  if (!ws) return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(ws)) return LRM_ERR_UNSUPPORTED;
+  *wl = lrm::ws_layout(*p);
+  if (ws_bytes < wl->total) return LRM_ERR_WORKSPACE_TOO_SMALL;
+  return LRM_OK;
+}
+
+lrm_status from_hip(hipError_t e) { return e == hipSuccess ? LRM_OK : LRM_ERR_HIP; }
+
+}  // namespace
+
+#define LRM_TRY(expr)                  \
+  do {                                 \
+    const lrm_status _s = (expr);      \
+    if (_s != LRM_OK) return _s;       \
+  } while (0)
+
+extern "C" {
+
+size_t lrm_workspace_bytes(const lrm_problem* problem) {
+  if (check_problem(problem) != LRM_OK) return 0;
+  return lrm::ws_layout(*problem).total;
+}
+
+lrm_status lrm_plan_quotas(const lrm_problem* problem, const lrm_quota_policy* policy,
+                           const int32_t* topk_idx, int32_t* counts, int32_t* fwd_off,
+                           int32_t* row_pair, int32_t* quota, int32_t* cmp_off, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!policy || !topk_idx || !counts || !fwd_off || !row_pair || !quota || !cmp_off)
+    return LRM_ERR_INVALID_ARGUMENT;
+  if (!policy->full && (policy->rho_den <= 0 || policy->rho_num < 0))
+    return LRM_ERR_INVALID_ARGUMENT;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_plan(*problem, *policy, topk_idx, counts, fwd_off, row_pair, quota,
+                                   cmp_off, (char*)ws, wl, stream));
+}
+
+lrm_status lrm_score(const lrm_problem* problem, const float* topk_w, const void* g,
+                     const void* phi, const int32_t* row_pair, const int32_t* fwd_off,
+                     float* score, void* ws, size_t ws_bytes, hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!topk_w || !g || !phi || !row_pair || !fwd_off || !score) return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(g) || !aligned16(phi)) return LRM_ERR_UNSUPPORTED;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_score(*problem, topk_w, g, phi, row_pair, fwd_off, score, (char*)ws,
+                                    wl, stream));
+}
+
+lrm_status lrm_select(const lrm_problem* problem, const float* score, const int32_t* fwd_off,
+                      const int32_t* quota, const int32_t* cmp_off, int32_t* sel_row, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!score || !fwd_off || !quota || !cmp_off || !sel_row) return LRM_ERR_INVALID_ARGUMENT;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_select(*problem, score, fwd_off, quota, cmp_off, sel_row, (char*)ws,
+                                     wl, stream));
+}
+
+lrm_status lrm_compact(const lrm_problem* problem, const int32_t* sel_row, const int32_t* row_pair,
+                       const int32_t* cmp_off, const float* topk_w, const void* g,
+                       const void* phi, void* Gc, void* Phic, int32_t* sel_pair, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!sel_row || !row_pair || !cmp_off || !topk_w || !g || !phi || !Gc || !Phic || !sel_pair)
+    return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(g) || !aligned16(phi) || !aligned16(Gc) || !aligned16(Phic))
+    return LRM_ERR_UNSUPPORTED;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_compact(*problem, sel_row, row_pair, cmp_off, topk_w, g, phi, Gc,
+                                      Phic, sel_pair, (char*)ws, wl, stream));
+}
+
+lrm_status lrm_grouped_dw(const lrm_problem* problem, const void* Gc, const void* Phic,
+                          const int32_t* cmp_off, float* dW, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!Gc || !Phic || !cmp_off || !dW) return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(Gc) || !aligned16(Phic) || !aligned16(dW)) return LRM_ERR_UNSUPPORTED;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_dw(*problem, Gc, Phic, cmp_off, dW, (char*)ws, wl, stream));
+}
+
+lrm_status lrm_grouped_dx(const lrm_problem* problem, const void* Gc, const void* W,
+                          const int32_t* cmp_off, float* dphi, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!Gc || !W || !cmp_off || !dphi) return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(Gc) || !aligned16(W) || !aligned16(dphi)) return LRM_ERR_UNSUPPORTED;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_dx(*problem, Gc, W, cmp_off, dphi, (char*)ws, wl, stream));
+}
+
+lrm_status lrm_read_device_error(void* ws, int32_t* code, int32_t clear, hipStream_t stream) {
+  if (!ws || !code) return LRM_ERR_INVALID_ARGUMENT;
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, ws, sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return LRM_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return LRM_ERR_HIP;
+  *code = v;
+  if (clear) {
+    const int32_t z = 0;
+    if (hipMemcpyAsync(ws, &z, sizeof(z), hipMemcpyHostToDevice, stream) != hipSuccess)
+      return LRM_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return LRM_ERR_HIP;
+  }
+  return LRM_OK;
+}
+
+const char* lrm_status_string(lrm_status status) {
+  switch (status) {
+    case LRM_OK: return "ok";
+    case LRM_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case LRM_ERR_UNSUPPORTED: return "unsupported problem or alignment";
+    case LRM_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case LRM_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Internal declarations shared by the host glue and the kernel translation units of liblrm.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/lrm.h"
+
+namespace lrm {
+
+// Pairs handled by one wavefront in the counting passes of lrm_plan_quotas.
+constexpr int kPlanChunk = 1024;
+// Row tile of the grouped input-gradient GEMM (rows of one expert segment per tile).
+constexpr int kDxTileM = 128;
+
+// Layout of the caller-provided workspace (byte offsets, all 256-byte aligned).
+struct WsLayout {
+  size_t err;     // int32 error word, then reserved header words
+  size_t hist;    // int32 [nchunks][E]   per-chunk expert histograms / local prefixes
+  size_t gnorm;   // double [T]           ||g_t||^2
+  size_t tiles;   // int32 [1 + 2*max_tiles] dx tile table: count, then (expert, row0) pairs
+  size_t total;
+  int64_t nchunks;
+  int64_t max_tiles;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline WsLayout ws_layout(const lrm_problem& p) {
+  WsLayout w{};
+  const int64_t P = (int64_t)p.T * p.k;
+  w.nchunks = (P + kPlanChunk - 1) / kPlanChunk;
+  w.max_tiles = ((int64_t)p.K_cap + kDxTileM - 1) / kDxTileM + p.E_loc;
+  size_t off = 0;
+  w.err = off;
+  off += 256;
+  w.hist = off;
+  off = align_up(off + (size_t)w.nchunks * p.E * 4, 256);
+  w.gnorm = off;
+  off = align_up(off + (size_t)p.T * 8, 256);
+  w.tiles = off;
+  off = align_up(off + (size_t)(1 + 2 * w.max_tiles) * 4, 256);
+  w.total = off;
+  return w;
+}
+
+// Kernel launchers (one per translation unit).  Each returns the hipError_t of its launches.
+hipError_t launch_plan(const lrm_problem& p, const lrm_quota_policy& pol, const int32_t* topk_idx,
+                       int32_t* counts, int32_t* fwd_off, int32_t* row_pair, int32_t* quota,
+                       int32_t* cmp_off, char* ws, const WsLayout& wl, hipStream_t s);
+hipError_t launch_score(const lrm_problem& p, const float* topk_w, const void* g, const void* phi,
+                        const int32_t* row_pair, const int32_t* fwd_off, float* score, char* ws,
+                        const WsLayout& wl, hipStream_t s);
+hipError_t launch_select(const lrm_problem& p, const float* score, const int32_t* fwd_off,
+                         const int32_t* quota, const int32_t* cmp_off, int32_t* sel_row, char* ws,
+                         const WsLayout& wl, hipStream_t s);
+hipError_t launch_compact(const lrm_problem& p, const int32_t* sel_row, const int32_t* row_pair,
+                          const int32_t* cmp_off, const float* topk_w, const void* g,
+                          const void* phi, void* Gc, void* Phic, int32_t* sel_pair, char* ws,
+                          const WsLayout& wl, hipStream_t s);
+hipError_t launch_dw(const lrm_problem& p, const void* Gc, const void* Phic, const int32_t* cmp_off,
+                     float* dW, char* ws, const WsLayout& wl, hipStream_t s);
+hipError_t launch_dx(const lrm_problem& p, const void* Gc, const void* W, const int32_t* cmp_off,
+                     float* dphi, char* ws, const WsLayout& wl, hipStream_t s);
+
+}  // namespace lrm

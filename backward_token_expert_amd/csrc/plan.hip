@@ -1,0 +1,225 @@
+// lrm_plan_quotas: routed counts, stable forward layout, quotas and compacted offsets.
+//
+// LRMoE (arXiv 2610.37720) Algorithm 1 step 1 (N_e <- |P_e|), Sec. 3.1/3.3 (quotas fixed before
+// backward, 0 <= K_e <= N_e; rows kept in a consistent pair order grouped by expert), Fig. 4
+// (counts and prefix offsets define the segments).  The quota cap follows the capacity rule
+// C = CF * mean load of "Expert Parallel Math Deep" ("Capacity and the exact drop-rate formula").
+//
+// Four launches, all sizes device-resident (no host round trip, as the TopoEP paper argues for
+// planning in its host-plan latency model):
+//   plan_init    clear the sticky device error word
+//   plan_hist    one wavefront per chunk of kPlanChunk pairs: per-chunk expert histogram
+//   plan_scan    one workgroup: expert totals, per-chunk prefixes, fwd_off, quotas, cmp_off
+//   plan_scatter one wavefront per chunk: stable counting-sort scatter of the local pairs
+// The scatter ranks equal experts inside a wavefront with ballots (a 64-lane "match"), so the
+// layout is stable (pair index ascending within each expert) without any sort.
+#include "lrm_device.hpp"
+#include "lrm_internal.hpp"
+
+namespace lrm {
+namespace {
+
+constexpr int kPlanBlock = 256;                 // 4 wavefronts, one chunk each
+constexpr int kChunksPerBlock = kPlanBlock / kWave;
+constexpr int kMaxE = 4096;
+
+__global__ void plan_init(int32_t* err) {
+  if (threadIdx.x == 0) *err = 0;
+}
+
+__global__ __launch_bounds__(kPlanBlock) void plan_hist(const int32_t* __restrict__ idx, int64_t P,
+                                                        int E, int64_t nchunks,
+                                                        int32_t* __restrict__ hist,
+                                                        int32_t* __restrict__ err) {
+  __shared__ int32_t h[kChunksPerBlock][kMaxE];
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  for (int i = threadIdx.x; i < kChunksPerBlock * E; i += kPlanBlock) h[i / E][i % E] = 0;
+  __syncthreads();
+  const int64_t c = (int64_t)blockIdx.x * kChunksPerBlock + w;
+  bool bad = false;
+  if (c < nchunks) {
+    const int64_t p0 = c * kPlanChunk;
+    for (int r = 0; r < kPlanChunk; r += kWave) {
+      const int64_t p = p0 + r + lane;
+      if (p < P) {
+        const int e = idx[p];
+        if (e >= 0 && e < E) atomicAdd(&h[w][e], 1);
+        else bad = true;
+      }
+    }
+  }
+  if (bad) set_error(err, LRM_DEVERR_EXPERT_ID);
+  __syncthreads();
+  for (int i = threadIdx.x; i < kChunksPerBlock * E; i += kPlanBlock) {
+    const int64_t cc = (int64_t)blockIdx.x * kChunksPerBlock + i / E;
+    if (cc < nchunks) hist[cc * E + i % E] = h[i / E][i % E];
+  }
+}
+
+// Exclusive prefix sum over the 1024 threads of a workgroup; returns the prefix, *total the sum.
+__device__ int block_exclusive_scan_1024(int v, int* sh /* >= 17 ints */, int* total) {
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) sh[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    const int t = lane < 16 ? sh[lane] : 0;
+    const int ti = wave_inclusive_scan(t);
+    if (lane < 16) sh[lane] = ti - t;  // exclusive wave offsets
+    if (lane == 15) sh[16] = ti;
+  }
+  __syncthreads();
+  const int res = sh[w] + inc - v;
+  *total = sh[16];
+  __syncthreads();
+  return res;
+}
+
+__global__ __launch_bounds__(1024) void plan_scan(int32_t* __restrict__ hist, int64_t nchunks,
+                                                  int E, int e_lo, int E_loc, int L_cap, int K_cap,
+                                                  lrm_quota_policy pol, int32_t* __restrict__ counts,
+                                                  int32_t* __restrict__ fwd_off,
+                                                  int32_t* __restrict__ quota,
+                                                  int32_t* __restrict__ cmp_off,
+                                                  int32_t* __restrict__ err) {
+  __shared__ int part[16][64];
+  __shared__ int nloc[1024];
+  __shared__ int sh[32];
+  const int tid = threadIdx.x, sub = tid & 63, grp = tid >> 6;
+  const int64_t cpg = (nchunks + 15) / 16;
+  const int64_t c0 = grp * cpg, c1 = (c0 + cpg < nchunks) ? c0 + cpg : nchunks;
+
+  // Phase A: expert totals; per-chunk exclusive prefixes (in place) for the local experts.
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + sub;
+    int s = 0;
+    if (e < E)
+      for (int64_t c = c0; c < c1; ++c) s += hist[c * E + e];
+    part[grp][sub] = s;
+    __syncthreads();
+    if (tid < 64) {
+      int run = 0;
+      for (int g2 = 0; g2 < 16; ++g2) {
+        const int v = part[g2][tid];
+        part[g2][tid] = run;
+        run += v;
+      }
+      if (e0 + tid < E) {
+        counts[e0 + tid] = run;
+        const int el = e0 + tid - e_lo;
+        if (el >= 0 && el < E_loc) nloc[el] = run;
+      }
+    }
+    __syncthreads();
+    if (e < E && e >= e_lo && e < e_lo + E_loc) {
+      int run = part[grp][sub];
+      for (int64_t c = c0; c < c1; ++c) {
+        const int v = hist[c * E + e];
+        hist[c * E + e] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+  }
+
+  // Phase B: forward offsets (clamped to L_cap), quotas, compacted offsets (clamped to K_cap).
+  const int n = tid < E_loc ? nloc[tid] : 0;
+  int L = 0;
+  const int pre = block_exclusive_scan_1024(n, sh, &L);
+  const int f0 = pre < L_cap ? pre : L_cap;
+  const int f1 = pre + n < L_cap ? pre + n : L_cap;
+  const int seg = f1 - f0;
+  const int Lc = L < L_cap ? L : L_cap;
+  if (tid < E_loc) fwd_off[tid] = f0;
+  if (tid == 0) {
+    fwd_off[E_loc] = Lc;
+    if (L > L_cap) set_error(err, LRM_DEVERR_L_CAP);
+  }
+  int q = 0;
+  if (tid < E_loc) {
+    if (pol.full) {
+      q = seg;
+    } else {
+      const int64_t c = ((int64_t)pol.rho_num * Lc) / ((int64_t)pol.rho_den * E_loc);
+      int64_t qq = seg < c ? seg : c;
+      if (pol.cap_abs >= 0 && qq > pol.cap_abs) qq = pol.cap_abs;
+      q = (int)qq;
+    }
+  }
+  int K = 0;
+  const int cpre = block_exclusive_scan_1024(q, sh, &K);
+  const int o0 = cpre < K_cap ? cpre : K_cap;
+  const int o1 = cpre + q < K_cap ? cpre + q : K_cap;
+  if (tid < E_loc) {
+    cmp_off[tid] = o0;
+    quota[tid] = o1 - o0;
+  }
+  if (tid == 0) {
+    cmp_off[E_loc] = K < K_cap ? K : K_cap;
+    if (K > K_cap) set_error(err, LRM_DEVERR_K_CAP);
+  }
+}
+
+__global__ __launch_bounds__(kPlanBlock) void plan_scatter(const int32_t* __restrict__ idx,
+                                                           int64_t P, int E, int e_lo, int E_loc,
+                                                           int nbits, int64_t nchunks,
+                                                           const int32_t* __restrict__ hist,
+                                                           const int32_t* __restrict__ fwd_off,
+                                                           int32_t* __restrict__ row_pair) {
+  __shared__ int base[kChunksPerBlock][1024];
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int64_t c = (int64_t)blockIdx.x * kChunksPerBlock + w;
+  if (c >= nchunks) return;  // whole wavefront leaves; no block barrier follows
+  for (int i = lane; i < E_loc; i += kWave) base[w][i] = fwd_off[i] + hist[c * E + e_lo + i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t lt = lanemask_lt();
+  const int64_t p0 = c * kPlanChunk;
+  for (int r = 0; r < kPlanChunk; r += kWave) {
+    const int64_t p = p0 + r + lane;
+    int e = p < P ? idx[p] : -1;
+    const bool local = e >= e_lo && e < e_lo + E_loc;
+    const int el = local ? e - e_lo : 0;
+    uint64_t peers = ballot(local);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (el >> b) & 1;
+      const uint64_t m = ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const int leader = local ? __builtin_ctzll(peers) : lane;
+    int old = 0;
+    if (local && leader == lane) {
+      old = base[w][el];
+      base[w][el] = old + __builtin_popcountll(peers);
+    }
+    old = __shfl(old, leader, kWave);
+    if (local) {
+      const int row = old + __builtin_popcountll(peers & lt);
+      if (row < fwd_off[el + 1]) row_pair[row] = (int32_t)p;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const lrm_problem& p, const lrm_quota_policy& pol, const int32_t* topk_idx,
+                       int32_t* counts, int32_t* fwd_off, int32_t* row_pair, int32_t* quota,
+                       int32_t* cmp_off, char* ws, const WsLayout& wl, hipStream_t s) {
+  int32_t* err = (int32_t*)(ws + wl.err);
+  int32_t* hist = (int32_t*)(ws + wl.hist);
+  const int64_t P = (int64_t)p.T * p.k;
+  const unsigned nblk = (unsigned)((wl.nchunks + kChunksPerBlock - 1) / kChunksPerBlock);
+  int nbits = 0;
+  while ((1 << nbits) < p.E_loc) ++nbits;
+  hipLaunchKernelGGL(plan_init, dim3(1), dim3(64), 0, s, err);
+  hipLaunchKernelGGL(plan_hist, dim3(nblk), dim3(kPlanBlock), 0, s, topk_idx, P, p.E, wl.nchunks,
+                     hist, err);
+  hipLaunchKernelGGL(plan_scan, dim3(1), dim3(1024), 0, s, hist, wl.nchunks, p.E, p.e_lo, p.E_loc,
+                     p.L_cap, p.K_cap, pol, counts, fwd_off, quota, cmp_off, err);
+  hipLaunchKernelGGL(plan_scatter, dim3(nblk), dim3(kPlanBlock), 0, s, topk_idx, P, p.E, p.e_lo,
+                     p.E_loc, nbits, wl.nchunks, hist, fwd_off, row_pair);
+  return hipGetLastError();
+}
+
+}  // namespace lrm

@@ -1,0 +1,148 @@
+// lrm_score: Load Recalibration Metric of every local forward row.
+//
+// LRMoE (arXiv 2610.37720) Sec. 3.2, Prop. 3.1, Eq. (3) and Algorithm 1 step 13:
+//   R_u = alpha_u^2 * ||g_t||_2^2 * ||phi_u||_2^2,
+// the squared Frobenius norm of the pair's FC2 weight-gradient contribution (alpha_u g_t) phi_u^T,
+// evaluated without materialising it (rank-one identity, Appendix 7.1 Eq. (11)-(12)).
+//
+// Two streaming launches, HBM-bound (about 2 flops per loaded element):
+//   token_sqnorm  ||g_t||^2 for all T tokens (one wavefront per row, 16-byte loads)
+//   row_score     ||phi_r||^2 per forward row, then the product with alpha^2 and ||g_t||^2
+// Squares of bf16/fp32 values are exact in float64, and the sums are accumulated in float64 with
+// a fixed lane assignment and a fixed butterfly, so two rows with equal contents give bitwise
+// equal scores wherever they sit; the final product is rounded once to float32.
+#include "lrm_device.hpp"
+#include "lrm_internal.hpp"
+
+namespace lrm {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// Sum of squares of one row of `chunks` 16-byte chunks, accumulated by this lane, in float64.
+template <bool kBF16>
+__device__ __forceinline__ double lane_sqsum(const uint4* __restrict__ row, int chunks) {
+  double acc = 0.0;
+  const int lane = lane_id();
+  int c = lane;
+  // Two chunks in flight per lane per step.
+  for (; c + kWave < chunks; c += 2 * kWave) {
+    const uint4 a = load_nt(row + c);
+    const uint4 b = load_nt(row + c + kWave);
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+    const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (kBF16) {
+        const double x0 = bf16_lo(wa[i]), x1 = bf16_hi(wa[i]);
+        acc += x0 * x0;
+        acc += x1 * x1;
+      } else {
+        const double x = __uint_as_float(wa[i]);
+        acc += x * x;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (kBF16) {
+        const double x0 = bf16_lo(wb[i]), x1 = bf16_hi(wb[i]);
+        acc += x0 * x0;
+        acc += x1 * x1;
+      } else {
+        const double x = __uint_as_float(wb[i]);
+        acc += x * x;
+      }
+    }
+  }
+  if (c < chunks) {
+    const uint4 a = load_nt(row + c);
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (kBF16) {
+        const double x0 = bf16_lo(wa[i]), x1 = bf16_hi(wa[i]);
+        acc += x0 * x0;
+        acc += x1 * x1;
+      } else {
+        const double x = __uint_as_float(wa[i]);
+        acc += x * x;
+      }
+    }
+  }
+  return acc;
+}
+
+template <bool kBF16>
+__global__ __launch_bounds__(kBlock) void token_sqnorm(const uint4* __restrict__ g, int T,
+                                                       int chunks, double* __restrict__ gnorm) {
+  const int lane = lane_id();
+  const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
+  for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; t < T; t += nw) {
+    const double s = wave_sum(lane_sqsum<kBF16>(g + t * chunks, chunks));
+    if (lane == 0) gnorm[t] = s;
+  }
+}
+
+template <bool kBF16>
+__global__ __launch_bounds__(kBlock) void row_score(const uint4* __restrict__ phi, int chunks,
+                                                    const int32_t* __restrict__ fwd_off, int E_loc,
+                                                    int L_cap, const int32_t* __restrict__ row_pair,
+                                                    const float* __restrict__ topk_w, int k,
+                                                    int64_t P, const double* __restrict__ gnorm,
+                                                    float* __restrict__ score,
+                                                    int32_t* __restrict__ err) {
+  const int lane = lane_id();
+  int L = fwd_off[E_loc];
+  L = L < 0 ? 0 : (L > L_cap ? L_cap : L);
+  const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
+  int bad = 0;
+  for (int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; r < L; r += nw) {
+    const int p = row_pair[r];
+    const double s = wave_sum(lane_sqsum<kBF16>(phi + r * chunks, chunks));
+    if (lane == 0) {
+      float out = 0.0f;
+      if (p < 0 || p >= P) {
+        bad |= LRM_DEVERR_INDEX;
+      } else {
+        const double a = (double)topk_w[p];
+        out = (float)(((a * a) * gnorm[p / k]) * s);
+        // Scores are products of squares: anything but a finite value >= +0 is an input error.
+        if (!(out >= 0.0f && out <= 3.402823466e38f)) bad |= LRM_DEVERR_NONFINITE;
+      }
+      score[r] = out;
+    }
+  }
+  if (bad) set_error(err, bad);
+}
+
+}  // namespace
+
+hipError_t launch_score(const lrm_problem& p, const float* topk_w, const void* g, const void* phi,
+                        const int32_t* row_pair, const int32_t* fwd_off, float* score, char* ws,
+                        const WsLayout& wl, hipStream_t s) {
+  int32_t* err = (int32_t*)(ws + wl.err);
+  double* gnorm = (double*)(ws + wl.gnorm);
+  const int esz = p.dtype == LRM_BF16 ? 2 : 4;
+  const int gch = p.h * esz / 16, pch = p.d * esz / 16;
+  // Persistent grids: enough wavefronts to keep every CU's memory pipeline full.
+  const int64_t tb = ((int64_t)p.T + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t lb = ((int64_t)p.L_cap + kWavesPerBlock - 1) / kWavesPerBlock;
+  const unsigned gblk = (unsigned)(tb < 4096 ? tb : 4096);
+  const unsigned lblk = (unsigned)(lb < 4096 ? lb : 4096);
+  const int64_t P = (int64_t)p.T * p.k;
+  if (p.dtype == LRM_BF16) {
+    hipLaunchKernelGGL(token_sqnorm<true>, dim3(gblk), dim3(kBlock), 0, s, (const uint4*)g, p.T,
+                       gch, gnorm);
+    hipLaunchKernelGGL(row_score<true>, dim3(lblk), dim3(kBlock), 0, s, (const uint4*)phi, pch,
+                       fwd_off, p.E_loc, p.L_cap, row_pair, topk_w, p.k, P, gnorm, score, err);
+  } else {
+    hipLaunchKernelGGL(token_sqnorm<false>, dim3(gblk), dim3(kBlock), 0, s, (const uint4*)g, p.T,
+                       gch, gnorm);
+    hipLaunchKernelGGL(row_score<false>, dim3(lblk), dim3(kBlock), 0, s, (const uint4*)phi, pch,
+                       fwd_off, p.E_loc, p.L_cap, row_pair, topk_w, p.k, P, gnorm, score, err);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lrm

@@ -1,0 +1,67 @@
+"""Device buffers and the six-call sequence of the hot path (marshalling only).
+
+``DeviceBuffers`` allocates, with PyTorch, every output and the workspace of one problem; ``run``
+enqueues lrm_plan_quotas -> lrm_score -> lrm_select -> lrm_compact -> lrm_grouped_dw ->
+lrm_grouped_dx on one stream.  No step of the path is computed here.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import lrm
+
+
+def storage_dtype(dtype: str):
+    return torch.int16 if dtype == "bf16" else torch.float32
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """Upload a host array; bf16 bit patterns (uint16) travel as int16."""
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_host(t: torch.Tensor, bf16: bool = False) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    return a.view(np.uint16) if bf16 else a
+
+
+class DeviceBuffers:
+    """Outputs and workspace of one problem, sized to its capacities."""
+
+    def __init__(self, problem: lrm.Problem, device="cuda"):
+        p = problem
+        i32 = dict(dtype=torch.int32, device=device)
+        st = storage_dtype("bf16" if p.dtype == lrm.LRM_BF16 else "f32")
+        self.problem = p
+        self.counts = torch.zeros(p.E, **i32)
+        self.fwd_off = torch.zeros(p.E_loc + 1, **i32)
+        self.row_pair = torch.zeros(p.L_cap, **i32)
+        self.quota = torch.zeros(p.E_loc, **i32)
+        self.cmp_off = torch.zeros(p.E_loc + 1, **i32)
+        self.score = torch.zeros(p.L_cap, dtype=torch.float32, device=device)
+        self.sel_row = torch.zeros(p.K_cap, **i32)
+        self.sel_pair = torch.zeros(p.K_cap, **i32)
+        self.Gc = torch.zeros((p.K_cap, p.h), dtype=st, device=device)
+        self.Phic = torch.zeros((p.K_cap, p.d), dtype=st, device=device)
+        self.dW = torch.zeros((p.E_loc, p.h, p.d), dtype=torch.float32, device=device)
+        self.dphi = torch.zeros((p.K_cap, p.d), dtype=torch.float32, device=device)
+        nws = lrm.lrm_workspace_bytes(p)
+        if nws == 0:
+            raise lrm.LrmError("invalid problem")
+        self.ws = torch.zeros(nws, dtype=torch.uint8, device=device)
+
+
+def run(problem, policy, topk_idx, topk_w, g, phi, W, bufs: DeviceBuffers, stream=None):
+    """Enqueue the whole hot path on `stream` (default: torch's current stream)."""
+    b = bufs
+    lrm.lrm_plan_quotas(problem, policy, topk_idx, b.counts, b.fwd_off, b.row_pair, b.quota,
+                        b.cmp_off, b.ws, stream)
+    lrm.lrm_score(problem, topk_w, g, phi, b.row_pair, b.fwd_off, b.score, b.ws, stream)
+    lrm.lrm_select(problem, b.score, b.fwd_off, b.quota, b.cmp_off, b.sel_row, b.ws, stream)
+    lrm.lrm_compact(problem, b.sel_row, b.row_pair, b.cmp_off, topk_w, g, phi, b.Gc, b.Phic,
+                    b.sel_pair, b.ws, stream)
+    lrm.lrm_grouped_dw(problem, b.Gc, b.Phic, b.cmp_off, b.dW, b.ws, stream)
+    lrm.lrm_grouped_dx(problem, b.Gc, W, b.cmp_off, b.dphi, b.ws, stream)

@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Throughput of the LRMoE backward hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input already resident in HBM:
+lrm_plan_quotas -> lrm_score -> lrm_select -> lrm_compact -> lrm_grouped_dw -> lrm_grouped_dx.
+
+Default workload: the Qwen3-30B-A3B-shaped share of one GPU (128 experts, 16 local, top-8,
+32768 tokens, h=2048, d_ffn=768, bf16, retention rho = 0.5).  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "pairs/s thru LRM score+select+compact+grouped dW/dφ GEMM; % bf16 MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix-core peaks, TFLOP/s
+
+STAGES = ("plan", "score", "select", "compact", "dw", "dx")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-experts", type=int, default=4)
+    return ap.parse_args()
+
+
+def algorithmic(w, oracle_like):
+    """Algorithmic bytes / flops of each stage (what the method must move or compute)."""
+    sp = w.spec
+    b = 2 if sp.dtype == "bf16" else 4
+    L, K = oracle_like["L"], oracle_like["K"]
+    k = sp.k
+    loc = (w.topk_idx >= sp.e_lo) & (w.topk_idx < sp.e_lo + sp.E_loc)
+    T_loc = int(np.unique(np.flatnonzero(loc) // k).size)
+    T_ret = oracle_like["T_ret"]
+    Ke = oracle_like["Ke"]
+    h, d, E_loc = sp.h, sp.d, sp.E_loc
+    return {
+        "plan": 4 * sp.T * k + 4 * L + 16 * E_loc,
+        "score": T_loc * h * b + L * d * b + 12 * L,
+        "select": 4 * L + 4 * K,
+        "compact": 16 * K + T_ret * h * b + K * d * b + K * (h + d) * b,
+        "dw": K * (h + d) * b + 4 * E_loc * h * d,
+        "dx": K * h * b + int((Ke > 0).sum()) * h * d * b + 4 * K * d,
+        "flops_dw": 2 * K * h * d,
+        "flops_dx": 2 * K * h * d,
+    }
+
+
+def gpu_bench(w, pol_dict, steps, warmup):
+    import torch
+    from backward_token_expert_amd import lrm, path
+    from backward_token_expert_amd.path import to_device, to_host
+    sp = w.spec
+    L_cap = sp.T * min(sp.k, sp.E_loc)
+    P = lrm.make_problem(sp.T, sp.k, sp.E, sp.e_lo, sp.E_loc, sp.h, sp.d, sp.dtype, L_cap, L_cap)
+    pol = lrm.make_policy(pol_dict["full"], pol_dict["rho_num"], pol_dict["rho_den"],
+                          pol_dict["cap_abs"])
+    phi = w.phi
+    if phi.shape[0] < L_cap:
+        phi = np.concatenate([phi, np.zeros((L_cap - phi.shape[0], sp.d), phi.dtype)])
+    idx, tw, g, ph, W = (to_device(a) for a in (w.topk_idx, w.topk_w, w.g, phi, w.W))
+    b = path.DeviceBuffers(P)
+    s = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(s)
+        lrm.lrm_plan_quotas(P, pol, idx, b.counts, b.fwd_off, b.row_pair, b.quota, b.cmp_off, b.ws, s)
+        if ev is not None:
+            ev[1].record(s)
+        lrm.lrm_score(P, tw, g, ph, b.row_pair, b.fwd_off, b.score, b.ws, s)
+        if ev is not None:
+            ev[2].record(s)
+        lrm.lrm_select(P, b.score, b.fwd_off, b.quota, b.cmp_off, b.sel_row, b.ws, s)
+        if ev is not None:
+            ev[3].record(s)
+        lrm.lrm_compact(P, b.sel_row, b.row_pair, b.cmp_off, tw, g, ph, b.Gc, b.Phic, b.sel_pair,
+                        b.ws, s)
+        if ev is not None:
+            ev[4].record(s)
+        lrm.lrm_grouped_dw(P, b.Gc, b.Phic, b.cmp_off, b.dW, b.ws, s)
+        if ev is not None:
+            ev[5].record(s)
+        lrm.lrm_grouped_dx(P, b.Gc, W, b.cmp_off, b.dphi, b.ws, s)
+        if ev is not None:
+            ev[6].record(s)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    err = lrm.lrm_read_device_error(b.ws)
+    if err:
+        raise RuntimeError(f"device error word {err}: {lrm.deverr_names(err)}")
+
+    # Timed region: exactly `steps` whole-path steps.  HIP events bracket every stage on the
+    # stream the kernels are launched on; they cost nothing measurable next to the stages.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record(s)
+    for i in range(steps):
+        step(evs[i])
+    t_end.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = t_start.elapsed_time(t_end)
+    stage_ms = {st: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+                for j, st in enumerate(STAGES)}
+    fo = to_host(b.fwd_off)
+    co = to_host(b.cmp_off)
+    sel_pair = to_host(b.sel_pair)[:int(co[-1])]
+    info = {"L": int(fo[-1]), "K": int(co[-1]), "Ke": np.diff(co),
+            "T_ret": int(np.unique(sel_pair // sp.k).size)}
+    return ms_total / steps, wall / steps * 1e3, stage_ms, info
+
+
+def cpu_baseline(w, pol_dict, n_experts):
+    """The oracle, as it stands, on a bounded sample: all counting/planning plus scoring,
+    selection, compaction and both GEMMs of the first `n_experts` local experts."""
+    import oracle as O
+    sp = w.spec
+    threads = None
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=None)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    n = O.routed_counts(w.topk_idx, sp.E)
+    row_pair, fwd_off = O.forward_layout(w.topk_idx, sp.e_lo, sp.E_loc)
+    quota, cmp_off = O.plan_quotas(n[sp.e_lo:sp.e_lo + sp.E_loc], pol_dict)
+    ne = min(n_experts, sp.E_loc)
+    rows = slice(0, int(fwd_off[ne]))
+    R = O.lrm_scores(w.topk_w, w.g, w.phi[rows], row_pair[rows], sp.k, sp.dtype)
+    sel = O.select_top_quota(R.astype(np.float32), fwd_off[:ne + 1], quota[:ne], row_pair)
+    Gc, Phic, _ = O.compact(sel, row_pair, w.topk_w, w.g, w.phi, sp.k, sp.dtype)
+    off = cmp_off[:ne + 1]
+    O.grouped_dw(Gc, Phic, off, sp.dtype)
+    O.grouped_dx(Gc, w.W[:ne], off, sp.dtype)
+    dt = time.perf_counter() - t0
+    pairs = int(fwd_off[ne])
+    return {"value": pairs / dt, "unit": "pairs/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle: counts/layout/quotas over all {sp.T * sp.k} pairs, "
+                      f"then score/select/compact/dW/dphi for local experts 0..{ne - 1} "
+                      f"({pairs} routed pairs, {int(off[-1])} retained), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import synth
+    w = synth.make(args.config)
+    sp = w.spec
+    pol = synth.policy(sp)
+    ms, wall_ms, stages, info = gpu_bench(w, pol, args.steps, args.warmup)
+    alg = algorithmic(w, info)
+    L, K = info["L"], info["K"]
+    # rho = 1 (full retention) on the same input
+    pol_full = synth.policy(sp, full=True)
+    ms1, _, stages1, info1 = gpu_bench(w, pol_full, max(3, args.steps // 2), 2)
+    alg1 = algorithmic(w, info1)
+
+    def fractions(st, a, dtype):
+        t_ssc = (st["score"] + st["select"] + st["compact"]) * 1e-3
+        by = a["score"] + a["select"] + a["compact"]
+        t_g = (st["dw"] + st["dx"]) * 1e-3
+        fl = a["flops_dw"] + a["flops_dx"]
+        return {"score_select_compact_GBps": by / t_ssc / 1e9,
+                "score_select_compact_hbm_frac": by / t_ssc / 1e9 / HBM_PEAK_GBS,
+                "gemms_TFLOPs": fl / t_g / 1e12,
+                "gemms_mfma_frac": fl / t_g / 1e12 / MFMA_PEAK_TFLOPS[dtype]}
+
+    dom = max(("dw", "dx"), key=lambda s: stages[s])
+    ach = alg["flops_" + dom] / (stages[dom] * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[sp.dtype]
+    out = {
+        "metric": METRIC,
+        "value": L / (ms * 1e-3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sp.dtype,
+        "data": "synthetic",
+        "config": {"workload": sp.name, "T": sp.T, "top_k": sp.k, "experts": sp.E,
+                   "local_experts": sp.E_loc, "h": sp.h, "d_ffn": sp.d,
+                   "rho": f"{pol['rho_num']}/{pol['rho_den']}", "L_pairs": L, "K_retained": K},
+        "roofline": {"bound": "mfma", "kernel": {"dw": "lrm_grouped_dw", "dx": "lrm_grouped_dx"}[dom],
+                     "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
+                     "traffic": None},
+        "retained_rows_per_s": K / (ms * 1e-3),
+        "wall_ms_per_step": wall_ms,
+        "stages_ms": stages,
+        "fractions": fractions(stages, alg, sp.dtype),
+        "rho1": {"value": info1["L"] / (ms1 * 1e-3), "ms_per_step": ms1, "K_retained": info1["K"],
+                 "stages_ms": stages1, "fractions": fractions(stages1, alg1, sp.dtype)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, pol, args.cpu_sample_experts)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+/*
+ * lrm.h -- C ABI of the LRMoE backward hot path on one MI355X (gfx950).
+ *
+ * The library implements, for one GPU's share of an expert-parallel MoE layer, the backward-time
+ * steps of "LRMoE: Demand-Side Load Re-Calibration for Efficient MoE Training on
+ * Memory-Constrained Nodes" (Hu et al., arXiv 2610.37720):
+ *   lrm_plan_quotas  routed counts n_e, forward layout, quotas q_e, compacted offsets
+ *                    (Algorithm 1 step 1; Sec. 3.1 and 3.3 quotas 0 <= K_e <= N_e; the capacity
+ *                    form of "Expert Parallel Math Deep", "Capacity and the exact drop-rate
+ *                    formula")
+ *   lrm_score        Load Recalibration Metric R_u = alpha_u^2 ||g_t||^2 ||phi_u||^2
+ *                    (Sec. 3.2, Prop. 3.1, Eq. (3); Algorithm 1 step 13)
+ *   lrm_select       per-expert TopK(q_e) (Algorithm 1 step 14; Sec. 3.3; Appendix 7.2 Prop. 7.1)
+ *   lrm_compact      physical compaction into contiguous expert-major segments
+ *                    (Sec. 3.3, Sec. 3.4, Fig. 4; Appendix 7.1 Eq. (5))
+ *   lrm_grouped_dw   variable-size grouped FC2 weight gradient dW_e = sum_u delta_u phi_u^T
+ *                    (Sec. 3.2 Eq. (1); Appendix 7.1 Eq. (8)-(9); Algorithm 1 step 17)
+ *   lrm_grouped_dx   variable-size grouped FC2 input gradient dphi_u = W_e^T delta_u
+ *                    (Appendix 7.1 Eq. (4)-(7); Sec. 3.3: the retained count is the row dimension
+ *                    of the input-gradient product)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pairs.  Token t routes to k experts; pair p = t*k + j, slot j in descending-logit order.
+ *    topk_idx[p] is the expert of pair p, topk_w[p] its routing weight alpha (float32).
+ *  - Local experts are [e_lo, e_lo + E_loc).  L = number of local pairs, K = sum of quotas.
+ *  - Forward layout: the L local pairs ordered by (expert, pair index); "row" r indexes it.
+ *    row_pair[r] = p, rows of expert e_lo+i are [fwd_off[i], fwd_off[i+1]).  phi is given in this
+ *    layout: phi[r] is the saved SwiGLU activation of pair row_pair[r].
+ *  - Compacted layout: retained rows of local expert i are [cmp_off[i], cmp_off[i+1]), in
+ *    ascending forward-row (= pair) order.
+ *  - Element type (problem.dtype): LRM_F32 or LRM_BF16 for g, phi, W, Gc, Phic.  Scores, dW and
+ *    dphi are float32; indices and offsets int32.
+ *  - Layouts are row-major and dense.  Row widths: g, Gc have h elements; phi, Phic, dphi have
+ *    d elements; W is [E_loc][h][d] (W_e maps d_in = d to d_out = h); dW is [E_loc][h][d].
+ *  - Every pointer except problem/policy (host structs, read during the call only) is device
+ *    memory owned by the caller.  The library never allocates, frees or retains anything.
+ *    Inputs are never written.  Outputs are fully (re)written up to their device-side lengths;
+ *    entries past L or K are left untouched.
+ *  - Every call enqueues work on `stream` and returns without waiting: no host synchronisation,
+ *    no allocation, so a sequence of calls can be captured in a HIP graph.  Results are bitwise
+ *    deterministic for identical inputs.
+ *  - ws is caller-provided device scratch of at least lrm_workspace_bytes(problem) bytes,
+ *    16-byte aligned.  Its first word is a sticky device error word (LRM_DEVERR_* bits) that
+ *    lrm_plan_quotas clears and every call may set; read it with lrm_read_device_error.
+ *  - Host-side validation returns LRM_ERR_INVALID_ARGUMENT (null pointer, non-positive sizes,
+ *    k > E, e_lo + E_loc > E, rho_den <= 0, caps too small for the problem) or
+ *    LRM_ERR_UNSUPPORTED (pointer not 16-byte aligned, h or d not a multiple of 8, unknown dtype,
+ *    E > 4096 or E_loc > 1024).  Launch failures return LRM_ERR_HIP.  Nothing is enqueued when a
+ *    call returns an error.
+ *  - Device-detected violations set error bits instead of faulting; results are then unspecified
+ *    but every access stays inside the buffers described here.
+ */
+#ifndef LRM_H_
+#define LRM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LRM_OK = 0,
+  LRM_ERR_INVALID_ARGUMENT = 1,
+  LRM_ERR_UNSUPPORTED = 2,
+  LRM_ERR_WORKSPACE_TOO_SMALL = 3,
+  LRM_ERR_HIP = 4
+} lrm_status;
+
+typedef enum { LRM_F32 = 0, LRM_BF16 = 1 } lrm_dtype;
+
+/* Device error word bits. */
+#define LRM_DEVERR_EXPERT_ID 1  /* a topk_idx entry outside [0, E); the pair was ignored        */
+#define LRM_DEVERR_L_CAP 2      /* L > L_cap; forward segments were truncated at L_cap           */
+#define LRM_DEVERR_K_CAP 4      /* K > K_cap (or an offset past K_cap); segments truncated       */
+#define LRM_DEVERR_QUOTA 8      /* quota[i] outside [0, n_i]; clamped into range                  */
+#define LRM_DEVERR_NONFINITE 16 /* a score that is NaN, infinite or negative                      */
+#define LRM_DEVERR_INDEX 32     /* sel_row / row_pair entry out of range; the row was skipped     */
+
+typedef struct {
+  int32_t T;      /* tokens                                                                   */
+  int32_t k;      /* experts per token (top-k)                                                */
+  int32_t E;      /* global experts                                                           */
+  int32_t e_lo;   /* first local expert                                                       */
+  int32_t E_loc;  /* number of local experts                                                  */
+  int32_t h;      /* FC2 output width (hidden size): columns of g, Gc; rows of W_e, dW_e      */
+  int32_t d;      /* FC2 input width (expert FFN size): columns of phi, Phic, dphi, W_e, dW_e */
+  int32_t dtype;  /* lrm_dtype of g, phi, W, Gc, Phic                                          */
+  int32_t L_cap;  /* rows of row_pair, phi, score; >= 1                                        */
+  int32_t K_cap;  /* rows of sel_row, sel_pair, Gc, Phic, dphi; >= 1                           */
+} lrm_problem;
+
+/*
+ * Quota policy (the pages leave the allocation policy open, LRMoE Sec. 3.2; this is the capacity
+ * form C = CF * mean load of "Expert Parallel Math Deep"):
+ *   full != 0 :  q_i = n_i                                  (full retention, rho = 1)
+ *   otherwise :  q_i = min(n_i, floor(rho_num * L / (rho_den * E_loc)), cap_abs if cap_abs >= 0)
+ * computed exactly in 64-bit integers, with n_i the routed count of local expert e_lo + i.
+ */
+typedef struct {
+  int32_t full;
+  int32_t rho_num;
+  int32_t rho_den;
+  int32_t cap_abs;
+} lrm_quota_policy;
+
+/* Bytes of device scratch the calls need for this problem (0 if the problem is invalid). */
+size_t lrm_workspace_bytes(const lrm_problem* problem);
+
+/*
+ * Counts, forward layout, quotas and compacted offsets (LRMoE Algorithm 1 step 1; Sec. 3.3).
+ *  in : topk_idx  int32 [T*k]
+ *  out: counts    int32 [E]          routed pairs of every global expert (sum = T*k)
+ *       fwd_off   int32 [E_loc + 1]  exclusive prefix of the local counts; fwd_off[E_loc] = L
+ *       row_pair  int32 [L_cap]      pair index of each forward row (first L written)
+ *       quota     int32 [E_loc]      q_i under `policy`
+ *       cmp_off   int32 [E_loc + 1]  exclusive prefix of the quotas; cmp_off[E_loc] = K
+ * Clears the device error word first.  Out-of-range expert ids are skipped and flagged.
+ */
+lrm_status lrm_plan_quotas(const lrm_problem* problem, const lrm_quota_policy* policy,
+                           const int32_t* topk_idx, int32_t* counts, int32_t* fwd_off,
+                           int32_t* row_pair, int32_t* quota, int32_t* cmp_off, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/*
+ * LRM score of every local forward row (LRMoE Sec. 3.2, Prop. 3.1, Eq. (3)):
+ *   score[r] = fl32(alpha_p^2 * ||g_t||^2 * ||phi_r||^2),  p = row_pair[r], t = p / k,
+ * with both squared norms accumulated in float64 (every square of a bf16 or fp32 value is exact
+ * in float64) by a fixed-order reduction that does not depend on the row's position, then one
+ * rounding to float32.
+ *  in : topk_w float32 [T*k]; g [T][h]; phi [L_cap][d]; row_pair int32 [L_cap];
+ *       fwd_off int32 [E_loc+1] (only fwd_off[E_loc] = L is read)
+ *  out: score float32 [L_cap] (first L written)
+ * Non-finite or negative results set LRM_DEVERR_NONFINITE.
+ */
+lrm_status lrm_score(const lrm_problem* problem, const float* topk_w, const void* g,
+                     const void* phi, const int32_t* row_pair, const int32_t* fwd_off,
+                     float* score, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Per-expert top-q selection (LRMoE Algorithm 1 step 14; Appendix 7.2 Prop. 7.1).  In each
+ * forward segment i keep the quota[i] rows that come first in the order (score descending, pair
+ * index ascending; within a segment pair order equals row order) and write their forward-row ids,
+ * ascending, to sel_row[cmp_off[i] ...].  Scores are compared as float32 (equal bit patterns tie).
+ *  in : score float32 [L_cap]; fwd_off, quota, cmp_off as written by lrm_plan_quotas (any values
+ *       with cmp_off[i+1] - cmp_off[i] == quota[i] are accepted)
+ *  out: sel_row int32 [K_cap] (first K written)
+ * A quota outside [0, n_i] is clamped (LRM_DEVERR_QUOTA); a NaN/negative score sets
+ * LRM_DEVERR_NONFINITE.
+ */
+lrm_status lrm_select(const lrm_problem* problem, const float* score, const int32_t* fwd_off,
+                      const int32_t* quota, const int32_t* cmp_off, int32_t* sel_row, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Physical compaction (LRMoE Sec. 3.3/3.4, Fig. 4; Appendix 7.1 Eq. (5)).  For i < K:
+ *   r = sel_row[i], p = row_pair[r], t = p / k
+ *   Gc[i]       = RNE_dtype(fl32(topk_w[p] * g[t]))   (one float32 product per element, then
+ *                                                      round-to-nearest-even to the element type)
+ *   Phic[i]     = phi[r]                              (bit copy)
+ *   sel_pair[i] = p
+ *  in : sel_row int32 [K_cap]; row_pair int32 [L_cap]; cmp_off int32 [E_loc+1] (only
+ *       cmp_off[E_loc] = K is read); topk_w; g; phi
+ *  out: Gc [K_cap][h]; Phic [K_cap][d]; sel_pair int32 [K_cap]
+ */
+lrm_status lrm_compact(const lrm_problem* problem, const int32_t* sel_row, const int32_t* row_pair,
+                       const int32_t* cmp_off, const float* topk_w, const void* g,
+                       const void* phi, void* Gc, void* Phic, int32_t* sel_pair, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Grouped FC2 weight gradient over the retained rows only (LRMoE Sec. 3.2 Eq. (1); Appendix 7.1
+ * Eq. (8)-(9); Sec. 3.4 "no padding rows"):  for every local expert i,
+ *   dW[i] = sum_{c in [cmp_off[i], cmp_off[i+1])} Gc[c]^T (outer) Phic[c]      ([h][d], float32)
+ * bf16 inputs use bf16 matrix-core products with float32 accumulation; fp32 inputs use fp32
+ * matrix-core products.  An expert with no retained row gets exact zeros.  Summation order is
+ * fixed, so results are bitwise reproducible.
+ */
+lrm_status lrm_grouped_dw(const lrm_problem* problem, const void* Gc, const void* Phic,
+                          const int32_t* cmp_off, float* dW, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
+ * Grouped FC2 input gradient over the retained rows only (LRMoE Appendix 7.1 Eq. (4)-(7)):
+ *   dphi[c] = W_e^T Gc[c]   for c in [cmp_off[i], cmp_off[i+1]),   i.e. dphi[c][j] =
+ *   sum_o Gc[c][o] * W[i][o][j]  ([K_cap][d] float32; first K rows written).
+ * The row tiles are scheduled on the device from cmp_off; no host synchronisation.
+ */
+lrm_status lrm_grouped_dx(const lrm_problem* problem, const void* Gc, const void* W,
+                          const int32_t* cmp_off, float* dphi, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
+ * Copies the device error word to *code (host).  Synchronises `stream` (tests and diagnostics
+ * only, never inside a captured sequence).  If clear != 0 the word is reset to zero afterwards.
+ */
+lrm_status lrm_read_device_error(void* ws, int32_t* code, int32_t clear, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* lrm_status_string(lrm_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRM_H_ */

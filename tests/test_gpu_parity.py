@@ -1,0 +1,457 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Bar (per the contract of the path):
+  * counts, forward layout, quotas, offsets, selected rows, compacted buffers and pair ids:
+    bit-exact;
+  * scores: |s - R| <= 1e-5 * R against the oracle's float64 R;
+  * dW and dphi: relative Frobenius error per expert <= 1e-5 (fp32 inputs) or 2e-3 (bf16
+    inputs); experts without retained rows must be exactly zero.
+Selection is also gated in reverse: the GPU select applied to the oracle's float32 scores must
+reproduce the oracle's selection exactly (both decide on the same float32 values).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from tests import _common as C
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def run_gpu(w, pol, K_cap=None):
+    torch = _torch()
+    from backward_token_expert_amd import lrm, path
+    P = C.problem(w.spec, K_cap)
+    bufs = path.DeviceBuffers(P)
+    inp = C.upload(w)
+    path.run(P, C.policy_obj(pol), inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"], inp["W"],
+             bufs)
+    torch.cuda.synchronize()
+    err = lrm.lrm_read_device_error(bufs.ws)
+    return P, bufs, inp, err
+
+
+def host(bufs, sp):
+    from backward_token_expert_amd.path import to_host
+    bf = sp.dtype == "bf16"
+    fo = to_host(bufs.fwd_off)
+    co = to_host(bufs.cmp_off)
+    L, K = int(fo[-1]), int(co[-1])
+    return dict(counts=to_host(bufs.counts), fwd_off=fo, row_pair=to_host(bufs.row_pair)[:L],
+                quota=to_host(bufs.quota), cmp_off=co, score=to_host(bufs.score)[:L],
+                sel_row=to_host(bufs.sel_row)[:K], sel_pair=to_host(bufs.sel_pair)[:K],
+                Gc=to_host(bufs.Gc, bf)[:K], Phic=to_host(bufs.Phic, bf)[:K],
+                dW=to_host(bufs.dW), dphi=to_host(bufs.dphi)[:K])
+
+
+def check_plan(g, o):
+    np.testing.assert_array_equal(g["counts"], o["counts"])
+    np.testing.assert_array_equal(g["fwd_off"], o["fwd_off"])
+    np.testing.assert_array_equal(g["row_pair"], o["row_pair"])
+    np.testing.assert_array_equal(g["quota"], o["quota"])
+    np.testing.assert_array_equal(g["cmp_off"], o["cmp_off"])
+
+
+def check_scores(g, o):
+    R = o["score64"]
+    s = g["score"].astype(np.float64)
+    bad = np.abs(s - R) > 1e-5 * R
+    assert not bad.any(), f"{int(bad.sum())} scores off, worst rel {np.max(np.abs(s - R) / np.maximum(R, 1e-300))}"
+    return int((g["score"].view(np.uint32) != o["score32"].view(np.uint32)).sum())
+
+
+def check_selection_valid(g, o):
+    """GPU selection from the GPU's own scores: bit-exact with the oracle wherever the two float32
+    score vectors agree bitwise; otherwise the kept set must be the unique top-q under the GPU's
+    scores and every disagreement must sit on a boundary that the 1e-5 score tolerance reaches."""
+    s_bits = g["score"].view(np.uint32).astype(np.int64)
+    fo, co, q = g["fwd_off"], g["cmp_off"], g["quota"]
+    rp = g["row_pair"]
+    for e in range(len(q)):
+        rows = np.arange(fo[e], fo[e + 1])
+        kept = g["sel_row"][co[e]:co[e + 1]]
+        assert kept.size == q[e]
+        assert np.all(np.diff(kept) > 0)
+        if kept.size == 0 or kept.size == rows.size:
+            continue
+        dropped = np.setdiff1d(rows, kept)
+        # rank key: higher score first, then lower pair index
+        kk = s_bits[kept] * (1 << 32) - rp[kept]
+        kd = s_bits[dropped] * (1 << 32) - rp[dropped]
+        assert kk.min() > kd.max()
+    same = np.array_equal(g["score"].view(np.uint32), o["score32"].view(np.uint32))
+    if same:
+        np.testing.assert_array_equal(g["sel_row"], o["sel_row"])
+    else:
+        diff = np.setxor1d(g["sel_row"], o["sel_row"])
+        R = o["score64"]
+        for r in diff:
+            e = np.searchsorted(fo, r, side="right") - 1
+            seg = np.arange(fo[e], fo[e + 1])
+            kept_o = o["sel_row"][o["cmp_off"][e]:o["cmp_off"][e + 1]]
+            drop_o = np.setdiff1d(seg, kept_o)
+            lo = R[kept_o].min() if kept_o.size else 0.0
+            hi = R[drop_o].max() if drop_o.size else 0.0
+            assert abs(R[r] - lo) <= 2e-5 * lo or abs(R[r] - hi) <= 2e-5 * hi
+
+
+def check_compact(g, o, bit_exact=True):
+    np.testing.assert_array_equal(g["sel_row"], o["sel_row"])
+    np.testing.assert_array_equal(g["sel_pair"], o["sel_pair"])
+    assert g["Gc"].tobytes() == o["Gc"].tobytes()
+    assert g["Phic"].tobytes() == o["Phic"].tobytes()
+
+
+def check_gemms_full(g, o, dtype):
+    tol = C.tol_for(dtype)
+    co = o["cmp_off"]
+    for e in range(len(co) - 1):
+        if co[e + 1] == co[e]:
+            assert not g["dW"][e].any(), f"expert {e} has no rows but nonzero dW"
+            continue
+        err = C.rel_fro(g["dW"][e], o["dW"][e])
+        assert err <= tol, f"dW expert {e}: rel fro {err}"
+        errx = C.rel_fro(g["dphi"][co[e]:co[e + 1]], o["dphi"][co[e]:co[e + 1]])
+        assert errx <= tol, f"dphi expert {e}: rel fro {errx}"
+
+
+def check_gemms_sampled(g, o, W, dtype, seed=0, rows_per_expert=8, dx_rows=24):
+    tol = C.tol_for(dtype)
+    co = o["cmp_off"]
+    rng = np.random.default_rng(seed)
+    h = o["Gc"].shape[1] if o["Gc"].ndim == 2 else W.shape[1]
+    for e in range(len(co) - 1):
+        if co[e + 1] == co[e]:
+            assert not g["dW"][e].any()
+            continue
+        rows_h = np.unique(np.concatenate([[0, h - 1], rng.choice(h, rows_per_expert)]))
+        ref = O.dw_rows(o["Gc"], o["Phic"], co, e, rows_h, dtype)
+        err = C.rel_fro(g["dW"][e][rows_h], ref)
+        assert err <= tol, f"dW expert {e}: rel fro {err} on sampled rows"
+        n = co[e + 1] - co[e]
+        ri = np.unique(np.concatenate([[co[e], co[e + 1] - 1],
+                                       co[e] + rng.choice(n, min(n, dx_rows))]))
+        refx = O.dx_rows(o["Gc"], W, co, ri, dtype)
+        errx = C.rel_fro(g["dphi"][ri], refx)
+        assert errx <= tol, f"dphi expert {e}: rel fro {errx} on sampled rows"
+
+
+def gate_select(P, bufs, o):
+    """GPU select on the oracle's float32 scores and offsets must equal the oracle's selection."""
+    torch = _torch()
+    from backward_token_expert_amd import lrm
+    from backward_token_expert_amd.path import to_device, to_host
+    L = int(o["fwd_off"][-1])
+    score = torch.zeros_like(bufs.score)
+    score[:L] = to_device(o["score32"])
+    fo = to_device(o["fwd_off"].astype(np.int32))
+    q = to_device(o["quota"].astype(np.int32))
+    co = to_device(o["cmp_off"].astype(np.int32))
+    sel = torch.full_like(bufs.sel_row, -1)
+    lrm.lrm_select(P, score, fo, q, co, sel, bufs.ws)
+    torch.cuda.synchronize()
+    K = int(o["cmp_off"][-1])
+    np.testing.assert_array_equal(to_host(sel)[:K], o["sel_row"])
+
+
+def gate_compact_gemms(P, bufs, inp, o, W, dtype, sampled):
+    """GPU compaction of the oracle's selection, then the GPU GEMMs on those buffers."""
+    torch = _torch()
+    from backward_token_expert_amd import lrm
+    from backward_token_expert_amd.path import to_device, to_host
+    K = int(o["cmp_off"][-1])
+    L = int(o["fwd_off"][-1])
+    sel = torch.zeros_like(bufs.sel_row)
+    sel[:K] = to_device(o["sel_row"].astype(np.int32))
+    rp = torch.zeros_like(bufs.row_pair)
+    rp[:L] = to_device(o["row_pair"].astype(np.int32))
+    co = to_device(o["cmp_off"].astype(np.int32))
+    lrm.lrm_compact(P, sel, rp, co, inp["topk_w"], inp["g"], inp["phi"], bufs.Gc, bufs.Phic,
+                    bufs.sel_pair, bufs.ws)
+    lrm.lrm_grouped_dw(P, bufs.Gc, bufs.Phic, co, bufs.dW, bufs.ws)
+    lrm.lrm_grouped_dx(P, bufs.Gc, inp["W"], co, bufs.dphi, bufs.ws)
+    torch.cuda.synchronize()
+    bf = dtype == "bf16"
+    g = dict(sel_row=o["sel_row"], sel_pair=to_host(bufs.sel_pair)[:K],
+             Gc=to_host(bufs.Gc, bf)[:K], Phic=to_host(bufs.Phic, bf)[:K],
+             dW=to_host(bufs.dW), dphi=to_host(bufs.dphi)[:K])
+    check_compact(g, o)
+    if sampled:
+        check_gemms_sampled(g, o, W, dtype)
+    else:
+        check_gemms_full(g, o, dtype)
+
+
+# ------------------------------------------------------------------------------------------------
+# small workloads: full oracle, everything compared
+# ------------------------------------------------------------------------------------------------
+
+SMALL = [
+    ("tiny-fp32", 0, {}),
+    ("qwen3-T2048", 1, {"T": 2048}),
+    ("glm45-T1024", 2, {"T": 1024}),
+    ("skew-T4096", 3, {"T": 4096}),
+    ("layer-T2048", 4, {"T": 2048}),
+]
+
+
+@pytest.mark.parametrize("full", [False, True], ids=["cfg-rho", "rho1"])
+@pytest.mark.parametrize("name,cfg,over", SMALL, ids=[s[0] for s in SMALL])
+def test_small_end_to_end(name, cfg, over, full):
+    w = C.workload(cfg, **over)
+    sp = w.spec
+    pol = synth.policy(sp, full=full)
+    print(f"[case] {name} full={full}", flush=True)
+    P, bufs, inp, err = run_gpu(w, pol)
+    assert err == 0, f"device error {err}"
+    o = C.oracle_run(w, pol)
+    g = host(bufs, sp)
+    check_plan(g, o)
+    check_scores(g, o)
+    check_selection_valid(g, o)
+    gate_select(P, bufs, o)
+    if np.array_equal(g["sel_row"], o["sel_row"]):
+        check_compact(g, o)
+        check_gemms_full(g, o, sp.dtype)
+    else:
+        gate_compact_gemms(P, bufs, inp, o, w.W, sp.dtype, sampled=False)
+
+
+@pytest.mark.parametrize("rho", synth.RHO_SWEEP_3, ids=["1.0", "0.75", "0.5", "0.25"])
+def test_small_skew_rho_sweep(rho):
+    w = C.workload(3, T=4096)
+    pol = synth.policy(w.spec, rho=rho)
+    print(f"[case] skew-T4096 rho={rho}", flush=True)
+    P, bufs, inp, err = run_gpu(w, pol)
+    assert err == 0
+    o = C.oracle_run(w, pol)
+    g = host(bufs, w.spec)
+    check_plan(g, o)
+    check_scores(g, o)
+    check_selection_valid(g, o)
+    gate_select(P, bufs, o)
+    check_compact(g, o)
+    check_gemms_full(g, o, w.spec.dtype)
+
+
+# ------------------------------------------------------------------------------------------------
+# hand-built edge cases
+# ------------------------------------------------------------------------------------------------
+
+def custom(idx_rows, E, e_lo, E_loc, h, d, dtype, seed=7, weights=None):
+    """Workload from explicit routing (rows of expert ids per token) with seeded values."""
+    idx = np.asarray(idx_rows, np.int32)
+    T, k = idx.shape
+    rng = np.random.default_rng(seed)
+    if weights is None:
+        a = rng.random((T, k)) + 0.05
+        weights = (a / a.sum(1, keepdims=True)).astype(np.float32)
+    sp = dataclasses.replace(synth.SPECS[1], name="custom", T=T, k=k, E=E, e_lo=e_lo, E_loc=E_loc,
+                             h=h, d=d, dtype=dtype, seed=seed)
+    flat = idx.reshape(-1)
+    loc = (flat >= e_lo) & (flat < e_lo + E_loc)
+    lp = np.flatnonzero(loc)
+    layout = lp[np.argsort(flat[loc], kind="stable")]
+    g = synth.rows(seed, synth.S_G, T, h, kind=dtype)
+    phi = synth.swiglu_rows(seed, layout, d, kind=dtype)
+    W = synth.rows(seed, synth.S_W, E_loc * h, d, scale=d ** -0.5, kind=dtype).reshape(E_loc, h, d)
+    return synth.Workload(sp, flat.copy(), np.asarray(weights, np.float32).reshape(-1).copy(), g,
+                          phi, W, layout, np.zeros(E), np.arange(T))
+
+
+def full_compare(w, pol, expect_err=0):
+    P, bufs, inp, err = run_gpu(w, pol)
+    assert err == expect_err, f"device error {err}"
+    o = C.oracle_run(w, pol)
+    g = host(bufs, w.spec)
+    check_plan(g, o)
+    check_scores(g, o)
+    check_selection_valid(g, o)
+    gate_select(P, bufs, o)
+    check_compact(g, o)
+    check_gemms_full(g, o, w.spec.dtype)
+    return g, o
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_segment_sizes_and_ragged_tiles(dtype):
+    # local segments of 0, 1, 63, 64, 65 and 4097 rows; h and d multiples of 8 but not of 128
+    sizes = [0, 1, 63, 64, 65, 4097]
+    rows = []
+    for e, n in enumerate(sizes):
+        rows += [[e]] * n
+    rows += [[6]] * 50 + [[7]] * 30            # non-local experts
+    rng = np.random.default_rng(3)
+    rows = np.asarray(rows)[rng.permutation(len(rows))]
+    w = custom(rows, E=8, e_lo=0, E_loc=6, h=200, d=72, dtype=dtype)
+    print(f"[case] segment sizes {sizes} dtype={dtype}", flush=True)
+    for pol in ({"full": 1, "rho_num": 1, "rho_den": 1, "cap_abs": -1},
+                {"full": 0, "rho_num": 1, "rho_den": 2, "cap_abs": -1},
+                {"full": 0, "rho_num": 0, "rho_den": 1, "cap_abs": -1},     # q = 0 everywhere
+                {"full": 0, "rho_num": 4, "rho_den": 1, "cap_abs": 64}):    # cap binds
+        full_compare(w, pol)
+
+
+def test_single_local_expert_and_no_local_pairs():
+    rng = np.random.default_rng(4)
+    rows = np.stack([rng.permutation(6)[:2] for _ in range(300)])
+    w = custom(rows, E=6, e_lo=2, E_loc=1, h=64, d=128, dtype="bf16")
+    print("[case] E_loc=1", flush=True)
+    full_compare(w, {"full": 0, "rho_num": 1, "rho_den": 3, "cap_abs": -1})
+    rows = np.stack([rng.permutation([0, 1, 2])[:2] for _ in range(100)])
+    w = custom(rows, E=6, e_lo=3, E_loc=3, h=64, d=64, dtype="bf16")
+    print("[case] L=0", flush=True)
+    g, o = full_compare(w, {"full": 0, "rho_num": 1, "rho_den": 2, "cap_abs": -1})
+    assert g["fwd_off"][-1] == 0 and not g["dW"].any()
+
+
+def test_all_equal_scores_keep_first_rows():
+    T = 500
+    rows = np.zeros((T, 1), np.int32)
+    w = custom(rows, E=2, e_lo=0, E_loc=1, h=64, d=64, dtype="bf16",
+               weights=np.full((T, 1), 0.5, np.float32))
+    w.g[:] = w.g[0]
+    w.phi[:] = w.phi[0]
+    print("[case] all-equal scores", flush=True)
+    g, o = full_compare(w, {"full": 0, "rho_num": 1, "rho_den": 3, "cap_abs": -1})
+    assert g["sel_row"].tolist() == list(range(T // 3))
+
+
+def test_ties_straddling_the_boundary():
+    rng = np.random.default_rng(5)
+    rows = np.stack([rng.permutation(8)[:2] for _ in range(3000)])
+    w = custom(rows, E=8, e_lo=0, E_loc=8, h=128, d=64, dtype="bf16")
+    pol = {"full": 0, "rho_num": 1, "rho_den": 2, "cap_abs": -1}
+    o = C.oracle_run(w, pol, gemms=False)
+    k = w.spec.k
+    # in every expert, copy the q-th ranked pair's (alpha, g, phi) onto the next two ranked pairs
+    for e in range(8):
+        r0, r1 = o["fwd_off"][e], o["fwd_off"][e + 1]
+        q = o["quota"][e]
+        if q == 0 or q + 2 > r1 - r0:
+            continue
+        seg = np.arange(r0, r1)
+        order = seg[np.lexsort((o["row_pair"][seg], -o["score32"][seg].astype(np.float64)))]
+        src = order[q - 1]
+        ps = o["row_pair"][src]
+        for dst in order[q:q + 2]:
+            pd = o["row_pair"][dst]
+            w.topk_w[pd] = w.topk_w[ps]
+            w.g[pd // k] = w.g[ps // k]
+            w.phi[dst] = w.phi[src]
+    o2 = C.oracle_run(w, pol, gemms=False)
+    n_ties = 0
+    for e in range(8):
+        r0, r1 = o2["fwd_off"][e], o2["fwd_off"][e + 1]
+        kept = o2["sel_row"][o2["cmp_off"][e]:o2["cmp_off"][e + 1]]
+        dropped = np.setdiff1d(np.arange(r0, r1), kept)
+        if kept.size and dropped.size:
+            n_ties += int(o2["score32"][kept].min() == o2["score32"][dropped].max())
+    assert n_ties >= 4, "fixture must put ties on the boundary"
+    print(f"[case] boundary ties in {n_ties} experts", flush=True)
+    full_compare(w, pol)
+
+
+def test_segment_longer_than_lds_stage():
+    T = 40000
+    rows = np.zeros((T, 1), np.int32)
+    rows[::7] = 1
+    w = custom(rows, E=2, e_lo=0, E_loc=2, h=64, d=64, dtype="bf16")
+    print("[case] segment of 34285 rows (global-memory select)", flush=True)
+    full_compare(w, {"full": 0, "rho_num": 1, "rho_den": 3, "cap_abs": -1})
+
+
+def test_out_of_range_expert_id_sets_error_word():
+    rng = np.random.default_rng(6)
+    rows = np.stack([rng.permutation(4)[:2] for _ in range(200)])
+    w = custom(rows, E=4, e_lo=0, E_loc=4, h=64, d=64, dtype="bf16")
+    w.topk_idx[5] = 9     # invalid id: skipped and flagged, never dereferenced
+    print("[case] invalid expert id", flush=True)
+    P, bufs, inp, err = run_gpu(w, {"full": 1, "rho_num": 1, "rho_den": 1, "cap_abs": -1})
+    assert err & 1
+    from backward_token_expert_amd.path import to_host
+    cnt = to_host(bufs.counts)
+    valid = np.delete(w.topk_idx, 5)
+    np.testing.assert_array_equal(cnt, np.bincount(valid, minlength=4))
+
+
+# ------------------------------------------------------------------------------------------------
+# determinism and graph capture
+# ------------------------------------------------------------------------------------------------
+
+def test_bitwise_determinism_and_graph_replay():
+    torch = _torch()
+    from backward_token_expert_amd import path
+    w = C.workload(1, T=2048)
+    sp = w.spec
+    pol = C.policy_obj(synth.policy(sp))
+    P = C.problem(sp)
+    inp = C.upload(w)
+    outs = []
+    for _ in range(2):
+        b = path.DeviceBuffers(P)
+        path.run(P, pol, inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"], inp["W"], b)
+        torch.cuda.synchronize()
+        outs.append(host(b, sp))
+    for key in outs[0]:
+        assert outs[0][key].tobytes() == outs[1][key].tobytes(), key
+    # capture the six calls in a graph and replay it; every replay must equal the eager result
+    b = path.DeviceBuffers(P)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        path.run(P, pol, inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"], inp["W"], b, s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            path.run(P, pol, inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"], inp["W"], b, s)
+    for rep in range(3):
+        b.dW.fill_(7.0)
+        b.sel_row.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host(b, sp)
+        for key in got:
+            assert got[key].tobytes() == outs[0][key].tobytes(), (rep, key)
+
+
+# ------------------------------------------------------------------------------------------------
+# full-size workloads (the launch configuration bench.py times): exact where cheap, sampled GEMMs
+# ------------------------------------------------------------------------------------------------
+
+FULL = [(0, None), (1, None), (2, None), (3, (1, 1)), (3, (3, 4)), (3, (1, 2)), (3, (1, 4)),
+        (4, None)]
+
+
+@pytest.mark.parametrize("full", [False, True], ids=["cfg-rho", "rho1"])
+@pytest.mark.parametrize("cfg,rho", FULL, ids=[f"cfg{c}-{r}" for c, r in FULL])
+def test_full_size(cfg, rho, full):
+    if full and rho not in (None, (1, 2)):
+        pytest.skip("full retention is covered once per workload")
+    w = C.workload(cfg)
+    sp = w.spec
+    pol = synth.policy(sp, full=full, rho=rho)
+    print(f"[case] full-size cfg{cfg} rho={rho} full={full}", flush=True)
+    P, bufs, inp, err = run_gpu(w, pol)
+    assert err == 0, f"device error {err}"
+    o = C.oracle_run(w, pol, gemms=False)
+    g = host(bufs, sp)
+    check_plan(g, o)
+    nd = check_scores(g, o)
+    print(f"  scores differing in float32 bits from the oracle's rounding: {nd}", flush=True)
+    check_selection_valid(g, o)
+    gate_select(P, bufs, o)
+    if np.array_equal(g["sel_row"], o["sel_row"]):
+        check_compact(g, o)
+        check_gemms_sampled(g, o, w.W, sp.dtype)
+    else:
+        gate_compact_gemms(P, bufs, inp, o, w.W, sp.dtype, sampled=True)

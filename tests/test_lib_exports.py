@@ -1,0 +1,69 @@
+"""The C-ABI library loads on the CPU, exports every symbol include/lrm.h declares, and rejects
+invalid arguments on the host before any GPU work (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import backward_token_expert_amd as bte
+from backward_token_expert_amd import lrm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lrm.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(lrm_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_six_calls():
+    names = _declared()
+    for f in ("lrm_plan_quotas", "lrm_score", "lrm_select", "lrm_compact", "lrm_grouped_dw",
+              "lrm_grouped_dx"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bte.load_library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(_declared()) <= set(lrm.EXPORTS)
+
+
+def test_workspace_bytes_and_validation_on_host():
+    lib = bte.load_library()
+    p = bte.make_problem(32768, 8, 128, 0, 16, 2048, 768, "bf16", 262144, 262144)
+    n = bte.lrm_workspace_bytes(p)
+    # per-chunk histograms + token norms + tile table, 256-byte aligned
+    assert n % 256 == 0 and n >= 32768 * 8 + (262144 // 1024) * 128 * 4
+    bad = [bte.make_problem(0, 8, 128, 0, 16, 2048, 768, "bf16", 1, 1),       # T = 0
+           bte.make_problem(16, 9, 8, 0, 8, 64, 64, "bf16", 1, 1),            # k > E
+           bte.make_problem(16, 2, 8, 4, 8, 64, 64, "bf16", 1, 1),            # e_lo + E_loc > E
+           bte.make_problem(16, 2, 8, 0, 8, 60, 64, "bf16", 1, 1),            # h % 8 != 0
+           bte.make_problem(16, 2, 8, 0, 8, 64, 64, 7, 1, 1)]                 # unknown dtype
+    for b in bad:
+        assert bte.lrm_workspace_bytes(b) == 0
+    pol = bte.make_policy(0, 1, 2, -1)
+    P = ctypes.byref(p)
+    fake = 0x100000  # never dereferenced: each call below is rejected before any launch
+    # null pointers -> INVALID_ARGUMENT (1)
+    assert lib.lrm_plan_quotas(P, ctypes.byref(pol), None, fake, fake, fake, fake, fake, fake, n,
+                               None) == 1
+    assert lib.lrm_score(P, fake, fake, fake, fake, fake, None, fake, n, None) == 1
+    # misaligned g -> UNSUPPORTED (2)
+    assert lib.lrm_score(P, fake, fake + 2, fake, fake, fake, fake, fake, n, None) == 2
+    # short workspace -> WORKSPACE_TOO_SMALL (3)
+    assert lib.lrm_select(P, fake, fake, fake, fake, fake, fake, n - 256, None) == 3
+    # bad retention fraction
+    pol0 = bte.make_policy(0, 1, 0, -1)
+    assert lib.lrm_plan_quotas(P, ctypes.byref(pol0), fake, fake, fake, fake, fake, fake, fake, n,
+                               None) == 1
+    assert lib.lrm_status_string(3) == b"workspace too small"
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(lrm.LrmError):
+        lrm.load_library(str(tmp_path / "missing.so"))
