@@ -174,7 +174,7 @@ lrm_status lrm_compact(const lrm_problem* problem, const int32_t* sel_row, const
 
 /*
  * Grouped FC2 weight gradient over the retained rows only (LRMoE Sec. 3.2 Eq. (1); Appendix 7.1
- * Eq. (8)-(9); Sec. 3.4 "no padding rows"):  for every local expert i,
+ * Eq. (8)-(9); Sec. 3.4: no padding rows):  for every local expert i,
  *   dW[i] = sum_{c in [cmp_off[i], cmp_off[i+1])} Gc[c]^T (outer) Phic[c]      ([h][d], float32)
  * bf16 inputs use bf16 matrix-core products with float32 accumulation; fp32 inputs use fp32
  * matrix-core products.  An expert with no retained row gets exact zeros.  Summation order is

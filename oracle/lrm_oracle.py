@@ -19,10 +19,10 @@ Every function computes the plain definition: fp64 arithmetic on the exact store
 leave a step open:
   * pair index p = t*k + j, slot j in descending-logit order; token t = p // k;
   * the forward layout of the saved activations phi is expert-major with p ascending inside each
-    expert (the "consistent pair order" of Sec. 3.1/3.3);
+    expert (Sec. 3.1/3.3 keep one fixed pair order);
   * quota policy q_e = n_e (full retention) or min(n_e, floor(num*L / (den*E_loc)), cap) in
-    integer arithmetic, where L is the number of local routed pairs (the pages leave the
-    quota-allocation policy open, Sec. 3.2; this is the capacity form of [EPMath]);
+    integer arithmetic, where L is the number of local routed pairs (the pages leave open how the
+    retained total is split across experts, Sec. 3.2; this is the capacity form of [EPMath]);
   * selection is decided on float32 scores (the precision the GPU stores), ranking by score
     descending and then pair index ascending; kept rows are written in ascending forward-row
     order;
