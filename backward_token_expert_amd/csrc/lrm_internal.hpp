@@ -11,8 +11,10 @@ namespace lrm {
 
 // Pairs handled by one wavefront in the counting passes of lrm_plan_quotas.
 constexpr int kPlanChunk = 1024;
-// Row tile of the grouped input-gradient GEMM (rows of one expert segment per tile).
+// Smallest row tile of the grouped input-gradient GEMMs (sizes the workspace tile table).
 constexpr int kDxTileM = 128;
+// Upper bound on the accelerator dies (XCDs) the GEMM schedules spread work over.
+constexpr int kMaxXcd = 8;
 
 // Layout of the caller-provided workspace (byte offsets, all 256-byte aligned).
 struct WsLayout {
@@ -20,6 +22,7 @@ struct WsLayout {
   size_t hist;    // int32 [nchunks][E]   per-chunk expert histograms / local prefixes
   size_t gnorm;   // double [T]           ||g_t||^2
   size_t tiles;   // int32 [1 + 2*max_tiles] dx tile table: count, then (expert, row0) pairs
+  size_t order;   // int32 [kMaxXcd + kMaxXcd * (E_loc + 1)] dW schedule: per-XCD expert lists
   size_t total;
   int64_t nchunks;
   int64_t max_tiles;
@@ -41,6 +44,8 @@ inline WsLayout ws_layout(const lrm_problem& p) {
   off = align_up(off + (size_t)p.T * 8, 256);
   w.tiles = off;
   off = align_up(off + (size_t)(1 + 2 * w.max_tiles) * 4, 256);
+  w.order = off;
+  off = align_up(off + (size_t)(kMaxXcd + kMaxXcd * (p.E_loc + 1)) * 4, 256);
   w.total = off;
   return w;
 }

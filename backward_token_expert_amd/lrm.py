@@ -13,7 +13,7 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblrm.so")
+LIB_PATH = os.environ.get("LRM_LIBRARY") or os.path.join(_PKG, "liblrm.so")
 
 LRM_F32, LRM_BF16 = 0, 1
 DEVERR = {1: "EXPERT_ID", 2: "L_CAP", 4: "K_CAP", 8: "QUOTA", 16: "NONFINITE", 32: "INDEX"}

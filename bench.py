@@ -33,7 +33,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-experts", type=int, default=4)
+    ap.add_argument("--cpu-sample-experts", type=int, default=16)
+    ap.add_argument("--rho1-steps", type=int, default=None,
+                    help="timed steps of the full-retention pass (default steps/2; 0 skips it)")
     return ap.parse_args()
 
 
@@ -177,9 +179,11 @@ def main():
     alg = algorithmic(w, info)
     L, K = info["L"], info["K"]
     # rho = 1 (full retention) on the same input
-    pol_full = synth.policy(sp, full=True)
-    ms1, _, stages1, info1 = gpu_bench(w, pol_full, max(3, args.steps // 2), 2)
-    alg1 = algorithmic(w, info1)
+    n1 = max(3, args.steps // 2) if args.rho1_steps is None else args.rho1_steps
+    if n1 > 0:
+        pol_full = synth.policy(sp, full=True)
+        ms1, _, stages1, info1 = gpu_bench(w, pol_full, n1, 2)
+        alg1 = algorithmic(w, info1)
 
     def fractions(st, a, dtype):
         t_ssc = (st["score"] + st["select"] + st["compact"]) * 1e-3
@@ -217,9 +221,11 @@ def main():
         "wall_ms_per_step": wall_ms,
         "stages_ms": stages,
         "fractions": fractions(stages, alg, sp.dtype),
-        "rho1": {"value": info1["L"] / (ms1 * 1e-3), "ms_per_step": ms1, "K_retained": info1["K"],
-                 "stages_ms": stages1, "fractions": fractions(stages1, alg1, sp.dtype)},
     }
+    if n1 > 0:
+        out["rho1"] = {"value": info1["L"] / (ms1 * 1e-3), "ms_per_step": ms1,
+                       "K_retained": info1["K"], "stages_ms": stages1,
+                       "fractions": fractions(stages1, alg1, sp.dtype)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, pol, args.cpu_sample_experts)
     print(json.dumps(out))
