@@ -10,14 +10,21 @@
 //   dW[e]   (h x d) = Gc[seg e]^T (h x K_e) * Phic[seg e] (K_e x d)   reduction over rows
 //   dphi    (K_e x d) = Gc[seg e] (K_e x h) * W[e] (h x d)            reduction over h
 //
-// bf16: v_mfma_f32_32x32x16_bf16 with fp32 accumulation; tiles of 256 rows x 128/256 columns,
-// operands staged in LDS in their memory orientation and transposed on the LDS read (see the bf16
-// section).  fp32: v_mfma_f32_32x32x2f32 on 128 x 128 tiles.  LDS is double-buffered with a
-// register prefetch of the next K step.  Expert sizes stay on the device: dW workgroups read their
-// segment bounds from cmp_off (a zero-length segment writes zeros) and take experts in order of
-// decreasing retained rows from a one-workgroup ranking kernel; dphi row tiles come from a tile
-// table that a one-workgroup kernel builds from cmp_off.  No atomics: every output element is
-// owned by one workgroup, so results are deterministic.
+// bf16 (the production path): v_mfma_f32_32x32x16_bf16 with fp32 accumulation, workgroup tiles of
+// 256 rows x 128/192/256 columns, K step 64.  Operands are staged in LDS in their memory
+// orientation and transposed on the LDS read (see the bf16 section).  The kernels are persistent:
+// one workgroup per CU, and the work is laid out per XCD (the MI355X has 8 dies of 32 CUs, each
+// with its own L2; workgroup ids are dealt to dies round-robin):
+//   dW   whole experts are dealt to dies (largest first, in a snake order), and the 32 workgroups
+//        of a die walk the tiles of their experts together, so every row of Gc/Phic is fetched
+//        from HBM once per die and the other tiles of that expert hit in L2;
+//   dphi each die takes a contiguous range of (row tile, column tile) units, columns fastest, so
+//        a row tile's Gc rows and the expert's W stay in that die's L2.
+// Global loads run one K step ahead of the MFMAs (one register stage, two LDS stages).
+// fp32: v_mfma_f32_32x32x2f32 on 128 x 128 tiles, plain grids.
+// Expert sizes stay on the device: schedules are built by one-workgroup kernels from cmp_off; a
+// zero-length segment writes zeros.  No atomics: every output element is owned by one workgroup,
+// so results are bitwise deterministic.
 #include "lrm_device.hpp"
 #include "lrm_internal.hpp"
 
@@ -26,34 +33,19 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
-
-// bf16 tile shapes (MFMA 32x32 tiles per wavefront in M and N; workgroup = 2 x 2 wavefronts).
-#ifndef LRM_DW_MT
-#define LRM_DW_MT 4
-#endif
-#ifndef LRM_DW_NT
-#define LRM_DW_NT 4
-#endif
-#ifndef LRM_DW_BK
-#define LRM_DW_BK 64
-#endif
-#ifndef LRM_DX_MT
-#define LRM_DX_MT 4
-#endif
-#ifndef LRM_DX_NT
-#define LRM_DX_NT 4
-#endif
-#ifndef LRM_DX_BK
-#define LRM_DX_BK 64
-#endif
+constexpr int kWaves = kThreads / kWave;
+constexpr int kBK = 32;      // bf16 K step
+constexpr int kStages = 4;   // LDS stages of the bf16 pipeline
 
 // ------------------------------------------------------------------------------------------------
 // bf16 path
 //
 // Workgroup = 4 wavefronts in a 2 x 2 arrangement; a wavefront owns MT x NT tiles of 32 x 32, so
-// the workgroup tile is (64 MT) x (64 NT), K step 32.  Operands are staged in LDS in their memory
+// the workgroup tile is (64 MT) x (64 NT).  Operands are staged in LDS in their memory
 // orientation:
 //   [k][mn] (mn contiguous): Gc and Phic for dW, W for dphi.  MFMA fragments are read with
 //       ds_read_b64_tr_b16, which transposes 16-bit elements across each group of 16 lanes:
@@ -62,121 +54,251 @@ constexpr int kThreads = 256;
 //       result lane i receives column c0 + i at rows k0 .. k0+3; two such reads give the 8
 //       consecutive reduction elements a 32x32x16 operand lane needs.
 //   [mn][k] (k contiguous): Gc as the row operand of dphi; fragments are plain 16-byte reads.
-// Pitches are padded (by 16 elements for [k][mn], 8 for [mn][k]) against LDS bank conflicts.
 // ------------------------------------------------------------------------------------------------
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-
-template <int MT, int NT, int BK, bool AKMN, bool BKMN>
+template <int MT, int NT, bool AKMN>
 struct Tile {
   static constexpr int BM = 64 * MT, BN = 64 * NT;
-  // LDS pitch (elements).  [k][mn]: +32 elements puts the four rows a 16-lane transpose read
-  // touches 64 bytes apart in the 256-byte bank window, and the next 16 lanes 32 bytes further;
-  // [mn][k]: +8 elements spreads 16 consecutive rows over distinct 16-byte bank groups.
-  static constexpr int PA = AKMN ? BM + 32 : BK + 8;
-  static constexpr int PB = BKMN ? BN + 32 : BK + 8;
-  static constexpr int SA = AKMN ? BK * PA : BM * PA;  // elements per stage
-  static constexpr int SB = BKMN ? BK * PB : BN * PB;
-  static constexpr int CA = BM * BK / 8 / kThreads;     // 16-byte chunks per thread per stage
-  static constexpr int CB = BN * BK / 8 / kThreads;
-  static_assert(CA * 8 * kThreads == BM * BK && CB * 8 * kThreads == BN * BK, "tile / threads");
+  static constexpr int SA = BM * kBK;               // elements per LDS stage (no padding)
+  static constexpr int SB = BN * kBK;
+  static constexpr int IA = SA * 2 / 1024 / kWaves;  // 1 KiB LDS-DMA loads per wavefront per stage
+  static constexpr int IB = SB * 2 / 1024 / kWaves;
+  static_assert(IA * 1024 * kWaves == SA * 2 && IB * 1024 * kWaves == SB * 2, "tile / wavefronts");
+  static_assert(BM % 128 == 0 && (BN % 128 == 0 || BN == 192), "swizzle needs these row widths");
 };
+
+// LDS layouts (element offsets).  Chunks of 8 elements (16 bytes) are XOR-swizzled inside a row
+// instead of padding the pitch, because LDS-DMA writes 1 KiB contiguous blocks.
+//   [k][mn], BMN wide: a 16-lane transpose read touches four consecutive rows, 32 bytes each, and
+//     the next 16 lanes the next 32 bytes of the same rows.  With 512- or 256-byte rows all rows
+//     start in the same bank, so chunk c of row r sits at chunk c ^ 4 (r % 4): the four rows fall
+//     in four different 64-byte quarters of the 256-byte bank window.  With 384-byte rows
+//     (BMN = 192) consecutive rows alternate between the two 128-byte halves, so chunk c ^ 4
+//     ((r / 2) % 2) separates rows r and r + 2 inside a half.
+//   [mn][k], 32 wide: chunk c of row r sits at chunk c ^ ((r / 4) % 4), so 16 consecutive rows
+//     read at one k offset hit 16 different 16-byte bank groups.
+template <int BMN>
+__device__ __forceinline__ int swz_chunk(int row) {
+  return BMN == 192 ? ((row >> 1) & 1) << 2 : (row & 3) << 2;
+}
+template <int BMN>
+__device__ __forceinline__ int swz_kmn(int row, int col) {
+  return row * BMN + ((((col >> 3) ^ swz_chunk<BMN>(row))) << 3) + (col & 7);
+}
+__device__ __forceinline__ int swz_mnk(int row, int k) {
+  return row * kBK + ((((k >> 3) ^ ((row >> 2) & 3))) << 3) + (k & 7);
+}
 
 __device__ __forceinline__ s16x4 ds_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
 
 // 32x32x16 operand fragment from a [k][mn] LDS tile: 32 mn starting at `base`, 16 k at `ks`.
-template <int P>
+template <int BMN>
 __device__ __forceinline__ bf16x8 frag_kmn(const uint16_t* t, int ks, int base, int lane) {
   const int row = ks + 8 * (lane >> 5) + ((lane & 15) >> 2);
   const int col = base + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const uint16_t* p = t + row * P + col;
+  const uint16_t* p = t + swz_kmn<BMN>(row, col);
   const s16x4 lo = ds_tr16(p);
-  const s16x4 hi = ds_tr16(p + 4 * P);
+  const s16x4 hi = ds_tr16(p + 4 * BMN);  // row + 4: same swizzle for both row widths
   return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Same fragment from a [mn][k] LDS tile.
-template <int P>
 __device__ __forceinline__ bf16x8 frag_mnk(const uint16_t* t, int ks, int base, int lane) {
-  return *(const bf16x8*)(t + (base + (lane & 31)) * P + ks + 8 * (lane >> 5));
+  return *(const bf16x8*)(t + swz_mnk(base + (lane & 31), ks + 8 * (lane >> 5)));
 }
 
-// Global -> registers for one stage.  [k][mn] source: rows k0.., columns mn0.. (BMN wide);
-// consecutive threads take consecutive 16-byte chunks of a row.
-template <int BMN, int C>
-__device__ __forceinline__ void gload_kmn(const uint16_t* __restrict__ X, int64_t ld, int k0,
-                                          int kend, int mn0, int mnend, int tid, uint4 (&v)[C]) {
+// Global loads go straight to LDS (buffer_load_dwordx4 ... lds: lane l's 16 bytes land at the
+// wave-uniform LDS address + 16 l).  Buffer resources end at the last valid row, so rows past a
+// segment read as zeros in hardware; chunks past the matrix edge get an offset beyond any range.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n, 0x00020000);
+}
+
+// The load is written as inline assembly: the compiler then does not track it as an LDS write
+// and does not drain all outstanding loads before every LDS read; the pipeline below orders the
+// stages with explicit vmcnt waits and barriers instead.  M0 holds the LDS byte address.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(r)
+               : "memory", "m0");
+}
+
+// Per-lane source offsets (bytes, relative to the stage's first row / the tile's first row) of the
+// DMA loads this wavefront issues for one stage.
+template <int BMN, int I>
+__device__ __forceinline__ void dma_offs_kmn(int64_t ld, int mn0, int mnend, int w, int lane,
+                                             uint32_t (&o)[I]) {
 #pragma unroll
-  for (int j = 0; j < C; ++j) {
-    const int c = tid + kThreads * j, row = c / (BMN / 8), col = (c % (BMN / 8)) * 8;
-    if (k0 + row < kend && mn0 + col < mnend)
-      v[j] = *(const uint4*)(X + (int64_t)(k0 + row) * ld + mn0 + col);
-    else
-      v[j] = make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < I; ++j) {
+    const int q = (w * I + j) * 64 + lane, row = q / (BMN / 8);
+    const int c = (q % (BMN / 8)) ^ swz_chunk<BMN>(row);
+    const int col = mn0 + 8 * c;
+    o[j] = col < mnend ? (uint32_t)((row * ld + col) * 2) : kOutOfRange;
   }
 }
 
-template <int BMN, int C, int P>
-__device__ __forceinline__ void sstore_kmn(uint16_t* __restrict__ t, int tid, const uint4 (&v)[C]) {
+template <int I>
+__device__ __forceinline__ void dma_offs_mnk(int64_t ld, int w, int lane, uint32_t (&o)[I],
+                                             int (&kc)[I]) {
 #pragma unroll
-  for (int j = 0; j < C; ++j) {
-    const int c = tid + kThreads * j, row = c / (BMN / 8), col = (c % (BMN / 8)) * 8;
-    *(uint4*)(t + row * P + col) = v[j];
+  for (int j = 0; j < I; ++j) {
+    const int q = (w * I + j) * 64 + lane, row = q / 4;
+    const int c = (q % 4) ^ ((row >> 2) & 3);
+    kc[j] = 8 * c;
+    o[j] = (uint32_t)((row * ld + 8 * c) * 2);
   }
 }
 
-// [mn][k] source: rows mn0.. , reduction columns k0 .. k0+BK-1.
-template <int BK, int C>
-__device__ __forceinline__ void gload_mnk(const uint16_t* __restrict__ X, int64_t ld, int mn0,
-                                          int mnend, int k0, int kend, int tid, uint4 (&v)[C]) {
+// Fragments of one 16-wide reduction slice for this wavefront.
+template <int MT, int NT, bool AKMN>
+__device__ __forceinline__ void load_frags(const uint16_t* sa, const uint16_t* sb, int ks, int wm,
+                                           int wn, int lane, bf16x8 (&a)[MT], bf16x8 (&b)[NT]) {
+  using C = Tile<MT, NT, AKMN>;
 #pragma unroll
-  for (int j = 0; j < C; ++j) {
-    const int c = tid + kThreads * j, row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-    if (mn0 + row < mnend && k0 + kc < kend)
-      v[j] = *(const uint4*)(X + (int64_t)(mn0 + row) * ld + k0 + kc);
-    else
-      v[j] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < MT; ++i) {
+    const int base = wm * 32 * MT + i * 32;
+    a[i] = AKMN ? frag_kmn<C::BM>(sa, ks, base, lane) : frag_mnk(sa, ks, base, lane);
   }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) b[j] = frag_kmn<C::BN>(sb, ks, wn * 32 * NT + j * 32, lane);
 }
 
-template <int BK, int C, int P>
-__device__ __forceinline__ void sstore_mnk(uint16_t* __restrict__ t, int tid, const uint4 (&v)[C]) {
+template <int MT, int NT>
+__device__ __forceinline__ void mfmas(const bf16x8 (&a)[MT], const bf16x8 (&b)[NT],
+                                      f32x16 (&acc)[MT][NT]) {
 #pragma unroll
-  for (int j = 0; j < C; ++j) {
-    const int c = tid + kThreads * j, row = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-    *(uint4*)(t + row * P + kc) = v[j];
-  }
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-// One K step of MFMAs for this wavefront.
-template <int MT, int NT, int BK, bool AKMN, bool BKMN>
+// One K step (32) of MFMAs for this wavefront: the second slice's fragments are read from LDS
+// while the first slice's MFMAs run; scheduling groups pin that interleave (one MFMA, then one
+// or two LDS reads) so the compiler neither serialises reads and MFMAs nor hoists them.
+template <int MT, int NT, bool AKMN>
 __device__ __forceinline__ void mma_stage(const uint16_t* sa, const uint16_t* sb, int wm, int wn,
                                           int lane, f32x16 (&acc)[MT][NT]) {
-  using C = Tile<MT, NT, BK, AKMN, BKMN>;
+  constexpr int kReads = (AKMN ? 2 : 1) * MT + 2 * NT;  // LDS read instructions per slice
+  constexpr int kMfma = MT * NT;
+  bf16x8 a0[MT], b0[NT], a1[MT], b1[NT];
+  load_frags<MT, NT, AKMN>(sa, sb, 0, wm, wn, lane, a0, b0);
+  load_frags<MT, NT, AKMN>(sa, sb, 16, wm, wn, lane, a1, b1);
+  mfmas<MT, NT>(a0, b0, acc);
+  mfmas<MT, NT>(a1, b1, acc);
+  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+  constexpr int per = (kReads + kMfma - 1) / kMfma;
 #pragma unroll
-  for (int ks = 0; ks < BK; ks += 16) {
-    bf16x8 a[MT], b[NT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int base = wm * 32 * MT + i * 32;
-      a[i] = AKMN ? frag_kmn<C::PA>(sa, ks, base, lane) : frag_mnk<C::PA>(sa, ks, base, lane);
-    }
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int base = wn * 32 * NT + j * 32;
-      b[j] = BKMN ? frag_kmn<C::PB>(sb, ks, base, lane) : frag_mnk<C::PB>(sb, ks, base, lane);
-    }
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  for (int q = 0; q < kMfma; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
   }
+  __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
+}
+
+// Operands of one output tile.  A: [k][mn] (AKMN) or [mn][k]; B: always [k][mn].
+struct Operands {
+  const uint16_t* A;
+  int64_t lda;
+  int a_mn0, a_mnend;
+  const uint16_t* B;
+  int64_t ldb;
+  int b_mn0, b_mnend;
+  int kbeg, kend;
+};
+
+// Barrier for LDS reuse: the waves have already waited for their own loads (vmcnt); no memory
+// fence (which would wait for every outstanding load) is wanted here.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// acc += A^T-or-A * B over k in [kbeg, kend).  kStages LDS stages; the DMA loads of step k+3 are
+// issued right after the barrier of step k, so three steps of loads are in flight while the MFMAs
+// of step k run.  Before the barrier of step k every wave waits (vmcnt) until only the loads of
+// the later steps are outstanding, so after the barrier stage k is complete in LDS for all waves.
+// Ends with a barrier, so the LDS may be reused right away.
+template <int MT, int NT, bool AKMN>
+__device__ __forceinline__ void mainloop(const Operands& o, uint16_t* sa, uint16_t* sb, int tid,
+                                         int wm, int wn, int lane, f32x16 (&acc)[MT][NT]) {
+  using C = Tile<MT, NT, AKMN>;
+  constexpr int I = C::IA + C::IB;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int nk = o.kend > o.kbeg ? (o.kend - o.kbeg + kBK - 1) / kBK : 0;
+  uint32_t oa[C::IA], ob[C::IB];
+  int kca[C::IA];
+  if (AKMN)
+    dma_offs_kmn<C::BM, C::IA>(o.lda, o.a_mn0, o.a_mnend, w, lane, oa);
+  else
+    dma_offs_mnk<C::IA>(o.lda, w, lane, oa, kca);
+  dma_offs_kmn<C::BN, C::IB>(o.ldb, o.b_mn0, o.b_mnend, w, lane, ob);
+  const __amdgpu_buffer_rsrc_t ra_rows =
+      make_rsrc(o.A + (int64_t)o.a_mn0 * o.lda, (int64_t)(o.a_mnend - o.a_mn0) * o.lda * 2);
+
+  auto issue = [&](int kt) {
+    const int stg = kt % kStages, k0 = o.kbeg + kt * kBK;
+    uint16_t* la = sa + stg * C::SA + w * C::IA * 512;
+    uint16_t* lb = sb + stg * C::SB + w * C::IB * 512;
+    if (AKMN) {
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(o.A + (int64_t)k0 * o.lda, (int64_t)(o.kend - k0) * o.lda * 2);
+#pragma unroll
+      for (int j = 0; j < C::IA; ++j) dma16(r, la + j * 512, oa[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::IA; ++j)
+        dma16(ra_rows, la + j * 512,
+              k0 + kca[j] < o.kend ? oa[j] + 2u * (uint32_t)k0 : kOutOfRange);
+    }
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(o.B + (int64_t)k0 * o.ldb, (int64_t)(o.kend - k0) * o.ldb * 2);
+#pragma unroll
+    for (int j = 0; j < C::IB; ++j) dma16(rb, lb + j * 512, ob[j]);
+  };
+
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st)
+    if (st < nk) issue(st);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int later = (nk - 1 - kt) < (kStages - 2) ? (nk - 1 - kt) : (kStages - 2);
+    if (later >= 2) wait_vm<2 * I>();
+    else if (later == 1) wait_vm<I>();
+    else wait_vm<0>();
+    lds_barrier();
+    if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
+    mma_stage<MT, NT, AKMN>(sa + (kt % kStages) * C::SA, sb + (kt % kStages) * C::SB, wm, wn,
+                            lane, acc);
+  }
+  lds_barrier();
+}
+
+template <int MT, int NT>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[MT][NT]) {
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 }
 
 // C[m][n] for the wavefront's MT x NT tiles, rows < mend and columns < nend only.
+// 32x32 accumulator layout: lane l holds column l % 32, rows 8 (r / 4) + 4 (l / 32) + r % 4.
 template <int MT, int NT>
 __device__ __forceinline__ void store_acc(float* __restrict__ out, int64_t ldo, int m0, int mend,
                                           int n0, int nend, int wm, int wn, int lane,
@@ -194,111 +316,73 @@ __device__ __forceinline__ void store_acc(float* __restrict__ out, int64_t ldo, 
     }
 }
 
-// dW[e] tile: reduction over the retained rows of expert e.  Blocks walk the experts in the order
-// of `order` (largest segment first), so the dispatcher hands out the longest tiles first.
-template <int MT, int NT, int BK>
+// dW: persistent.  sched[x] = number of experts dealt to die x; sched[kMaxXcd + x * (E_loc + 1)
+// + g] = its g-th expert.  The nb workgroups of die x take units u = i, i + nb, ... of that die's
+// list (unit = expert-major, tile-minor), so they sweep one expert's tiles together.
+template <int MT, int NT>
 __global__ __launch_bounds__(kThreads) void dw_bf16(const uint16_t* __restrict__ Gc,
                                                    const uint16_t* __restrict__ Phic,
                                                    const int32_t* __restrict__ cmp_off,
-                                                   const int32_t* __restrict__ order, int K_cap,
-                                                   int h, int d, float* __restrict__ dW) {
-  using C = Tile<MT, NT, BK, true, true>;
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][C::SA];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][C::SB];
-  const int tn = (d + C::BN - 1) / C::BN, tm = (h + C::BM - 1) / C::BM;
-  const int b = blockIdx.x, e = order[b / (tm * tn)], local = b % (tm * tn);
-  const int m0 = (local / tn) * C::BM, n0 = (local % tn) * C::BN;
+                                                   const int32_t* __restrict__ sched, int nxcd,
+                                                   int E_loc, int K_cap, int h, int d,
+                                                   float* __restrict__ dW) {
+  using C = Tile<MT, NT, true>;
+  __shared__ __attribute__((aligned(1024))) uint16_t sa[kStages * C::SA];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb[kStages * C::SB];
+  const int tn = (d + C::BN - 1) / C::BN, tm = (h + C::BM - 1) / C::BM, tpe = tm * tn;
+  const int x = blockIdx.x % nxcd, i = blockIdx.x / nxcd, nb = gridDim.x / nxcd;
+  const int units = sched[x] * tpe;
+  const int32_t* list = sched + kMaxXcd + x * (E_loc + 1);
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave, wm = wv >> 1, wn = wv & 1;
-  int s = cmp_off[e], t = cmp_off[e + 1];
-  s = s < 0 ? 0 : (s > K_cap ? K_cap : s);
-  t = t < s ? s : (t > K_cap ? K_cap : t);
   f32x16 acc[MT][NT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  const int nk = (t - s + BK - 1) / BK;
-  uint4 va[C::CA], vb[C::CB];
-  if (nk > 0) {
-    gload_kmn<C::BM, C::CA>(Gc, h, s, t, m0, h, tid, va);
-    gload_kmn<C::BN, C::CB>(Phic, d, s, t, n0, d, tid, vb);
-    sstore_kmn<C::BM, C::CA, C::PA>(sa[0], tid, va);
-    sstore_kmn<C::BN, C::CB, C::PB>(sb[0], tid, vb);
+  for (int u = i; u < units; u += nb) {
+    const int e = list[u / tpe], local = u % tpe;
+    const int m0 = (local / tn) * C::BM, n0 = (local % tn) * C::BN;
+    int s = cmp_off[e], t = cmp_off[e + 1];
+    s = s < 0 ? 0 : (s > K_cap ? K_cap : s);
+    t = t < s ? s : (t > K_cap ? K_cap : t);
+    const Operands o{Gc, h, m0, h, Phic, d, n0, d, s, t};
+    zero_acc(acc);
+    mainloop<MT, NT, true>(o, sa, sb, tid, wm, wn, lane, acc);
+    store_acc<MT, NT>(dW + (int64_t)e * h * d, d, m0, h, n0, d, wm, wn, lane, acc);
   }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k1 = s + (kt + 1) * BK;
-      gload_kmn<C::BM, C::CA>(Gc, h, k1, t, m0, h, tid, va);
-      gload_kmn<C::BN, C::CB>(Phic, d, k1, t, n0, d, tid, vb);
-    }
-    mma_stage<MT, NT, BK, true, true>(sa[cur], sb[cur], wm, wn, lane, acc);
-    if (more) {
-      sstore_kmn<C::BM, C::CA, C::PA>(sa[cur ^ 1], tid, va);
-      sstore_kmn<C::BN, C::CB, C::PB>(sb[cur ^ 1], tid, vb);
-    }
-    __syncthreads();
-  }
-  store_acc<MT, NT>(dW + (int64_t)e * h * d, d, m0, h, n0, d, wm, wn, lane, acc);
 }
 
-// dphi tile: rows [m0, m0 + BM) of one expert segment (from the tile table), reduction over h.
-template <int MT, int NT, int BK>
+// dphi: persistent.  Units = (row tile from the tile table, column tile), columns fastest; die x
+// owns the contiguous unit range [x * per, (x + 1) * per).
+template <int MT, int NT>
 __global__ __launch_bounds__(kThreads) void dx_bf16(const uint16_t* __restrict__ Gc,
                                                    const uint16_t* __restrict__ W,
                                                    const int32_t* __restrict__ cmp_off,
-                                                   const int32_t* __restrict__ tiles, int K_cap,
-                                                   int h, int d, float* __restrict__ dphi) {
-  using C = Tile<MT, NT, BK, false, true>;
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][C::SA];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][C::SB];
-  const int tile = blockIdx.x;
-  if (tile >= tiles[0]) return;
-  const int e = tiles[1 + 2 * tile], m0 = tiles[2 + 2 * tile];
-  int mend = cmp_off[e + 1];
-  mend = mend > K_cap ? K_cap : mend;
-  const int n0 = blockIdx.y * C::BN;
+                                                   const int32_t* __restrict__ tiles, int nxcd,
+                                                   int K_cap, int h, int d,
+                                                   float* __restrict__ dphi) {
+  using C = Tile<MT, NT, false>;
+  __shared__ __attribute__((aligned(1024))) uint16_t sa[kStages * C::SA];
+  __shared__ __attribute__((aligned(1024))) uint16_t sb[kStages * C::SB];
+  const int tn = (d + C::BN - 1) / C::BN;
+  const int total = tiles[0] * tn, per = (total + nxcd - 1) / nxcd;
+  const int x = blockIdx.x % nxcd, i = blockIdx.x / nxcd, nb = gridDim.x / nxcd;
+  const int u0 = x * per, u1 = u0 + per < total ? u0 + per : total;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave, wm = wv >> 1, wn = wv & 1;
   f32x16 acc[MT][NT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  const uint16_t* We = W + (int64_t)e * h * d;
-  const int nk = (h + BK - 1) / BK;
-  uint4 va[C::CA], vb[C::CB];
-  gload_mnk<BK, C::CA>(Gc, h, m0, mend, 0, h, tid, va);
-  gload_kmn<C::BN, C::CB>(We, d, 0, h, n0, d, tid, vb);
-  sstore_mnk<BK, C::CA, C::PA>(sa[0], tid, va);
-  sstore_kmn<C::BN, C::CB, C::PB>(sb[0], tid, vb);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k1 = (kt + 1) * BK;
-      gload_mnk<BK, C::CA>(Gc, h, m0, mend, k1, h, tid, va);
-      gload_kmn<C::BN, C::CB>(We, d, k1, h, n0, d, tid, vb);
-    }
-    mma_stage<MT, NT, BK, false, true>(sa[cur], sb[cur], wm, wn, lane, acc);
-    if (more) {
-      sstore_mnk<BK, C::CA, C::PA>(sa[cur ^ 1], tid, va);
-      sstore_kmn<C::BN, C::CB, C::PB>(sb[cur ^ 1], tid, vb);
-    }
-    __syncthreads();
+  for (int u = u0 + i; u < u1; u += nb) {
+    const int mt = u / tn, n0 = (u % tn) * C::BN;
+    const int e = tiles[1 + 2 * mt], m0 = tiles[2 + 2 * mt];
+    int mend = cmp_off[e + 1];
+    mend = mend > K_cap ? K_cap : mend;
+    const Operands o{Gc, h, m0, mend, W + (int64_t)e * h * d, d, n0, d, 0, h};
+    zero_acc(acc);
+    mainloop<MT, NT, false>(o, sa, sb, tid, wm, wn, lane, acc);
+    store_acc<MT, NT>(dphi, d, m0, mend, n0, d, wm, wn, lane, acc);
   }
-  store_acc<MT, NT>(dphi, d, m0, mend, n0, d, wm, wn, lane, acc);
 }
 
-// Experts ranked by retained rows, descending (ties by id): order[rank] = expert.
-__global__ __launch_bounds__(1024) void dw_order(const int32_t* __restrict__ cmp_off, int E_loc,
-                                                 int K_cap, int32_t* __restrict__ order) {
+// dW schedule: experts ranked by retained rows (descending, ties by id) and dealt to the dies in
+// a snake order (0, 1, .., n-1, n-1, .., 0, 0, ..), which balances the dies' total rows.
+__global__ __launch_bounds__(1024) void dw_schedule(const int32_t* __restrict__ cmp_off, int E_loc,
+                                                    int K_cap, int nxcd,
+                                                    int32_t* __restrict__ sched) {
   __shared__ int ke[1024];
   const int tid = threadIdx.x;
   if (tid < E_loc) {
@@ -308,14 +392,22 @@ __global__ __launch_bounds__(1024) void dw_order(const int32_t* __restrict__ cmp
     ke[tid] = t - s;
   }
   __syncthreads();
+  const int n2 = 2 * nxcd;
   if (tid < E_loc) {
     const int mine = ke[tid];
     int rank = 0;
-    for (int x = 0; x < E_loc; ++x) {
-      const int o = ke[x];
-      rank += (o > mine) || (o == mine && x < tid);
+    for (int y = 0; y < E_loc; ++y) {
+      const int o = ke[y];
+      rank += (o > mine) || (o == mine && y < tid);
     }
-    order[rank] = tid;
+    const int r = rank % n2, cyc = rank / n2;
+    const int bin = r < nxcd ? r : n2 - 1 - r;
+    const int pos = 2 * cyc + (r < nxcd ? 0 : 1);
+    sched[kMaxXcd + bin * (E_loc + 1) + pos] = tid;
+  }
+  if (tid < nxcd) {
+    const int full = E_loc / n2, rem = E_loc % n2;
+    sched[tid] = 2 * full + (rem > tid) + (rem > n2 - 1 - tid);
   }
 }
 
@@ -523,14 +615,46 @@ __global__ __launch_bounds__(1024) void dx_schedule(const int32_t* __restrict__ 
   if (tid == 0) tiles[0] = (int)(base_tiles < max_tiles ? base_tiles : max_tiles);
 }
 
-template <int MT, int NT, int BK>
-void launch_dw_bf16(const lrm_problem& p, const void* Gc, const void* Phic, const int32_t* cmp_off,
-                    const int32_t* order, float* dW, hipStream_t s) {
-  using C = Tile<MT, NT, BK, true, true>;
-  const int tiles = ((p.h + C::BM - 1) / C::BM) * ((p.d + C::BN - 1) / C::BN);
-  hipLaunchKernelGGL((dw_bf16<MT, NT, BK>), dim3((unsigned)(tiles * p.E_loc)), dim3(kThreads), 0, s,
-                     (const uint16_t*)Gc, (const uint16_t*)Phic, cmp_off, order, p.K_cap, p.h,
-                     p.d, dW);
+
+// Persistent grid: one workgroup per CU (the 131-147 KiB of LDS per workgroup allows one), and the
+// number of dies the workgroup ids are dealt over.
+struct Grid {
+  int blocks, nxcd;
+};
+
+Grid persistent_grid() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  const int n = cus[dev];
+  const int nxcd = (n % kMaxXcd == 0 && n >= 8 * kMaxXcd) ? kMaxXcd : 1;
+  return Grid{n / nxcd * nxcd, nxcd};
+}
+
+// Column-tile widths (measured on the Qwen3 share).  dW: 192 when it divides d (the 768-wide FFN
+// then has 4 column tiles, so an expert's dW is 8 x 4 = 32 tiles, one per CU of a die), else 256,
+// else 128.  dphi: 256 when it divides d (fewer, larger tiles), else 192, else 128.
+int pick_nt_dw(int d) { return d % 192 == 0 ? 3 : (d % 256 == 0 ? 4 : 2); }
+int pick_nt_dx(int d) { return d % 256 == 0 ? 4 : (d % 192 == 0 ? 3 : 2); }
+
+template <int NT>
+void launch_dw_nt(const lrm_problem& p, const void* Gc, const void* Phic, const int32_t* cmp_off,
+                  const int32_t* sched, float* dW, const Grid& g, hipStream_t s) {
+  hipLaunchKernelGGL((dw_bf16<4, NT>), dim3(g.blocks), dim3(kThreads), 0, s, (const uint16_t*)Gc,
+                     (const uint16_t*)Phic, cmp_off, sched, g.nxcd, p.E_loc, p.K_cap, p.h, p.d, dW);
+}
+
+template <int NT>
+void launch_dx_nt(const lrm_problem& p, const void* Gc, const void* W, const int32_t* cmp_off,
+                  const int32_t* tiles, float* dphi, const Grid& g, hipStream_t s) {
+  hipLaunchKernelGGL((dx_bf16<4, NT>), dim3(g.blocks), dim3(kThreads), 0, s, (const uint16_t*)Gc,
+                     (const uint16_t*)W, cmp_off, tiles, g.nxcd, p.K_cap, p.h, p.d, dphi);
 }
 
 }  // namespace
@@ -538,9 +662,15 @@ void launch_dw_bf16(const lrm_problem& p, const void* Gc, const void* Phic, cons
 hipError_t launch_dw(const lrm_problem& p, const void* Gc, const void* Phic, const int32_t* cmp_off,
                      float* dW, char* ws, const WsLayout& wl, hipStream_t s) {
   if (p.dtype == LRM_BF16) {
-    int32_t* order = (int32_t*)(ws + wl.order);
-    hipLaunchKernelGGL(dw_order, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, order);
-    launch_dw_bf16<LRM_DW_MT, LRM_DW_NT, LRM_DW_BK>(p, Gc, Phic, cmp_off, order, dW, s);
+    const Grid g = persistent_grid();
+    int32_t* sched = (int32_t*)(ws + wl.order);
+    hipLaunchKernelGGL(dw_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, g.nxcd,
+                       sched);
+    switch (pick_nt_dw(p.d)) {
+      case 3: launch_dw_nt<3>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
+      case 4: launch_dw_nt<4>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
+      default: launch_dw_nt<2>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
+    }
   } else {
     const dim3 grid((p.d + FBN - 1) / FBN, (p.h + FBM - 1) / FBM, p.E_loc);
     hipLaunchKernelGGL(dw_f32, grid, dim3(kThreads), 0, s, (const float*)Gc, (const float*)Phic,
@@ -553,14 +683,16 @@ hipError_t launch_dx(const lrm_problem& p, const void* Gc, const void* W, const 
                      float* dphi, char* ws, const WsLayout& wl, hipStream_t s) {
   int32_t* tiles = (int32_t*)(ws + wl.tiles);
   if (p.dtype == LRM_BF16) {
-    constexpr int MT = LRM_DX_MT, NT = LRM_DX_NT, BK = LRM_DX_BK;
-    using C = Tile<MT, NT, BK, false, true>;
-    const int64_t max_tiles = ((int64_t)p.K_cap + C::BM - 1) / C::BM + p.E_loc;
-    hipLaunchKernelGGL(dx_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, C::BM,
+    const Grid g = persistent_grid();
+    constexpr int BM = Tile<4, 2, false>::BM;
+    const int64_t max_tiles = ((int64_t)p.K_cap + BM - 1) / BM + p.E_loc;
+    hipLaunchKernelGGL(dx_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, BM,
                        max_tiles, tiles);
-    const dim3 grid((unsigned)max_tiles, (p.d + C::BN - 1) / C::BN);
-    hipLaunchKernelGGL((dx_bf16<MT, NT, BK>), grid, dim3(kThreads), 0, s, (const uint16_t*)Gc,
-                       (const uint16_t*)W, cmp_off, tiles, p.K_cap, p.h, p.d, dphi);
+    switch (pick_nt_dx(p.d)) {
+      case 3: launch_dx_nt<3>(p, Gc, W, cmp_off, tiles, dphi, g, s); break;
+      case 4: launch_dx_nt<4>(p, Gc, W, cmp_off, tiles, dphi, g, s); break;
+      default: launch_dx_nt<2>(p, Gc, W, cmp_off, tiles, dphi, g, s); break;
+    }
   } else {
     hipLaunchKernelGGL(dx_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, FBM,
                        wl.max_tiles, tiles);

@@ -300,6 +300,16 @@ def test_segment_sizes_and_ragged_tiles(dtype):
         full_compare(w, pol)
 
 
+@pytest.mark.parametrize("h,d", [(512, 384), (256, 512), (384, 1408), (2048, 200)])
+def test_gemm_tile_shapes(h, d):
+    # column tiles of 192 (d % 192 == 0), 256 (d % 256 == 0) and 128 (otherwise, ragged edge)
+    rng = np.random.default_rng(9)
+    rows = np.stack([rng.permutation(6)[:2] for _ in range(1500)])
+    w = custom(rows, E=6, e_lo=1, E_loc=4, h=h, d=d, dtype="bf16")
+    print(f"[case] tile shapes h={h} d={d}", flush=True)
+    full_compare(w, {"full": 0, "rho_num": 2, "rho_den": 3, "cap_abs": -1})
+
+
 def test_single_local_expert_and_no_local_pairs():
     rng = np.random.default_rng(4)
     rows = np.stack([rng.permutation(6)[:2] for _ in range(300)])
