@@ -7,7 +7,8 @@
 //
 // Two streaming launches, HBM-bound (about 2 flops per loaded element):
 //   token_sqnorm  ||g_t||^2 for all T tokens (one wavefront per row, 16-byte loads)
-//   row_score     ||phi_r||^2 per forward row, then the product with alpha^2 and ||g_t||^2
+//   row_score     ||phi_r||^2 per forward row (16 lanes per row, 4 rows per wavefront), then the
+//                 product with alpha^2 and ||g_t||^2
 // Squares of bf16/fp32 values are exact in float64, and the sums are accumulated in float64 with
 // a fixed lane assignment and a fixed butterfly, so two rows with equal contents give bitwise
 // equal scores wherever they sit; the final product is rounded once to float32.
@@ -84,6 +85,28 @@ __global__ __launch_bounds__(kBlock) void token_sqnorm(const uint4* __restrict__
   }
 }
 
+// ||phi_r||^2 and the score of 4 forward rows per wavefront: 16 lanes per row, each lane summing
+// every 16th chunk of its row, then a 16-lane butterfly (the same shape for every row).
+constexpr int kLanesPerRow = 16;
+constexpr int kRowsPerWave = kWave / kLanesPerRow;
+
+template <bool kBF16>
+__device__ __forceinline__ double add_chunk(double acc, uint4 a) {
+  const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (kBF16) {
+      const double x0 = bf16_lo(wa[i]), x1 = bf16_hi(wa[i]);
+      acc += x0 * x0;
+      acc += x1 * x1;
+    } else {
+      const double x = __uint_as_float(wa[i]);
+      acc += x * x;
+    }
+  }
+  return acc;
+}
+
 template <bool kBF16>
 __global__ __launch_bounds__(kBlock) void row_score(const uint4* __restrict__ phi, int chunks,
                                                     const int32_t* __restrict__ fwd_off, int E_loc,
@@ -92,21 +115,39 @@ __global__ __launch_bounds__(kBlock) void row_score(const uint4* __restrict__ ph
                                                     int64_t P, const double* __restrict__ gnorm,
                                                     float* __restrict__ score,
                                                     int32_t* __restrict__ err) {
-  const int lane = lane_id();
+  const int lane = lane_id(), sub = lane % kLanesPerRow;
   int L = fwd_off[E_loc];
   L = L < 0 ? 0 : (L > L_cap ? L_cap : L);
+  const int64_t groups = ((int64_t)L + kRowsPerWave - 1) / kRowsPerWave;
   const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
   int bad = 0;
-  for (int64_t r = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; r < L; r += nw) {
-    const int p = row_pair[r];
-    const double s = wave_sum(lane_sqsum<kBF16>(phi + r * chunks, chunks));
-    if (lane == 0) {
+  for (int64_t gi = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; gi < groups;
+       gi += nw) {
+    const int64_t r = gi * kRowsPerWave + lane / kLanesPerRow;
+    const bool live = r < L;
+    const int p = live ? row_pair[r] : 0;
+    const uint4* row = phi + (live ? r : 0) * chunks;
+    double acc = 0.0;
+    int c = sub;
+    // four chunks in flight per lane per step
+    for (; c + 3 * kLanesPerRow < chunks; c += 4 * kLanesPerRow) {
+      const uint4 a0 = load_nt(row + c), a1 = load_nt(row + c + kLanesPerRow);
+      const uint4 a2 = load_nt(row + c + 2 * kLanesPerRow), a3 = load_nt(row + c + 3 * kLanesPerRow);
+      acc = add_chunk<kBF16>(acc, a0);
+      acc = add_chunk<kBF16>(acc, a1);
+      acc = add_chunk<kBF16>(acc, a2);
+      acc = add_chunk<kBF16>(acc, a3);
+    }
+    for (; c < chunks; c += kLanesPerRow) acc = add_chunk<kBF16>(acc, load_nt(row + c));
+#pragma unroll
+    for (int o = kLanesPerRow / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+    if (live && sub == 0) {
       float out = 0.0f;
       if (p < 0 || p >= P) {
         bad |= LRM_DEVERR_INDEX;
       } else {
         const double a = (double)topk_w[p];
-        out = (float)(((a * a) * gnorm[p / k]) * s);
+        out = (float)(((a * a) * gnorm[p / k]) * acc);
         // Scores are products of squares: anything but a finite value >= +0 is an input error.
         if (!(out >= 0.0f && out <= 3.402823466e38f)) bad |= LRM_DEVERR_NONFINITE;
       }
@@ -127,7 +168,7 @@ hipError_t launch_score(const lrm_problem& p, const float* topk_w, const void* g
   const int gch = p.h * esz / 16, pch = p.d * esz / 16;
   // Persistent grids: enough wavefronts to keep every CU's memory pipeline full.
   const int64_t tb = ((int64_t)p.T + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int64_t lb = ((int64_t)p.L_cap + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t lb = ((int64_t)p.L_cap + 4 * kWavesPerBlock - 1) / (4 * kWavesPerBlock);
   const unsigned gblk = (unsigned)(tb < 4096 ? tb : 4096);
   const unsigned lblk = (unsigned)(lb < 4096 ? lb : 4096);
   const int64_t P = (int64_t)p.T * p.k;

@@ -8,8 +8,8 @@
 // One workgroup (16 wavefronts) per local expert:
 //   1. stage the segment's float32 score bit patterns in LDS (non-negative floats order like
 //      their unsigned bit patterns);
-//   2. MSB-first radix select, 4 passes of 8 bits, finds the q-th largest key T and how many
-//      keys equal to T must be kept (per-wavefront LDS histograms spread the atomics);
+//   2. MSB-first radix select, passes of 12, 10 and 10 bits, finds the q-th largest key T and
+//      how many keys equal to T must be kept;
 //   3. one ordered pass keeps key > T, and the first `need` keys == T in row order, writing the
 //      kept row ids ascending through a wavefront-ballot prefix sum and a cross-wave LDS scan.
 // Segments longer than the LDS stage are read from global memory in every pass instead.
@@ -22,6 +22,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kLdsKeys = 32768;   // 128 KiB of keys: a whole 32768-token segment fits on chip
+constexpr int kMaxBins = 4096;    // first radix digit: 12 bits
 
 __global__ __launch_bounds__(kThreads) void select_topq(const uint32_t* __restrict__ score,
                                                        const int32_t* __restrict__ fwd_off,
@@ -31,8 +32,8 @@ __global__ __launch_bounds__(kThreads) void select_topq(const uint32_t* __restri
                                                        int32_t* __restrict__ sel_row,
                                                        int32_t* __restrict__ err) {
   __shared__ uint32_t keys[kLdsKeys];
-  __shared__ int hist[kWaves][256];
-  __shared__ int wsum[4];
+  __shared__ int hist[kMaxBins];
+  __shared__ int wsum[kWaves + 1];
   __shared__ int pick[2];
   __shared__ int weq[kWaves], wkeep[kWaves];
 
@@ -65,54 +66,66 @@ __global__ __launch_bounds__(kThreads) void select_topq(const uint32_t* __restri
   const bool staged = n <= kLdsKeys;
   const uint32_t* src = score + r0;
   bool bad = false;
-  if (staged) {
-    for (int i = tid; i < n; i += kThreads) {
-      const uint32_t v = src[i];
-      bad |= v > 0x7F800000u;  // NaN or negative
-      keys[i] = v;
+  // Eight independent loads in flight per thread before any is used.
+  for (int base = 0; base < n; base += 8 * kThreads) {
+    uint32_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * kThreads + tid;
+      v[j] = i < n ? src[i] : 0u;
     }
-  } else {
-    for (int i = tid; i < n; i += kThreads) bad |= src[i] > 0x7F800000u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * kThreads + tid;
+      bad |= v[j] > 0x7F800000u;  // NaN or negative
+      if (staged && i < n) keys[i] = v[j];
+    }
   }
   if (bad) set_error(err, LRM_DEVERR_NONFINITE);
   __syncthreads();
 
-  // Radix select of the q-th largest key.
+  // Radix select of the q-th largest key: 3 passes of 12, 10 and 10 bits, MSB first.  Scores of
+  // one expert share their top bits (sign and most of the exponent), so the first digit also takes
+  // 4 mantissa bits: candidates then spread over many bins and the shared-histogram atomics rarely
+  // collide within a wavefront.
   uint32_t prefix = 0, mask = 0;
   int rank = q;  // rank (1-based, from the top) still to locate among the candidates
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+    const int nbins = pass == 0 ? 4096 : 1024;
+    const uint32_t dmask = (uint32_t)nbins - 1;
+    for (int i = tid; i < nbins; i += kThreads) hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += kThreads) {
       const uint32_t v = staged ? keys[i] : src[i];
-      if ((v & mask) == prefix) atomicAdd(&hist[w][(v >> shift) & 255u], 1);
+      if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & dmask], 1);
     }
     __syncthreads();
-    // Threads 0..255 (wavefronts 0..3): thread j takes digit 255 - j, so an inclusive scan over j
-    // counts the candidates whose digit is >= 255 - j.
-    const int dgt_j = 255 - tid;
+    // Thread t owns bins nbins-1-t*per .. nbins-per-t*per (descending); an exclusive scan over
+    // threads counts the candidates in all higher bins.
+    const int per = nbins / kThreads;
     int c = 0;
-    if (tid < 256) {
-#pragma unroll
-      for (int x = 0; x < kWaves; ++x) c += hist[x][dgt_j];
-    }
+    for (int j = 0; j < per; ++j) c += hist[nbins - 1 - tid * per - j];
     const int inc = wave_inclusive_scan(c);
-    if (tid < 256 && lane == kWave - 1) wsum[w] = inc;
+    if (lane == kWave - 1) wsum[w] = inc;
     __syncthreads();
-    if (tid < 256) {
-      int before = 0;
-      for (int x = 0; x < w; ++x) before += wsum[x];
-      const int ge = before + inc, gt = ge - c;
-      if (gt < rank && rank <= ge) {
-        pick[0] = dgt_j;
-        pick[1] = gt;
+    int before = 0;
+    for (int x = 0; x < w; ++x) before += wsum[x];
+    int cum = before + inc - c;
+    for (int j = 0; j < per; ++j) {
+      const int b = nbins - 1 - tid * per - j, hb = hist[b];
+      if (cum < rank && rank <= cum + hb) {
+        pick[0] = b;
+        pick[1] = cum;
       }
+      cum += hb;
     }
     __syncthreads();
     const int dgt = pick[0];
     rank -= pick[1];
     prefix |= (uint32_t)dgt << shift;
-    mask |= 255u << shift;
+    mask |= dmask << shift;
     __syncthreads();
   }
   const uint32_t thr = prefix;

@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--cpu-sample-experts", type=int, default=16)
     ap.add_argument("--rho1-steps", type=int, default=None,
                     help="timed steps of the full-retention pass (default steps/2; 0 skips it)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=512,
+                    help="after timing, copy a buffer of this size once (a plain copy kernel of "
+                         "known traffic, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE); 0 skips it")
     return ap.parse_args()
 
 
@@ -226,6 +229,15 @@ def main():
         out["rho1"] = {"value": info1["L"] / (ms1 * 1e-3), "ms_per_step": ms1,
                        "K_retained": info1["K"], "stages_ms": stages1,
                        "fractions": fractions(stages1, alg1, sp.dtype)}
+    if args.copy_calibration_mib > 0:
+        import torch
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, pol, args.cpu_sample_experts)
     print(json.dumps(out))
