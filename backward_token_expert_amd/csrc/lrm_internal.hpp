@@ -23,6 +23,7 @@ struct WsLayout {
   size_t gnorm;   // double [T]           ||g_t||^2
   size_t tiles;   // int32 [1 + 2*max_tiles] dx tile table: count, then (expert, row0) pairs
   size_t order;   // int32 [kMaxXcd + kMaxXcd * (E_loc + 1)] dW schedule: per-XCD expert lists
+  size_t inv;     // int32 [T*k]          compaction: pair id -> compacted row (validated on use)
   size_t total;
   int64_t nchunks;
   int64_t max_tiles;
@@ -46,6 +47,8 @@ inline WsLayout ws_layout(const lrm_problem& p) {
   off = align_up(off + (size_t)(1 + 2 * w.max_tiles) * 4, 256);
   w.order = off;
   off = align_up(off + (size_t)(kMaxXcd + kMaxXcd * (p.E_loc + 1)) * 4, 256);
+  w.inv = off;
+  off = align_up(off + (size_t)P * 4, 256);
   w.total = off;
   return w;
 }

@@ -163,9 +163,14 @@ lrm_status lrm_select(const lrm_problem* problem, const float* score, const int3
  *                                                      round-to-nearest-even to the element type)
  *   Phic[i]     = phi[r]                              (bit copy)
  *   sel_pair[i] = p
- *  in : sel_row int32 [K_cap]; row_pair int32 [L_cap]; cmp_off int32 [E_loc+1] (only
- *       cmp_off[E_loc] = K is read); topk_w; g; phi
+ *  in : sel_row int32 [K_cap], strictly ascending over [0, K) (as lrm_select writes it);
+ *       row_pair int32 [L_cap], distinct pair ids on the selected rows (as lrm_plan_quotas
+ *       writes it); cmp_off int32 [E_loc+1] (only cmp_off[E_loc] = K is read); topk_w; g; phi
  *  out: Gc [K_cap][h]; Phic [K_cap][d]; sel_pair int32 [K_cap]
+ * Each g[t] row is read once per call however many of its pairs are kept; the workspace holds a
+ * pair -> compacted-row map (T*k int32) that needs no clearing between calls.  A selected row out
+ * of [0, L_cap) or out of order, a pair id out of [0, T*k), or two selected rows with one pair id
+ * set LRM_DEVERR_INDEX; the rows concerned get sel_pair = -1 or undefined data.
  */
 lrm_status lrm_compact(const lrm_problem* problem, const int32_t* sel_row, const int32_t* row_pair,
                        const int32_t* cmp_off, const float* topk_w, const void* g,

@@ -393,6 +393,75 @@ def test_out_of_range_expert_id_sets_error_word():
     np.testing.assert_array_equal(cnt, np.bincount(valid, minlength=4))
 
 
+def _compact_with(P, bufs, inp, sel_host, rp_host, K):
+    """lrm_compact on a host-given selection / row map (the rest from the workload)."""
+    torch = _torch()
+    from backward_token_expert_amd import lrm
+    from backward_token_expert_amd.path import to_device
+    sel = torch.zeros_like(bufs.sel_row)
+    sel[:K] = to_device(np.asarray(sel_host, np.int32))
+    rp = torch.zeros_like(bufs.row_pair)
+    rp[:len(rp_host)] = to_device(np.asarray(rp_host, np.int32))
+    co = torch.zeros_like(bufs.cmp_off)
+    co[-1] = K
+    lrm.lrm_read_device_error(bufs.ws, clear=True)
+    lrm.lrm_compact(P, sel, rp, co, inp["topk_w"], inp["g"], inp["phi"], bufs.Gc, bufs.Phic,
+                    bufs.sel_pair, bufs.ws)
+    torch.cuda.synchronize()
+    return lrm.lrm_read_device_error(bufs.ws)
+
+
+def test_compaction_ignores_map_entries_of_earlier_calls():
+    """The pair -> row map in the workspace is never cleared: calls with different selections on
+    one workspace must each match the oracle's compaction of their own selection."""
+    from backward_token_expert_amd import path
+    from backward_token_expert_amd.path import to_host
+    w = C.workload(1, T=2048)
+    sp = w.spec
+    P = C.problem(sp)
+    bufs = path.DeviceBuffers(P)
+    inp = C.upload(w)
+    for full, rho in ((False, (1, 2)), (False, (1, 8)), (True, None), (False, (1, 3))):
+        pol = synth.policy(sp, full=full, rho=rho)
+        print(f"[case] compaction on a reused workspace, full={full} rho={rho}", flush=True)
+        o = C.oracle_run(w, pol, gemms=False)
+        K = int(o["cmp_off"][-1])
+        err = _compact_with(P, bufs, inp, o["sel_row"], o["row_pair"], K)
+        assert err == 0
+        bf = sp.dtype == "bf16"
+        g = dict(sel_row=o["sel_row"], sel_pair=to_host(bufs.sel_pair)[:K],
+                 Gc=to_host(bufs.Gc, bf)[:K], Phic=to_host(bufs.Phic, bf)[:K])
+        check_compact(g, o)
+
+
+def test_compaction_flags_unordered_or_shared_pairs():
+    from backward_token_expert_amd import path
+    from backward_token_expert_amd.path import to_host
+    w = C.workload(1, T=1024)
+    sp = w.spec
+    P = C.problem(sp)
+    bufs = path.DeviceBuffers(P)
+    inp = C.upload(w)
+    o = C.oracle_run(w, synth.policy(sp), gemms=False)
+    K = int(o["cmp_off"][-1])
+    sel, rp = o["sel_row"].copy(), o["row_pair"].copy()
+    print("[case] compaction of an in-order selection", flush=True)
+    assert _compact_with(P, bufs, inp, sel, rp, K) == 0
+    print("[case] compaction of a selection with two rows swapped", flush=True)
+    bad = sel.copy()
+    bad[[10, 11]] = bad[[11, 10]]
+    assert _compact_with(P, bufs, inp, bad, rp, K) & 32
+    print("[case] compaction with two selected rows naming one pair", flush=True)
+    rp2 = rp.copy()
+    rp2[sel[20]] = rp2[sel[21]]
+    assert _compact_with(P, bufs, inp, sel, rp2, K) & 32
+    print("[case] compaction with a selected row out of range", flush=True)
+    bad = sel.copy()
+    bad[-1] = P.L_cap
+    assert _compact_with(P, bufs, inp, bad, rp, K) & 32
+    assert to_host(bufs.sel_pair)[K - 1] == -1
+
+
 # ------------------------------------------------------------------------------------------------
 # determinism and graph capture
 # ------------------------------------------------------------------------------------------------
