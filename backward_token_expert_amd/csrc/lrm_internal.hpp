@@ -19,7 +19,8 @@ constexpr int kMaxXcd = 8;
 // Layout of the caller-provided workspace (byte offsets, all 256-byte aligned).
 struct WsLayout {
   size_t err;     // int32 error word, then reserved header words
-  size_t hist;    // int32 [nchunks][E]   per-chunk expert histograms / local prefixes
+  size_t hist;    // int32 [nchunks][E+1] per-chunk expert histograms / local prefixes; column E
+                  //                      counts expert ids outside [0, E)
   size_t gnorm;   // double [T]           ||g_t||^2
   size_t tiles;   // int32 [1 + 2*max_tiles] dx tile table: count, then (expert, row0) pairs
   size_t order;   // int32 [kMaxXcd + kMaxXcd * (E_loc + 1)] dW schedule: per-XCD expert lists
@@ -40,7 +41,7 @@ inline WsLayout ws_layout(const lrm_problem& p) {
   w.err = off;
   off += 256;
   w.hist = off;
-  off = align_up(off + (size_t)w.nchunks * p.E * 4, 256);
+  off = align_up(off + (size_t)w.nchunks * (p.E + 1) * 4, 256);
   w.gnorm = off;
   off = align_up(off + (size_t)p.T * 8, 256);
   w.tiles = off;

@@ -5,11 +5,12 @@
 // (counts and prefix offsets define the segments).  The quota cap follows the capacity rule
 // C = CF * mean load of "Expert Parallel Math Deep" ("Capacity and the exact drop-rate formula").
 //
-// Four launches, all sizes device-resident (no host round trip, as the TopoEP paper argues for
+// Three launches, all sizes device-resident (no host round trip, as the TopoEP paper argues for
 // planning in its host-plan latency model):
-//   plan_init    clear the sticky device error word
-//   plan_hist    one wavefront per chunk of kPlanChunk pairs: per-chunk expert histogram
-//   plan_scan    one workgroup: expert totals, per-chunk prefixes, fwd_off, quotas, cmp_off
+//   plan_hist    one wavefront per chunk of kPlanChunk pairs: per-chunk expert histogram, plus a
+//                column counting expert ids outside [0, E)
+//   plan_scan    one workgroup: expert totals, per-chunk prefixes, fwd_off, quotas, cmp_off, and
+//                the device error word (overwritten, which clears what earlier calls left)
 //   plan_scatter one wavefront per chunk: stable counting-sort scatter of the local pairs
 // The scatter ranks equal experts inside a wavefront with ballots (a 64-lane "match"), so the
 // layout is stable (pair index ascending within each expert) without any sort.
@@ -23,36 +24,37 @@ constexpr int kPlanBlock = 256;                 // 4 wavefronts, one chunk each
 constexpr int kChunksPerBlock = kPlanBlock / kWave;
 constexpr int kMaxE = 4096;
 
-__global__ void plan_init(int32_t* err) {
-  if (threadIdx.x == 0) *err = 0;
-}
+constexpr int kHistBatch = 4;  // index loads a lane issues before its LDS atomics
 
 __global__ __launch_bounds__(kPlanBlock) void plan_hist(const int32_t* __restrict__ idx, int64_t P,
                                                         int E, int64_t nchunks,
-                                                        int32_t* __restrict__ hist,
-                                                        int32_t* __restrict__ err) {
-  __shared__ int32_t h[kChunksPerBlock][kMaxE];
+                                                        int32_t* __restrict__ hist) {
+  __shared__ int32_t h[kChunksPerBlock][kMaxE + 1];
   const int w = threadIdx.x / kWave, lane = lane_id();
-  for (int i = threadIdx.x; i < kChunksPerBlock * E; i += kPlanBlock) h[i / E][i % E] = 0;
+  const int cols = E + 1;  // column E counts expert ids outside [0, E)
+  for (int i = threadIdx.x; i < kChunksPerBlock * cols; i += kPlanBlock) h[i / cols][i % cols] = 0;
   __syncthreads();
   const int64_t c = (int64_t)blockIdx.x * kChunksPerBlock + w;
-  bool bad = false;
   if (c < nchunks) {
     const int64_t p0 = c * kPlanChunk;
-    for (int r = 0; r < kPlanChunk; r += kWave) {
-      const int64_t p = p0 + r + lane;
-      if (p < P) {
-        const int e = idx[p];
-        if (e >= 0 && e < E) atomicAdd(&h[w][e], 1);
-        else bad = true;
+    for (int r = 0; r < kPlanChunk; r += kHistBatch * kWave) {
+      int e[kHistBatch];
+#pragma unroll
+      for (int u = 0; u < kHistBatch; ++u) {
+        const int64_t p = p0 + r + u * kWave + lane;
+        e[u] = p < P ? idx[p] : -2;
+      }
+#pragma unroll
+      for (int u = 0; u < kHistBatch; ++u) {
+        if (e[u] == -2) continue;
+        atomicAdd(&h[w][(e[u] >= 0 && e[u] < E) ? e[u] : E], 1);
       }
     }
   }
-  if (bad) set_error(err, LRM_DEVERR_EXPERT_ID);
   __syncthreads();
-  for (int i = threadIdx.x; i < kChunksPerBlock * E; i += kPlanBlock) {
-    const int64_t cc = (int64_t)blockIdx.x * kChunksPerBlock + i / E;
-    if (cc < nchunks) hist[cc * E + i % E] = h[i / E][i % E];
+  for (int i = threadIdx.x; i < kChunksPerBlock * cols; i += kPlanBlock) {
+    const int64_t cc = (int64_t)blockIdx.x * kChunksPerBlock + i / cols;
+    if (cc < nchunks) hist[cc * cols + i % cols] = h[i / cols][i % cols];
   }
 }
 
@@ -75,6 +77,8 @@ __device__ int block_exclusive_scan_1024(int v, int* sh /* >= 17 ints */, int* t
   return res;
 }
 
+constexpr int kScanBatch = 8;
+
 __global__ __launch_bounds__(1024) void plan_scan(int32_t* __restrict__ hist, int64_t nchunks,
                                                   int E, int e_lo, int E_loc, int L_cap, int K_cap,
                                                   lrm_quota_policy pol, int32_t* __restrict__ counts,
@@ -85,16 +89,25 @@ __global__ __launch_bounds__(1024) void plan_scan(int32_t* __restrict__ hist, in
   __shared__ int part[16][64];
   __shared__ int nloc[1024];
   __shared__ int sh[32];
+  __shared__ int nbad;
   const int tid = threadIdx.x, sub = tid & 63, grp = tid >> 6;
   const int64_t cpg = (nchunks + 15) / 16;
   const int64_t c0 = grp * cpg, c1 = (c0 + cpg < nchunks) ? c0 + cpg : nchunks;
 
-  // Phase A: expert totals; per-chunk exclusive prefixes (in place) for the local experts.
-  for (int e0 = 0; e0 < E; e0 += 64) {
+  // Phase A: expert totals; per-chunk exclusive prefixes (in place) for the local experts.  Each
+  // thread walks its contiguous chunk range of one column with kScanBatch loads in flight.
+  const int cols = E + 1;
+  for (int e0 = 0; e0 < cols; e0 += 64) {
     const int e = e0 + sub;
     int s = 0;
-    if (e < E)
-      for (int64_t c = c0; c < c1; ++c) s += hist[c * E + e];
+    if (e < cols)
+      for (int64_t c = c0; c < c1; c += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) v[u] = c + u < c1 ? hist[(c + u) * cols + e] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) s += v[u];
+      }
     part[grp][sub] = s;
     __syncthreads();
     if (tid < 64) {
@@ -108,15 +121,24 @@ __global__ __launch_bounds__(1024) void plan_scan(int32_t* __restrict__ hist, in
         counts[e0 + tid] = run;
         const int el = e0 + tid - e_lo;
         if (el >= 0 && el < E_loc) nloc[el] = run;
+      } else if (e0 + tid == E) {
+        nbad = run;
       }
     }
     __syncthreads();
     if (e < E && e >= e_lo && e < e_lo + E_loc) {
       int run = part[grp][sub];
-      for (int64_t c = c0; c < c1; ++c) {
-        const int v = hist[c * E + e];
-        hist[c * E + e] = run;
-        run += v;
+      for (int64_t c = c0; c < c1; c += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) v[u] = c + u < c1 ? hist[(c + u) * cols + e] : 0;
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) {
+          if (c + u < c1) {
+            hist[(c + u) * cols + e] = run;
+            run += v[u];
+          }
+        }
       }
     }
     __syncthreads();
@@ -131,10 +153,7 @@ __global__ __launch_bounds__(1024) void plan_scan(int32_t* __restrict__ hist, in
   const int seg = f1 - f0;
   const int Lc = L < L_cap ? L : L_cap;
   if (tid < E_loc) fwd_off[tid] = f0;
-  if (tid == 0) {
-    fwd_off[E_loc] = Lc;
-    if (L > L_cap) set_error(err, LRM_DEVERR_L_CAP);
-  }
+  if (tid == 0) fwd_off[E_loc] = Lc;
   int q = 0;
   if (tid < E_loc) {
     if (pol.full) {
@@ -156,7 +175,9 @@ __global__ __launch_bounds__(1024) void plan_scan(int32_t* __restrict__ hist, in
   }
   if (tid == 0) {
     cmp_off[E_loc] = K < K_cap ? K : K_cap;
-    if (K > K_cap) set_error(err, LRM_DEVERR_K_CAP);
+    // The first call of a sequence: its error word replaces whatever earlier calls left.
+    *err = (nbad ? LRM_DEVERR_EXPERT_ID : 0) | (L > L_cap ? LRM_DEVERR_L_CAP : 0) |
+           (K > K_cap ? LRM_DEVERR_K_CAP : 0);
   }
 }
 
@@ -170,33 +191,42 @@ __global__ __launch_bounds__(kPlanBlock) void plan_scatter(const int32_t* __rest
   const int w = threadIdx.x / kWave, lane = lane_id();
   const int64_t c = (int64_t)blockIdx.x * kChunksPerBlock + w;
   if (c >= nchunks) return;  // whole wavefront leaves; no block barrier follows
-  for (int i = lane; i < E_loc; i += kWave) base[w][i] = fwd_off[i] + hist[c * E + e_lo + i];
+  for (int i = lane; i < E_loc; i += kWave) base[w][i] = fwd_off[i] + hist[c * (E + 1) + e_lo + i];
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const uint64_t lt = lanemask_lt();
   const int64_t p0 = c * kPlanChunk;
-  for (int r = 0; r < kPlanChunk; r += kWave) {
-    const int64_t p = p0 + r + lane;
-    int e = p < P ? idx[p] : -1;
-    const bool local = e >= e_lo && e < e_lo + E_loc;
-    const int el = local ? e - e_lo : 0;
-    uint64_t peers = ballot(local);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (el >> b) & 1;
-      const uint64_t m = ballot(bit);
-      peers &= bit ? m : ~m;
+  for (int r0 = 0; r0 < kPlanChunk; r0 += kHistBatch * kWave) {
+    int ev[kHistBatch];
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u) {
+      const int64_t p = p0 + r0 + u * kWave + lane;
+      ev[u] = p < P ? idx[p] : -1;
     }
-    const int leader = local ? __builtin_ctzll(peers) : lane;
-    int old = 0;
-    if (local && leader == lane) {
-      old = base[w][el];
-      base[w][el] = old + __builtin_popcountll(peers);
-    }
-    old = __shfl(old, leader, kWave);
-    if (local) {
-      const int row = old + __builtin_popcountll(peers & lt);
-      if (row < fwd_off[el + 1]) row_pair[row] = (int32_t)p;
+#pragma unroll
+    for (int u = 0; u < kHistBatch; ++u) {
+      const int64_t p = p0 + r0 + u * kWave + lane;
+      const int e = ev[u];
+      const bool local = e >= e_lo && e < e_lo + E_loc;
+      const int el = local ? e - e_lo : 0;
+      uint64_t peers = ballot(local);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (el >> b) & 1;
+        const uint64_t m = ballot(bit);
+        peers &= bit ? m : ~m;
+      }
+      const int leader = local ? __builtin_ctzll(peers) : lane;
+      int old = 0;
+      if (local && leader == lane) {
+        old = base[w][el];
+        base[w][el] = old + __builtin_popcountll(peers);
+      }
+      old = __shfl(old, leader, kWave);
+      if (local) {
+        const int row = old + __builtin_popcountll(peers & lt);
+        if (row < fwd_off[el + 1]) row_pair[row] = (int32_t)p;
+      }
     }
   }
 }
@@ -212,9 +242,8 @@ hipError_t launch_plan(const lrm_problem& p, const lrm_quota_policy& pol, const 
   const unsigned nblk = (unsigned)((wl.nchunks + kChunksPerBlock - 1) / kChunksPerBlock);
   int nbits = 0;
   while ((1 << nbits) < p.E_loc) ++nbits;
-  hipLaunchKernelGGL(plan_init, dim3(1), dim3(64), 0, s, err);
   hipLaunchKernelGGL(plan_hist, dim3(nblk), dim3(kPlanBlock), 0, s, topk_idx, P, p.E, wl.nchunks,
-                     hist, err);
+                     hist);
   hipLaunchKernelGGL(plan_scan, dim3(1), dim3(1024), 0, s, hist, wl.nchunks, p.E, p.e_lo, p.E_loc,
                      p.L_cap, p.K_cap, pol, counts, fwd_off, quota, cmp_off, err);
   hipLaunchKernelGGL(plan_scatter, dim3(nblk), dim3(kPlanBlock), 0, s, topk_idx, P, p.E, p.e_lo,

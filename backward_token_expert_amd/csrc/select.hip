@@ -8,10 +8,12 @@
 // One workgroup (16 wavefronts) per local expert:
 //   1. stage the segment's float32 score bit patterns in LDS (non-negative floats order like
 //      their unsigned bit patterns);
-//   2. MSB-first radix select, passes of 12, 10 and 10 bits, finds the q-th largest key T and
-//      how many keys equal to T must be kept;
-//   3. one ordered pass keeps key > T, and the first `need` keys == T in row order, writing the
-//      kept row ids ascending through a wavefront-ballot prefix sum and a cross-wave LDS scan.
+//   2. MSB-first radix select over bits 30..0 in digits of 12, 10 and 9 bits finds the q-th
+//      largest key T and how many keys equal to T must be kept; after the first digit the keys
+//      still in play are gathered into a short list that the later digits scan;
+//   3. each wavefront owns a contiguous run of rows: it counts its keys > T and == T, one
+//      barrier publishes the counts, and each wavefront then writes its kept rows (key > T, or
+//      key == T among the first `need` tied rows) in row order with ballot prefix sums.
 // Segments longer than the LDS stage are read from global memory in every pass instead.
 #include "lrm_device.hpp"
 #include "lrm_internal.hpp"
@@ -23,6 +25,8 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kLdsKeys = 32768;   // 128 KiB of keys: a whole 32768-token segment fits on chip
 constexpr int kMaxBins = 4096;    // first radix digit: 12 bits
+constexpr int kCandBase = 1024;   // candidate list: histogram words past the later digits' bins
+constexpr int kMaxCand = kMaxBins - kCandBase;
 
 __global__ __launch_bounds__(kThreads) void select_topq(const uint32_t* __restrict__ score,
                                                        const int32_t* __restrict__ fwd_off,
@@ -34,8 +38,10 @@ __global__ __launch_bounds__(kThreads) void select_topq(const uint32_t* __restri
   __shared__ uint32_t keys[kLdsKeys];
   __shared__ int hist[kMaxBins];
   __shared__ int wsum[kWaves + 1];
-  __shared__ int pick[2];
+  __shared__ int pick[3];
   __shared__ int weq[kWaves], wkeep[kWaves];
+  __shared__ int ncand;
+  uint32_t* cand = (uint32_t*)(hist + kCandBase);
 
   const int e = blockIdx.x;
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
@@ -66,7 +72,8 @@ __global__ __launch_bounds__(kThreads) void select_topq(const uint32_t* __restri
   const bool staged = n <= kLdsKeys;
   const uint32_t* src = score + r0;
   bool bad = false;
-  // Eight independent loads in flight per thread before any is used.
+  // Eight independent loads in flight per thread before any is used.  A NaN or negative score is
+  // flagged and ranked as +0, so every key below has its sign bit clear.
   for (int base = 0; base < n; base += 8 * kThreads) {
     uint32_t v[8];
 #pragma unroll
@@ -77,36 +84,54 @@ __global__ __launch_bounds__(kThreads) void select_topq(const uint32_t* __restri
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int i = base + j * kThreads + tid;
-      bad |= v[j] > 0x7F800000u;  // NaN or negative
-      if (staged && i < n) keys[i] = v[j];
+      bad |= v[j] > 0x7F800000u;
+      if (staged && i < n) keys[i] = v[j] > 0x7F800000u ? 0u : v[j];
     }
   }
   if (bad) set_error(err, LRM_DEVERR_NONFINITE);
+  if (tid == 0) ncand = 0;
   __syncthreads();
+  auto key_at = [&](int i) -> uint32_t {
+    if (staged) return keys[i];
+    const uint32_t v = src[i];
+    return v > 0x7F800000u ? 0u : v;
+  };
 
-  // Radix select of the q-th largest key: 3 passes of 12, 10 and 10 bits, MSB first.  Scores of
-  // one expert share their top bits (sign and most of the exponent), so the first digit also takes
-  // 4 mantissa bits: candidates then spread over many bins and the shared-histogram atomics rarely
-  // collide within a wavefront.
+  // Radix select of the q-th largest key over bits 30..0, MSB first, in digits of 12, 10 and 9
+  // bits.  The first digit spans the whole exponent and 4 mantissa bits, so one expert's scores
+  // spread over many bins; the keys matching it (the candidates) are then gathered into a short
+  // list when it fits, and the last two digits are counted over that list only.
   uint32_t prefix = 0, mask = 0;
   int rank = q;  // rank (1-based, from the top) still to locate among the candidates
+  bool use_cand = false;
+  int nc = 0;
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
-    const int nbins = pass == 0 ? 4096 : 1024;
+    const int shift = pass == 0 ? 19 : (pass == 1 ? 9 : 0);
+    const int nbins = pass == 0 ? 4096 : (pass == 1 ? 1024 : 512);
     const uint32_t dmask = (uint32_t)nbins - 1;
     for (int i = tid; i < nbins; i += kThreads) hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kThreads) {
-      const uint32_t v = staged ? keys[i] : src[i];
-      if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & dmask], 1);
+    if (use_cand) {
+      for (int i = tid; i < nc; i += kThreads) {
+        const uint32_t v = cand[i];
+        if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & dmask], 1);
+      }
+    } else {
+      for (int i = tid; i < n; i += kThreads) {
+        const uint32_t v = key_at(i);
+        if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & dmask], 1);
+      }
     }
     __syncthreads();
     // Thread t owns bins nbins-1-t*per .. nbins-per-t*per (descending); an exclusive scan over
     // threads counts the candidates in all higher bins.
-    const int per = nbins / kThreads;
+    const int per = (nbins + kThreads - 1) / kThreads;
     int c = 0;
-    for (int j = 0; j < per; ++j) c += hist[nbins - 1 - tid * per - j];
+    for (int j = 0; j < per; ++j) {
+      const int b = nbins - 1 - tid * per - j;
+      c += b >= 0 ? hist[b] : 0;
+    }
     const int inc = wave_inclusive_scan(c);
     if (lane == kWave - 1) wsum[w] = inc;
     __syncthreads();
@@ -114,57 +139,83 @@ __global__ __launch_bounds__(kThreads) void select_topq(const uint32_t* __restri
     for (int x = 0; x < w; ++x) before += wsum[x];
     int cum = before + inc - c;
     for (int j = 0; j < per; ++j) {
-      const int b = nbins - 1 - tid * per - j, hb = hist[b];
-      if (cum < rank && rank <= cum + hb) {
+      const int b = nbins - 1 - tid * per - j;
+      const int hb = b >= 0 ? hist[b] : 0;
+      if (b >= 0 && cum < rank && rank <= cum + hb) {
         pick[0] = b;
         pick[1] = cum;
+        pick[2] = hb;
       }
       cum += hb;
     }
     __syncthreads();
     const int dgt = pick[0];
     rank -= pick[1];
+    const int in_bin = pick[2];
     prefix |= (uint32_t)dgt << shift;
     mask |= dmask << shift;
+    if (pass == 0 && in_bin <= kMaxCand) {
+      // Gather the candidates of the chosen first digit (any order: only values matter here).
+      // The list aliases the top of the histogram, which the later digits do not use.
+      for (int base = 0; base < n; base += kThreads) {
+        const int i = base + tid;
+        const uint32_t v = i < n ? key_at(i) : 0u;
+        const bool m = i < n && (v & mask) == prefix;
+        const uint64_t bm = ballot(m);
+        int slot = 0;
+        if (lane == 0 && bm) slot = atomicAdd(&ncand, __builtin_popcountll(bm));
+        slot = __shfl(slot, 0, kWave);
+        if (m) cand[slot + __builtin_popcountll(bm & lanemask_lt())] = v;
+      }
+      use_cand = true;
+    }
     __syncthreads();
+    if (pass == 0) nc = ncand;
   }
   const uint32_t thr = prefix;
   const int need = rank;  // keys equal to thr that are kept, first in row order
 
-  // Ordered output pass.
+  // Ordered output: wavefront w owns the contiguous rows [w*chunk, (w+1)*chunk).  One pass counts
+  // each wave's keys above and equal to thr; after one barrier every wave knows how many rows the
+  // waves before it keep and how many tied keys they hold, and writes its kept rows in row order
+  // with ballot prefix sums (no further barriers).
+  const int chunk = ((n + kWaves - 1) / kWaves + kWave - 1) / kWave * kWave;
+  const int c0 = w * chunk < n ? w * chunk : n;
+  const int c1 = c0 + chunk < n ? c0 + chunk : n;
+  int n_eq = 0, n_gt = 0;
+  for (int i = c0 + lane; i < c1; i += kWave) {
+    const uint32_t v = key_at(i);
+    n_eq += v == thr;
+    n_gt += v > thr;
+  }
+  n_eq = wave_sum_int(n_eq);
+  n_gt = wave_sum_int(n_gt);
+  if (lane == 0) {
+    weq[w] = n_eq;
+    wkeep[w] = n_gt;
+  }
+  __syncthreads();
+  int eq_before = 0, pos = 0;
+  for (int x = 0; x < w; ++x) {
+    const int e_x = weq[x];
+    int tied = need - eq_before;
+    tied = tied < 0 ? 0 : (tied > e_x ? e_x : tied);
+    pos += wkeep[x] + tied;
+    eq_before += e_x;
+  }
   const uint64_t lt = lanemask_lt();
-  int run_eq = 0, run_keep = 0;
-  for (int base = 0; base < n; base += kThreads) {
-    const int i = base + tid;
-    const bool valid = i < n;
-    const uint32_t v = valid ? (staged ? keys[i] : src[i]) : 0u;
+  for (int base = c0; base < c1; base += kWave) {
+    const int i = base + lane;
+    const bool valid = i < c1;
+    const uint32_t v = valid ? key_at(i) : 0u;
     const bool is_eq = valid && v == thr;
-    const bool is_gt = valid && v > thr;
     const uint64_t beq = ballot(is_eq);
-    if (lane == 0) weq[w] = __builtin_popcountll(beq);
-    __syncthreads();
-    int eq_before = run_eq + __builtin_popcountll(beq & lt);
-    int eq_total = 0;
-    for (int x = 0; x < kWaves; ++x) {
-      const int c = weq[x];
-      if (x < w) eq_before += c;
-      eq_total += c;
-    }
-    const bool keep = is_gt || (is_eq && eq_before < need);
+    const bool keep = (valid && v > thr) || (is_eq && eq_before + __builtin_popcountll(beq & lt) < need);
     const uint64_t bk = ballot(keep);
-    if (lane == 0) wkeep[w] = __builtin_popcountll(bk);
-    __syncthreads();
-    int pos = run_keep + __builtin_popcountll(bk & lt);
-    int keep_total = 0;
-    for (int x = 0; x < kWaves; ++x) {
-      const int c = wkeep[x];
-      if (x < w) pos += c;
-      keep_total += c;
-    }
-    if (keep && pos < q) sel_row[o0 + pos] = r0 + i;
-    run_eq += eq_total;
-    run_keep += keep_total;
-    __syncthreads();
+    const int at = pos + __builtin_popcountll(bk & lt);
+    if (keep && at < q) sel_row[o0 + at] = r0 + i;
+    pos += __builtin_popcountll(bk);
+    eq_before += __builtin_popcountll(beq);
   }
 }
 
