@@ -27,6 +27,217 @@ constexpr int kLdsKeys = 32768;   // 128 KiB of keys: a whole 32768-token segmen
 constexpr int kMaxBins = 4096;    // first radix digit: 12 bits
 constexpr int kCandBase = 1024;   // candidate list: histogram words past the later digits' bins
 constexpr int kMaxCand = kMaxBins - kCandBase;
+constexpr int kBatch = 8;         // keys a thread loads before using them (strided passes)
+constexpr int kOutBatch = 4;      // 64-key groups a wavefront loads ahead in the output pass
+
+struct SelectSmem {
+  uint32_t keys[kLdsKeys];
+  int hist[kMaxBins];  // radix bins; words from kCandBase on also hold the candidate list
+  int wsum[kWaves + 1];
+  int pick[3];
+  int weq[kWaves], wkeep[kWaves];
+  int ncand;
+};
+
+// Everything after the early exits; kStaged: the segment's keys are held in LDS.
+template <bool kStaged>
+__device__ __forceinline__ void select_segment(SelectSmem& sm, const uint32_t* __restrict__ src,
+                                               int n, int q, int r0, int o0,
+                                               int32_t* __restrict__ sel_row,
+                                               int32_t* __restrict__ err) {
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  uint32_t* sm_cand = (uint32_t*)(sm.hist + kCandBase);
+  // A NaN or negative score is flagged and ranked as +0, so every key has its sign bit clear.
+  auto sanitize = [](uint32_t v) -> uint32_t { return v > 0x7F800000u ? 0u : v; };
+  auto key_at = [&](int i) -> uint32_t { return kStaged ? sm.keys[i] : sanitize(src[i]); };
+
+  for (int i = tid; i < kMaxBins; i += kThreads) sm.hist[i] = 0;
+  if (tid == 0) sm.ncand = 0;
+  __syncthreads();
+
+  // Stage the keys in LDS and count the first radix digit (bits 30..19) on the way, kBatch
+  // independent loads in flight per thread.
+  bool bad = false;
+  for (int base = 0; base < n; base += kBatch * kThreads) {
+    uint32_t v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + j * kThreads + tid;
+      v[j] = i < n ? src[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + j * kThreads + tid;
+      if (i < n) {
+        bad |= v[j] > 0x7F800000u;
+        const uint32_t k = sanitize(v[j]);
+        if (kStaged) sm.keys[i] = k;
+        atomicAdd(&sm.hist[k >> 19], 1);
+      }
+    }
+  }
+  if (bad) set_error(err, LRM_DEVERR_NONFINITE);
+  __syncthreads();
+
+  // Radix select of the q-th largest key over bits 30..0, MSB first, in digits of 12, 10 and 9
+  // bits.  The first digit spans the whole exponent and 4 mantissa bits, so one expert's scores
+  // spread over many bins; the keys matching it (the candidates) are then gathered into a short
+  // list when it fits, and the last two digits are counted over that list only.
+  uint32_t prefix = 0, mask = 0;
+  int rank = q;  // rank (1-based, from the top) still to locate among the candidates
+  bool use_cand = false;
+  int nc = 0;
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 19 : (pass == 1 ? 9 : 0);
+    const int nbins = pass == 0 ? 4096 : (pass == 1 ? 1024 : 512);
+    const uint32_t dmask = (uint32_t)nbins - 1;
+    if (pass > 0) {
+      for (int i = tid; i < nbins; i += kThreads) sm.hist[i] = 0;
+      __syncthreads();
+      const int cnt = use_cand ? nc : n;
+      for (int base = 0; base < cnt; base += kBatch * kThreads) {
+        uint32_t v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int i = base + j * kThreads + tid;
+          v[j] = i < cnt ? (use_cand ? sm_cand[i] : key_at(i)) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int i = base + j * kThreads + tid;
+          if (i < cnt && (v[j] & mask) == prefix) atomicAdd(&sm.hist[(v[j] >> shift) & dmask], 1);
+        }
+      }
+      __syncthreads();
+    }
+    // Thread t owns bins nbins-1-t*per .. nbins-per-t*per (descending); an exclusive scan over
+    // threads counts the candidates in all higher bins.
+    const int per = (nbins + kThreads - 1) / kThreads;
+    int c = 0;
+    for (int j = 0; j < per; ++j) {
+      const int b = nbins - 1 - tid * per - j;
+      c += b >= 0 ? sm.hist[b] : 0;
+    }
+    const int inc = wave_inclusive_scan(c);
+    if (lane == kWave - 1) sm.wsum[w] = inc;
+    __syncthreads();
+    int before = 0;
+    for (int x = 0; x < w; ++x) before += sm.wsum[x];
+    int cum = before + inc - c;
+    for (int j = 0; j < per; ++j) {
+      const int b = nbins - 1 - tid * per - j;
+      const int hb = b >= 0 ? sm.hist[b] : 0;
+      if (b >= 0 && cum < rank && rank <= cum + hb) {
+        sm.pick[0] = b;
+        sm.pick[1] = cum;
+        sm.pick[2] = hb;
+      }
+      cum += hb;
+    }
+    __syncthreads();
+    const int dgt = sm.pick[0];
+    rank -= sm.pick[1];
+    const int in_bin = sm.pick[2];
+    prefix |= (uint32_t)dgt << shift;
+    mask |= dmask << shift;
+    if (pass == 0 && in_bin <= kMaxCand) {
+      // Gather the candidates of the chosen first digit (any order: only values matter here),
+      // one slot reservation per wavefront and batch.  The list aliases the top of the
+      // histogram, which the later digits do not use.
+      for (int base = 0; base < n; base += kBatch * kThreads) {
+        uint32_t v[kBatch];
+        uint64_t bm[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int i = base + j * kThreads + tid;
+          v[j] = i < n ? key_at(i) : 0u;
+        }
+        int tot = 0;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int i = base + j * kThreads + tid;
+          bm[j] = ballot(i < n && (v[j] & mask) == prefix);
+          tot += __builtin_popcountll(bm[j]);
+        }
+        int slot = 0;
+        if (lane == 0 && tot) slot = atomicAdd(&sm.ncand, tot);
+        slot = __shfl(slot, 0, kWave);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if ((bm[j] >> lane) & 1) sm_cand[slot + __builtin_popcountll(bm[j] & lt)] = v[j];
+          slot += __builtin_popcountll(bm[j]);
+        }
+      }
+      use_cand = true;
+    }
+    __syncthreads();
+    if (pass == 0) nc = sm.ncand;
+  }
+  const uint32_t thr = prefix;
+  const int need = rank;  // keys equal to thr that are kept, first in row order
+
+  // Ordered output: wavefront w owns the contiguous rows [w*chunk, (w+1)*chunk).  One pass counts
+  // each wave's keys above and equal to thr; after one barrier every wave knows how many rows the
+  // waves before it keep and how many tied keys they hold, and writes its kept rows in row order
+  // with ballot prefix sums (no further barriers).
+  const int chunk = ((n + kWaves - 1) / kWaves + kWave - 1) / kWave * kWave;
+  const int c0 = w * chunk < n ? w * chunk : n;
+  const int c1 = c0 + chunk < n ? c0 + chunk : n;
+  int n_eq = 0, n_gt = 0;
+  for (int base = c0; base < c1; base += kOutBatch * kWave) {
+    uint32_t v[kOutBatch];
+#pragma unroll
+    for (int u = 0; u < kOutBatch; ++u) {
+      const int i = base + u * kWave + lane;
+      v[u] = i < c1 ? key_at(i) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kOutBatch; ++u) {
+      const bool valid = base + u * kWave + lane < c1;
+      n_eq += valid && v[u] == thr;
+      n_gt += valid && v[u] > thr;
+    }
+  }
+  n_eq = wave_sum_int(n_eq);
+  n_gt = wave_sum_int(n_gt);
+  if (lane == 0) {
+    sm.weq[w] = n_eq;
+    sm.wkeep[w] = n_gt;
+  }
+  __syncthreads();
+  int eq_before = 0, pos = 0;
+  for (int x = 0; x < w; ++x) {
+    const int e_x = sm.weq[x];
+    int tied = need - eq_before;
+    tied = tied < 0 ? 0 : (tied > e_x ? e_x : tied);
+    pos += sm.wkeep[x] + tied;
+    eq_before += e_x;
+  }
+  for (int base = c0; base < c1; base += kOutBatch * kWave) {
+    uint32_t v[kOutBatch];
+#pragma unroll
+    for (int u = 0; u < kOutBatch; ++u) {
+      const int i = base + u * kWave + lane;
+      v[u] = i < c1 ? key_at(i) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kOutBatch; ++u) {
+      const int i = base + u * kWave + lane;
+      const bool valid = i < c1;
+      const bool is_eq = valid && v[u] == thr;
+      const uint64_t beq = ballot(is_eq);
+      const bool keep =
+          (valid && v[u] > thr) || (is_eq && eq_before + __builtin_popcountll(beq & lt) < need);
+      const uint64_t bk = ballot(keep);
+      const int at = pos + __builtin_popcountll(bk & lt);
+      if (keep && at < q) sel_row[o0 + at] = r0 + i;
+      pos += __builtin_popcountll(bk);
+      eq_before += __builtin_popcountll(beq);
+    }
+  }
+}
 
 __global__ __launch_bounds__(kThreads) void select_topq(const uint32_t* __restrict__ score,
                                                        const int32_t* __restrict__ fwd_off,
@@ -35,16 +246,10 @@ __global__ __launch_bounds__(kThreads) void select_topq(const uint32_t* __restri
                                                        int L_cap, int K_cap,
                                                        int32_t* __restrict__ sel_row,
                                                        int32_t* __restrict__ err) {
-  __shared__ uint32_t keys[kLdsKeys];
-  __shared__ int hist[kMaxBins];
-  __shared__ int wsum[kWaves + 1];
-  __shared__ int pick[3];
-  __shared__ int weq[kWaves], wkeep[kWaves];
-  __shared__ int ncand;
-  uint32_t* cand = (uint32_t*)(hist + kCandBase);
+  __shared__ SelectSmem sm;
 
   const int e = blockIdx.x;
-  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  const int tid = threadIdx.x;
   int r0 = fwd_off[e], r1 = fwd_off[e + 1];
   r0 = r0 < 0 ? 0 : (r0 > L_cap ? L_cap : r0);
   r1 = r1 < r0 ? r0 : (r1 > L_cap ? L_cap : r1);
@@ -69,154 +274,10 @@ __global__ __launch_bounds__(kThreads) void select_topq(const uint32_t* __restri
     return;
   }
 
-  const bool staged = n <= kLdsKeys;
-  const uint32_t* src = score + r0;
-  bool bad = false;
-  // Eight independent loads in flight per thread before any is used.  A NaN or negative score is
-  // flagged and ranked as +0, so every key below has its sign bit clear.
-  for (int base = 0; base < n; base += 8 * kThreads) {
-    uint32_t v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = base + j * kThreads + tid;
-      v[j] = i < n ? src[i] : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = base + j * kThreads + tid;
-      bad |= v[j] > 0x7F800000u;
-      if (staged && i < n) keys[i] = v[j] > 0x7F800000u ? 0u : v[j];
-    }
-  }
-  if (bad) set_error(err, LRM_DEVERR_NONFINITE);
-  if (tid == 0) ncand = 0;
-  __syncthreads();
-  auto key_at = [&](int i) -> uint32_t {
-    if (staged) return keys[i];
-    const uint32_t v = src[i];
-    return v > 0x7F800000u ? 0u : v;
-  };
-
-  // Radix select of the q-th largest key over bits 30..0, MSB first, in digits of 12, 10 and 9
-  // bits.  The first digit spans the whole exponent and 4 mantissa bits, so one expert's scores
-  // spread over many bins; the keys matching it (the candidates) are then gathered into a short
-  // list when it fits, and the last two digits are counted over that list only.
-  uint32_t prefix = 0, mask = 0;
-  int rank = q;  // rank (1-based, from the top) still to locate among the candidates
-  bool use_cand = false;
-  int nc = 0;
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 19 : (pass == 1 ? 9 : 0);
-    const int nbins = pass == 0 ? 4096 : (pass == 1 ? 1024 : 512);
-    const uint32_t dmask = (uint32_t)nbins - 1;
-    for (int i = tid; i < nbins; i += kThreads) hist[i] = 0;
-    __syncthreads();
-    if (use_cand) {
-      for (int i = tid; i < nc; i += kThreads) {
-        const uint32_t v = cand[i];
-        if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & dmask], 1);
-      }
-    } else {
-      for (int i = tid; i < n; i += kThreads) {
-        const uint32_t v = key_at(i);
-        if ((v & mask) == prefix) atomicAdd(&hist[(v >> shift) & dmask], 1);
-      }
-    }
-    __syncthreads();
-    // Thread t owns bins nbins-1-t*per .. nbins-per-t*per (descending); an exclusive scan over
-    // threads counts the candidates in all higher bins.
-    const int per = (nbins + kThreads - 1) / kThreads;
-    int c = 0;
-    for (int j = 0; j < per; ++j) {
-      const int b = nbins - 1 - tid * per - j;
-      c += b >= 0 ? hist[b] : 0;
-    }
-    const int inc = wave_inclusive_scan(c);
-    if (lane == kWave - 1) wsum[w] = inc;
-    __syncthreads();
-    int before = 0;
-    for (int x = 0; x < w; ++x) before += wsum[x];
-    int cum = before + inc - c;
-    for (int j = 0; j < per; ++j) {
-      const int b = nbins - 1 - tid * per - j;
-      const int hb = b >= 0 ? hist[b] : 0;
-      if (b >= 0 && cum < rank && rank <= cum + hb) {
-        pick[0] = b;
-        pick[1] = cum;
-        pick[2] = hb;
-      }
-      cum += hb;
-    }
-    __syncthreads();
-    const int dgt = pick[0];
-    rank -= pick[1];
-    const int in_bin = pick[2];
-    prefix |= (uint32_t)dgt << shift;
-    mask |= dmask << shift;
-    if (pass == 0 && in_bin <= kMaxCand) {
-      // Gather the candidates of the chosen first digit (any order: only values matter here).
-      // The list aliases the top of the histogram, which the later digits do not use.
-      for (int base = 0; base < n; base += kThreads) {
-        const int i = base + tid;
-        const uint32_t v = i < n ? key_at(i) : 0u;
-        const bool m = i < n && (v & mask) == prefix;
-        const uint64_t bm = ballot(m);
-        int slot = 0;
-        if (lane == 0 && bm) slot = atomicAdd(&ncand, __builtin_popcountll(bm));
-        slot = __shfl(slot, 0, kWave);
-        if (m) cand[slot + __builtin_popcountll(bm & lanemask_lt())] = v;
-      }
-      use_cand = true;
-    }
-    __syncthreads();
-    if (pass == 0) nc = ncand;
-  }
-  const uint32_t thr = prefix;
-  const int need = rank;  // keys equal to thr that are kept, first in row order
-
-  // Ordered output: wavefront w owns the contiguous rows [w*chunk, (w+1)*chunk).  One pass counts
-  // each wave's keys above and equal to thr; after one barrier every wave knows how many rows the
-  // waves before it keep and how many tied keys they hold, and writes its kept rows in row order
-  // with ballot prefix sums (no further barriers).
-  const int chunk = ((n + kWaves - 1) / kWaves + kWave - 1) / kWave * kWave;
-  const int c0 = w * chunk < n ? w * chunk : n;
-  const int c1 = c0 + chunk < n ? c0 + chunk : n;
-  int n_eq = 0, n_gt = 0;
-  for (int i = c0 + lane; i < c1; i += kWave) {
-    const uint32_t v = key_at(i);
-    n_eq += v == thr;
-    n_gt += v > thr;
-  }
-  n_eq = wave_sum_int(n_eq);
-  n_gt = wave_sum_int(n_gt);
-  if (lane == 0) {
-    weq[w] = n_eq;
-    wkeep[w] = n_gt;
-  }
-  __syncthreads();
-  int eq_before = 0, pos = 0;
-  for (int x = 0; x < w; ++x) {
-    const int e_x = weq[x];
-    int tied = need - eq_before;
-    tied = tied < 0 ? 0 : (tied > e_x ? e_x : tied);
-    pos += wkeep[x] + tied;
-    eq_before += e_x;
-  }
-  const uint64_t lt = lanemask_lt();
-  for (int base = c0; base < c1; base += kWave) {
-    const int i = base + lane;
-    const bool valid = i < c1;
-    const uint32_t v = valid ? key_at(i) : 0u;
-    const bool is_eq = valid && v == thr;
-    const uint64_t beq = ballot(is_eq);
-    const bool keep = (valid && v > thr) || (is_eq && eq_before + __builtin_popcountll(beq & lt) < need);
-    const uint64_t bk = ballot(keep);
-    const int at = pos + __builtin_popcountll(bk & lt);
-    if (keep && at < q) sel_row[o0 + at] = r0 + i;
-    pos += __builtin_popcountll(bk);
-    eq_before += __builtin_popcountll(beq);
-  }
+  if (n <= kLdsKeys)
+    select_segment<true>(sm, score + r0, n, q, r0, o0, sel_row, err);
+  else
+    select_segment<false>(sm, score + r0, n, q, r0, o0, sel_row, err);
 }
 
 }  // namespace
