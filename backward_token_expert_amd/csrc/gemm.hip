@@ -39,7 +39,6 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kBK = 32;      // bf16 K step
-constexpr int kStages = 4;   // LDS stages of the bf16 pipeline
 
 // ------------------------------------------------------------------------------------------------
 // bf16 path
@@ -88,29 +87,10 @@ __device__ __forceinline__ int swz_mnk(int row, int k) {
   return row * kBK + ((((k >> 3) ^ ((row >> 2) & 3))) << 3) + (k & 7);
 }
 
-__device__ __forceinline__ s16x4 ds_tr16(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
-}
-
-// 32x32x16 operand fragment from a [k][mn] LDS tile: 32 mn starting at `base`, 16 k at `ks`.
-template <int BMN>
-__device__ __forceinline__ bf16x8 frag_kmn(const uint16_t* t, int ks, int base, int lane) {
-  const int row = ks + 8 * (lane >> 5) + ((lane & 15) >> 2);
-  const int col = base + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const uint16_t* p = t + swz_kmn<BMN>(row, col);
-  const s16x4 lo = ds_tr16(p);
-  const s16x4 hi = ds_tr16(p + 4 * BMN);  // row + 4: same swizzle for both row widths
-  return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Same fragment from a [mn][k] LDS tile.
-__device__ __forceinline__ bf16x8 frag_mnk(const uint16_t* t, int ks, int base, int lane) {
-  return *(const bf16x8*)(t + swz_mnk(base + (lane & 31), ks + 8 * (lane >> 5)));
-}
-
 // Global loads go straight to LDS (buffer_load_dwordx4 ... lds: lane l's 16 bytes land at the
-// wave-uniform LDS address + 16 l).  Buffer resources end at the last valid row, so rows past a
-// segment read as zeros in hardware; chunks past the matrix edge get an offset beyond any range.
+// wave-uniform LDS address in M0 + 16 l).  Buffer resources end at the last valid row, so rows
+// past a segment read as zeros in hardware; chunks past the matrix edge get an offset beyond any
+// range.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, int64_t bytes) {
@@ -120,13 +100,103 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base
 
 // The load is written as inline assembly: the compiler then does not track it as an LDS write
 // and does not drain all outstanding loads before every LDS read; the pipeline below orders the
-// stages with explicit vmcnt waits and barriers instead.  M0 holds the LDS byte address.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint16_t* lds, uint32_t voff) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds;
+// stages with explicit vmcnt waits and barriers instead.  M0 = lds + OFF (LDS byte address).  The
+// sum is formed outside the assembly: an s_add inside it would overwrite SCC, which the compiler
+// may hold live across the statement.
+template <int OFF>
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(r)
+               : "s"(lds + OFF), "v"(voff), "s"(r)
                : "memory", "m0");
+}
+
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u16*)p);
+}
+
+template <int OFF>
+__device__ __forceinline__ s16x4 ds_tr16_at(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(uintptr_t)(addr + OFF));
+}
+
+template <int OFF>
+__device__ __forceinline__ bf16x8 ds_b128_at(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(addr + OFF);
+}
+
+// LDS ring of S stages; stage s holds the A tile (SA elements) then the B tile (SB elements).
+template <int MT, int NT, bool AKMN, int S>
+struct Ring {
+  using C = Tile<MT, NT, AKMN>;
+  static constexpr int A_BYTES = C::SA * 2, B_BYTES = C::SB * 2;
+  static constexpr int STG = A_BYTES + B_BYTES, BYTES = S * STG;
+  static_assert(BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
+};
+
+// Lane-dependent byte offsets (within a stage) of this wavefront's fragment reads, fixed for the
+// whole kernel.  [k][mn] operands: offset of the first of the two transpose reads at k = 0; the
+// second read is 4 rows on and the k = 16 slice 16 rows on, both constants.  [mn][k] operand:
+// one offset per 16-wide slice (the chunk swizzle differs between them).
+template <int MT, int NT, bool AKMN>
+struct FragOffsets {
+  uint32_t a[MT][AKMN ? 1 : 2];
+  uint32_t b[NT];
+};
+
+template <int BMN>
+__device__ __forceinline__ uint32_t kmn_offset(int base, int lane) {
+  const int row = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = base + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  return (uint32_t)swz_kmn<BMN>(row, col) * 2;
+}
+
+template <int MT, int NT, bool AKMN>
+__device__ __forceinline__ FragOffsets<MT, NT, AKMN> frag_offsets(int wm, int wn, int lane) {
+  using C = Tile<MT, NT, AKMN>;
+  FragOffsets<MT, NT, AKMN> f;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int base = wm * 32 * MT + i * 32;
+    if constexpr (AKMN) {
+      f.a[i][0] = kmn_offset<C::BM>(base, lane);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        f.a[i][h] = (uint32_t)swz_mnk(base + (lane & 31), 16 * h + 8 * (lane >> 5)) * 2;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) f.b[j] = C::SA * 2 + kmn_offset<C::BN>(wn * 32 * NT + j * 32, lane);
+  return f;
+}
+
+// Fragments of 16-wide slice H (0: k 0..15, 1: k 16..31) of the stage at LDS byte address `st`.
+template <int MT, int NT, bool AKMN, int H>
+__device__ __forceinline__ void read_frags(uint32_t st, const FragOffsets<MT, NT, AKMN>& f,
+                                           bf16x8 (&a)[MT], bf16x8 (&b)[NT]) {
+  using C = Tile<MT, NT, AKMN>;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    if constexpr (AKMN) {
+      const uint32_t p = st + f.a[i][0];
+      const s16x4 lo = ds_tr16_at<H * 16 * C::BM * 2>(p);
+      const s16x4 hi = ds_tr16_at<(H * 16 + 4) * C::BM * 2>(p);
+      a[i] = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      a[i] = ds_b128_at<0>(st + f.a[i][H]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const uint32_t p = st + f.b[j];
+    const s16x4 lo = ds_tr16_at<H * 16 * C::BN * 2>(p);
+    const s16x4 hi = ds_tr16_at<(H * 16 + 4) * C::BN * 2>(p);
+    b[j] = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
 }
 
 // Per-lane source offsets (bytes, relative to the stage's first row / the tile's first row) of the
@@ -155,20 +225,6 @@ __device__ __forceinline__ void dma_offs_mnk(int64_t ld, int w, int lane, uint32
   }
 }
 
-// Fragments of one 16-wide reduction slice for this wavefront.
-template <int MT, int NT, bool AKMN>
-__device__ __forceinline__ void load_frags(const uint16_t* sa, const uint16_t* sb, int ks, int wm,
-                                           int wn, int lane, bf16x8 (&a)[MT], bf16x8 (&b)[NT]) {
-  using C = Tile<MT, NT, AKMN>;
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int base = wm * 32 * MT + i * 32;
-    a[i] = AKMN ? frag_kmn<C::BM>(sa, ks, base, lane) : frag_mnk(sa, ks, base, lane);
-  }
-#pragma unroll
-  for (int j = 0; j < NT; ++j) b[j] = frag_kmn<C::BN>(sb, ks, wn * 32 * NT + j * 32, lane);
-}
-
 template <int MT, int NT>
 __device__ __forceinline__ void mfmas(const bf16x8 (&a)[MT], const bf16x8 (&b)[NT],
                                       f32x16 (&acc)[MT][NT]) {
@@ -179,27 +235,19 @@ __device__ __forceinline__ void mfmas(const bf16x8 (&a)[MT], const bf16x8 (&b)[N
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-// One K step (32) of MFMAs for this wavefront: the second slice's fragments are read from LDS
-// while the first slice's MFMAs run; scheduling groups pin that interleave (one MFMA, then one
-// or two LDS reads) so the compiler neither serialises reads and MFMAs nor hoists them.
+// Scheduling pattern of one half step: the MT x NT MFMAs of the fragments already in registers,
+// each followed by its share of the LDS reads of the next fragments, so the reads hide behind the
+// matrix work and no MFMA waits for a read issued in the same half.
 template <int MT, int NT, bool AKMN>
-__device__ __forceinline__ void mma_stage(const uint16_t* sa, const uint16_t* sb, int wm, int wn,
-                                          int lane, f32x16 (&acc)[MT][NT]) {
+__device__ __forceinline__ void interleave_reads() {
   constexpr int kReads = (AKMN ? 2 : 1) * MT + 2 * NT;  // LDS read instructions per slice
   constexpr int kMfma = MT * NT;
-  bf16x8 a0[MT], b0[NT], a1[MT], b1[NT];
-  load_frags<MT, NT, AKMN>(sa, sb, 0, wm, wn, lane, a0, b0);
-  load_frags<MT, NT, AKMN>(sa, sb, 16, wm, wn, lane, a1, b1);
-  mfmas<MT, NT>(a0, b0, acc);
-  mfmas<MT, NT>(a1, b1, acc);
-  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
   constexpr int per = (kReads + kMfma - 1) / kMfma;
 #pragma unroll
   for (int q = 0; q < kMfma; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
 }
 
 // Operands of one output tile.  A: [k][mn] (AKMN) or [mn][k]; B: always [k][mn].
@@ -228,62 +276,128 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// acc += A^T-or-A * B over k in [kbeg, kend).  kStages LDS stages; the DMA loads of step k+3 are
-// issued right after the barrier of step k, so three steps of loads are in flight while the MFMAs
-// of step k run.  Before the barrier of step k every wave waits (vmcnt) until only the loads of
-// the later steps are outstanding, so after the barrier stage k is complete in LDS for all waves.
-// Ends with a barrier, so the LDS may be reused right away.
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// Calls f(IntC<0>{}) .. f(IntC<N-1>{}) (compile-time indices, e.g. for instruction immediates).
+template <int N, int J = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (J < N) {
+    f(IntC<J>{});
+    static_for<N, J + 1>(f);
+  }
+}
+
+// Issues the DMA loads of one K step.  kmn operands move their buffer window down the K rows; the
+// [mn][k] operand moves its window along the rows and masks the chunks past kend when the step is
+// partial.  Past the end of the K range every load falls outside its window and writes zeros.
 template <int MT, int NT, bool AKMN>
-__device__ __forceinline__ void mainloop(const Operands& o, uint16_t* sa, uint16_t* sb, int tid,
-                                         int wm, int wn, int lane, f32x16 (&acc)[MT][NT]) {
+struct Loader {
   using C = Tile<MT, NT, AKMN>;
-  constexpr int I = C::IA + C::IB;
-  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int nk = o.kend > o.kbeg ? (o.kend - o.kbeg + kBK - 1) / kBK : 0;
   uint32_t oa[C::IA], ob[C::IB];
   int kca[C::IA];
-  if (AKMN)
-    dma_offs_kmn<C::BM, C::IA>(o.lda, o.a_mn0, o.a_mnend, w, lane, oa);
-  else
-    dma_offs_mnk<C::IA>(o.lda, w, lane, oa, kca);
-  dma_offs_kmn<C::BN, C::IB>(o.ldb, o.b_mn0, o.b_mnend, w, lane, ob);
-  const __amdgpu_buffer_rsrc_t ra_rows =
-      make_rsrc(o.A + (int64_t)o.a_mn0 * o.lda, (int64_t)(o.a_mnend - o.a_mn0) * o.lda * 2);
+  const char* pa;  // window starts for the next step
+  const char* pb;
+  int64_t ra, rb;  // bytes left in each window
+  int64_t sa, sb;  // bytes the windows move per step
+  int k0, kend;
 
-  auto issue = [&](int kt) {
-    const int stg = kt % kStages, k0 = o.kbeg + kt * kBK;
-    uint16_t* la = sa + stg * C::SA + w * C::IA * 512;
-    uint16_t* lb = sb + stg * C::SB + w * C::IB * 512;
-    if (AKMN) {
-      const __amdgpu_buffer_rsrc_t r =
-          make_rsrc(o.A + (int64_t)k0 * o.lda, (int64_t)(o.kend - k0) * o.lda * 2);
-#pragma unroll
-      for (int j = 0; j < C::IA; ++j) dma16(r, la + j * 512, oa[j]);
+  __device__ __forceinline__ void init(const Operands& o, int w, int lane) {
+    if constexpr (AKMN) {
+      dma_offs_kmn<C::BM, C::IA>(o.lda, o.a_mn0, o.a_mnend, w, lane, oa);
+      pa = (const char*)(o.A + (int64_t)o.kbeg * o.lda);
+      ra = (int64_t)(o.kend - o.kbeg) * o.lda * 2;
+      sa = (int64_t)kBK * o.lda * 2;
     } else {
-#pragma unroll
-      for (int j = 0; j < C::IA; ++j)
-        dma16(ra_rows, la + j * 512,
-              k0 + kca[j] < o.kend ? oa[j] + 2u * (uint32_t)k0 : kOutOfRange);
+      dma_offs_mnk<C::IA>(o.lda, w, lane, oa, kca);
+      pa = (const char*)(o.A + (int64_t)o.a_mn0 * o.lda + o.kbeg);
+      ra = (int64_t)(o.a_mnend - o.a_mn0) * o.lda * 2 - (int64_t)o.kbeg * 2;
+      sa = kBK * 2;
     }
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(o.B + (int64_t)k0 * o.ldb, (int64_t)(o.kend - k0) * o.ldb * 2);
-#pragma unroll
-    for (int j = 0; j < C::IB; ++j) dma16(rb, lb + j * 512, ob[j]);
-  };
-
-#pragma unroll
-  for (int st = 0; st < kStages - 1; ++st)
-    if (st < nk) issue(st);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int later = (nk - 1 - kt) < (kStages - 2) ? (nk - 1 - kt) : (kStages - 2);
-    if (later >= 2) wait_vm<2 * I>();
-    else if (later == 1) wait_vm<I>();
-    else wait_vm<0>();
-    lds_barrier();
-    if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
-    mma_stage<MT, NT, AKMN>(sa + (kt % kStages) * C::SA, sb + (kt % kStages) * C::SB, wm, wn,
-                            lane, acc);
+    dma_offs_kmn<C::BN, C::IB>(o.ldb, o.b_mn0, o.b_mnend, w, lane, ob);
+    pb = (const char*)(o.B + (int64_t)o.kbeg * o.ldb);
+    rb = (int64_t)(o.kend - o.kbeg) * o.ldb * 2;
+    sb = (int64_t)kBK * o.ldb * 2;
+    k0 = o.kbeg;
+    kend = o.kend;
   }
+
+  // wa / wb: LDS byte addresses of this wave's first 1 KiB block of the A / B part of the stage.
+  __device__ __forceinline__ void issue(uint32_t wa, uint32_t wb) {
+    const __amdgpu_buffer_rsrc_t r_a = make_rsrc((const uint16_t*)pa, ra);
+    const __amdgpu_buffer_rsrc_t r_b = make_rsrc((const uint16_t*)pb, rb);
+    if (AKMN || k0 + kBK <= kend) {
+      static_for<C::IA>([&](auto j) { dma16<decltype(j)::value * 1024>(r_a, wa, oa[decltype(j)::value]); });
+    } else {
+      static_for<C::IA>([&](auto j) {
+        constexpr int J = decltype(j)::value;
+        dma16<J * 1024>(r_a, wa, k0 + kca[J] < kend ? oa[J] : kOutOfRange);
+      });
+    }
+    static_for<C::IB>([&](auto j) { dma16<decltype(j)::value * 1024>(r_b, wb, ob[decltype(j)::value]); });
+    pa += sa;
+    pb += sb;
+    ra = ra > sa ? ra - sa : 0;
+    rb = rb > sb ? rb - sb : 0;
+    k0 += kBK;
+  }
+};
+
+// acc += A^T-or-A * B over k in [kbeg, kend), in K steps of 32 through the S-stage LDS ring at
+// LDS byte address `ring`.
+//
+// Step kt runs in two halves.  First half: the MFMAs of slice 0 (fragments already in registers)
+// while this wave reads slice 1 of the same stage.  Middle: wait for this wave's loads of stage
+// kt+1, barrier (stage kt+1 is then complete in LDS for every wave, and every wave is done with
+// stage kt-1), and issue the loads of step kt+S-1 into stage kt-1.  Second half: the MFMAs of
+// slice 1 while reading slice 0 of stage kt+1.  Loads are issued for every step, past the end of
+// the K range too (they fall outside their windows and write zeros), so the number of loads in
+// flight at each wait is the same constant.  Ends with every load drained and a barrier, so the
+// ring may be reused right away.
+template <int MT, int NT, bool AKMN, int S>
+__device__ __forceinline__ void mainloop(const Operands& o, uint32_t ring,
+                                         const FragOffsets<MT, NT, AKMN>& fo, int w, int lane,
+                                         f32x16 (&acc)[MT][NT]) {
+  using C = Tile<MT, NT, AKMN>;
+  using R = Ring<MT, NT, AKMN, S>;
+  constexpr int I = C::IA + C::IB;
+  static_assert(S >= 3 && (S - 2) * I < 64, "vmcnt range");
+  const int nk = o.kend > o.kbeg ? (o.kend - o.kbeg + kBK - 1) / kBK : 0;
+  if (nk == 0) return;
+  Loader<MT, NT, AKMN> ld;
+  ld.init(o, w, lane);
+  // this wave's first DMA block inside a stage, for the A and the B part
+  const uint32_t blk_a = w * C::IA * 1024, blk_b = R::A_BYTES + w * C::IB * 1024;
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) ld.issue(ring + st * R::STG + blk_a, ring + st * R::STG + blk_b);
+  wait_vm<(S - 2) * I>();
+  lds_barrier();
+  uint32_t rd = ring;                        // stage kt
+  uint32_t wr = ring + (S - 1) * R::STG;     // stage kt - 1 (the DMA target)
+  bf16x8 a0[MT], b0[NT], a1[MT], b1[NT];
+  read_frags<MT, NT, AKMN, 0>(rd, fo, a0, b0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // first half
+    read_frags<MT, NT, AKMN, 1>(rd, fo, a1, b1);
+    mfmas<MT, NT>(a0, b0, acc);
+    interleave_reads<MT, NT, AKMN>();
+    __builtin_amdgcn_sched_barrier(0);
+    // middle: stage kt+1 complete for every wave; stage kt-1 free
+    wait_vm<(S - 3) * I>();
+    lds_barrier();
+    ld.issue(wr + blk_a, wr + blk_b);
+    rd = rd + R::STG == ring + R::BYTES ? ring : rd + R::STG;
+    wr = wr + R::STG == ring + R::BYTES ? ring : wr + R::STG;
+    __builtin_amdgcn_sched_barrier(0);
+    // second half (after the last step the reads fetch a stage that is not used)
+    read_frags<MT, NT, AKMN, 0>(rd, fo, a0, b0);
+    mfmas<MT, NT>(a1, b1, acc);
+    interleave_reads<MT, NT, AKMN>();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wait_vm<0>();
   lds_barrier();
 }
 
@@ -319,7 +433,7 @@ __device__ __forceinline__ void store_acc(float* __restrict__ out, int64_t ldo, 
 // dW: persistent.  sched[x] = number of experts dealt to die x; sched[kMaxXcd + x * (E_loc + 1)
 // + g] = its g-th expert.  The nb workgroups of die x take units u = i, i + nb, ... of that die's
 // list (unit = expert-major, tile-minor), so they sweep one expert's tiles together.
-template <int MT, int NT>
+template <int MT, int NT, int S>
 __global__ __launch_bounds__(kThreads) void dw_bf16(const uint16_t* __restrict__ Gc,
                                                    const uint16_t* __restrict__ Phic,
                                                    const int32_t* __restrict__ cmp_off,
@@ -327,13 +441,16 @@ __global__ __launch_bounds__(kThreads) void dw_bf16(const uint16_t* __restrict__
                                                    int E_loc, int K_cap, int h, int d,
                                                    float* __restrict__ dW) {
   using C = Tile<MT, NT, true>;
-  __shared__ __attribute__((aligned(1024))) uint16_t sa[kStages * C::SA];
-  __shared__ __attribute__((aligned(1024))) uint16_t sb[kStages * C::SB];
+  using R = Ring<MT, NT, true, S>;
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[R::BYTES / 2];
   const int tn = (d + C::BN - 1) / C::BN, tm = (h + C::BM - 1) / C::BM, tpe = tm * tn;
   const int x = blockIdx.x % nxcd, i = blockIdx.x / nxcd, nb = gridDim.x / nxcd;
   const int units = sched[x] * tpe;
   const int32_t* list = sched + kMaxXcd + x * (E_loc + 1);
-  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave, wm = wv >> 1, wn = wv & 1;
+  const int tid = threadIdx.x, lane = lane_id(), wm = (tid / kWave) >> 1, wn = (tid / kWave) & 1;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const uint32_t ring_addr = lds_addr(ring);
+  const FragOffsets<MT, NT, true> fo = frag_offsets<MT, NT, true>(wm, wn, lane);
   f32x16 acc[MT][NT];
   for (int u = i; u < units; u += nb) {
     const int e = list[u / tpe], local = u % tpe;
@@ -343,14 +460,14 @@ __global__ __launch_bounds__(kThreads) void dw_bf16(const uint16_t* __restrict__
     t = t < s ? s : (t > K_cap ? K_cap : t);
     const Operands o{Gc, h, m0, h, Phic, d, n0, d, s, t};
     zero_acc(acc);
-    mainloop<MT, NT, true>(o, sa, sb, tid, wm, wn, lane, acc);
+    mainloop<MT, NT, true, S>(o, ring_addr, fo, w, lane, acc);
     store_acc<MT, NT>(dW + (int64_t)e * h * d, d, m0, h, n0, d, wm, wn, lane, acc);
   }
 }
 
 // dphi: persistent.  Units = (row tile from the tile table, column tile), columns fastest; die x
 // owns the contiguous unit range [x * per, (x + 1) * per).
-template <int MT, int NT>
+template <int MT, int NT, int S>
 __global__ __launch_bounds__(kThreads) void dx_bf16(const uint16_t* __restrict__ Gc,
                                                    const uint16_t* __restrict__ W,
                                                    const int32_t* __restrict__ cmp_off,
@@ -358,13 +475,16 @@ __global__ __launch_bounds__(kThreads) void dx_bf16(const uint16_t* __restrict__
                                                    int K_cap, int h, int d,
                                                    float* __restrict__ dphi) {
   using C = Tile<MT, NT, false>;
-  __shared__ __attribute__((aligned(1024))) uint16_t sa[kStages * C::SA];
-  __shared__ __attribute__((aligned(1024))) uint16_t sb[kStages * C::SB];
+  using R = Ring<MT, NT, false, S>;
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[R::BYTES / 2];
   const int tn = (d + C::BN - 1) / C::BN;
   const int total = tiles[0] * tn, per = (total + nxcd - 1) / nxcd;
   const int x = blockIdx.x % nxcd, i = blockIdx.x / nxcd, nb = gridDim.x / nxcd;
   const int u0 = x * per, u1 = u0 + per < total ? u0 + per : total;
-  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave, wm = wv >> 1, wn = wv & 1;
+  const int tid = threadIdx.x, lane = lane_id(), wm = (tid / kWave) >> 1, wn = (tid / kWave) & 1;
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const uint32_t ring_addr = lds_addr(ring);
+  const FragOffsets<MT, NT, false> fo = frag_offsets<MT, NT, false>(wm, wn, lane);
   f32x16 acc[MT][NT];
   for (int u = u0 + i; u < u1; u += nb) {
     const int mt = u / tn, n0 = (u % tn) * C::BN;
@@ -373,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void dx_bf16(const uint16_t* __restrict__
     mend = mend > K_cap ? K_cap : mend;
     const Operands o{Gc, h, m0, mend, W + (int64_t)e * h * d, d, n0, d, 0, h};
     zero_acc(acc);
-    mainloop<MT, NT, false>(o, sa, sb, tid, wm, wn, lane, acc);
+    mainloop<MT, NT, false, S>(o, ring_addr, fo, w, lane, acc);
     store_acc<MT, NT>(dphi, d, m0, mend, n0, d, wm, wn, lane, acc);
   }
 }
@@ -643,17 +763,21 @@ Grid persistent_grid() {
 int pick_nt_dw(int d) { return d % 192 == 0 ? 3 : (d % 256 == 0 ? 4 : 2); }
 int pick_nt_dx(int d) { return d % 256 == 0 ? 4 : (d % 192 == 0 ? 3 : 2); }
 
+// LDS stages: as many as fit in 160 KiB, at most 5.
+template <int NT>
+constexpr int stages_for() { return (160 * 1024) / ((256 + 64 * NT) * kBK * 2) < 5 ? (160 * 1024) / ((256 + 64 * NT) * kBK * 2) : 5; }
+
 template <int NT>
 void launch_dw_nt(const lrm_problem& p, const void* Gc, const void* Phic, const int32_t* cmp_off,
                   const int32_t* sched, float* dW, const Grid& g, hipStream_t s) {
-  hipLaunchKernelGGL((dw_bf16<4, NT>), dim3(g.blocks), dim3(kThreads), 0, s, (const uint16_t*)Gc,
+  hipLaunchKernelGGL((dw_bf16<4, NT, stages_for<NT>()>), dim3(g.blocks), dim3(kThreads), 0, s, (const uint16_t*)Gc,
                      (const uint16_t*)Phic, cmp_off, sched, g.nxcd, p.E_loc, p.K_cap, p.h, p.d, dW);
 }
 
 template <int NT>
 void launch_dx_nt(const lrm_problem& p, const void* Gc, const void* W, const int32_t* cmp_off,
                   const int32_t* tiles, float* dphi, const Grid& g, hipStream_t s) {
-  hipLaunchKernelGGL((dx_bf16<4, NT>), dim3(g.blocks), dim3(kThreads), 0, s, (const uint16_t*)Gc,
+  hipLaunchKernelGGL((dx_bf16<4, NT, stages_for<NT>()>), dim3(g.blocks), dim3(kThreads), 0, s, (const uint16_t*)Gc,
                      (const uint16_t*)W, cmp_off, tiles, g.nxcd, p.K_cap, p.h, p.d, dphi);
 }
 
