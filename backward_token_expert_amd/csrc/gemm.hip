@@ -36,15 +36,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kBK = 32;      // bf16 K step
+constexpr int kF32Threads = 256;  // fp32 path: 4 wavefronts in 2 x 2
+constexpr int kBK = 32;           // bf16 K step
 
 // ------------------------------------------------------------------------------------------------
 // bf16 path
 //
-// Workgroup = 4 wavefronts in a 2 x 2 arrangement; a wavefront owns MT x NT tiles of 32 x 32, so
-// the workgroup tile is (64 MT) x (64 NT).  Operands are staged in LDS in their memory
+// Workgroup = 2 x WN wavefronts (2 along M, WN along N); a wavefront owns MT x NT tiles of 32 x 32,
+// so the workgroup tile is (64 MT) x (32 NT WN).  Operands are staged in LDS in their memory
 // orientation:
 //   [k][mn] (mn contiguous): Gc and Phic for dW, W for dphi.  MFMA fragments are read with
 //       ds_read_b64_tr_b16, which transposes 16-bit elements across each group of 16 lanes:
@@ -54,25 +53,28 @@ constexpr int kBK = 32;      // bf16 K step
 //       consecutive reduction elements a 32x32x16 operand lane needs.
 //   [mn][k] (k contiguous): Gc as the row operand of dphi; fragments are plain 16-byte reads.
 // ------------------------------------------------------------------------------------------------
-template <int MT, int NT, bool AKMN>
+template <int MT_, int NT_, int WN_, bool AKMN_>
 struct Tile {
-  static constexpr int BM = 64 * MT, BN = 64 * NT;
+  static constexpr int MT = MT_, NT = NT_, WN = WN_;
+  static constexpr bool AKMN = AKMN_;
+  static constexpr int NWAVES = 2 * WN, THREADS = NWAVES * kWave;
+  static constexpr int BM = 64 * MT, BN = 32 * NT * WN;
   static constexpr int SA = BM * kBK;               // elements per LDS stage (no padding)
   static constexpr int SB = BN * kBK;
-  static constexpr int IA = SA * 2 / 1024 / kWaves;  // 1 KiB LDS-DMA loads per wavefront per stage
-  static constexpr int IB = SB * 2 / 1024 / kWaves;
-  static_assert(IA * 1024 * kWaves == SA * 2 && IB * 1024 * kWaves == SB * 2, "tile / wavefronts");
+  static constexpr int IA = SA * 2 / 1024 / NWAVES;  // 1 KiB LDS-DMA loads per wavefront per stage
+  static constexpr int IB = SB * 2 / 1024 / NWAVES;
+  static_assert(IA * 1024 * NWAVES == SA * 2 && IB * 1024 * NWAVES == SB * 2, "tile / wavefronts");
   static_assert(BM % 128 == 0 && (BN % 128 == 0 || BN == 192), "swizzle needs these row widths");
 };
 
 // LDS layouts (element offsets).  Chunks of 8 elements (16 bytes) are XOR-swizzled inside a row
 // instead of padding the pitch, because LDS-DMA writes 1 KiB contiguous blocks.
 //   [k][mn], BMN wide: a 16-lane transpose read touches four consecutive rows, 32 bytes each, and
-//     the next 16 lanes the next 32 bytes of the same rows.  With 512- or 256-byte rows all rows
-//     start in the same bank, so chunk c of row r sits at chunk c ^ 4 (r % 4): the four rows fall
-//     in four different 64-byte quarters of the 256-byte bank window.  With 384-byte rows
-//     (BMN = 192) consecutive rows alternate between the two 128-byte halves, so chunk c ^ 4
-//     ((r / 2) % 2) separates rows r and r + 2 inside a half.
+//     the next 16 lanes the next 32 bytes of the same rows.  With rows a multiple of 256 bytes all
+//     rows start in the same bank, so chunk c of row r sits at chunk c ^ 4 (r % 4): the four rows
+//     fall in four different 64-byte quarters of the 256-byte bank window.  With 384-byte rows
+//     (BMN = 192) consecutive rows alternate between the two 128-byte halves, so chunk
+//     c ^ 4 ((r / 2) % 2) separates rows r and r + 2 inside a half.
 //   [mn][k], 32 wide: chunk c of row r sits at chunk c ^ ((r / 4) % 4), so 16 consecutive rows
 //     read at one k offset hit 16 different 16-byte bank groups.
 template <int BMN>
@@ -129,22 +131,27 @@ __device__ __forceinline__ bf16x8 ds_b128_at(uint32_t addr) {
 }
 
 // LDS ring of S stages; stage s holds the A tile (SA elements) then the B tile (SB elements).
-template <int MT, int NT, bool AKMN, int S>
+template <class C, int S>
 struct Ring {
-  using C = Tile<MT, NT, AKMN>;
   static constexpr int A_BYTES = C::SA * 2, B_BYTES = C::SB * 2;
   static constexpr int STG = A_BYTES + B_BYTES, BYTES = S * STG;
   static_assert(BYTES <= 160 * 1024, "LDS ring exceeds 160 KiB");
 };
 
+// LDS stages: as many as fit in 160 KiB, at most 5.
+template <class C>
+constexpr int stages_for() {
+  return (160 * 1024) / ((C::SA + C::SB) * 2) < 5 ? (160 * 1024) / ((C::SA + C::SB) * 2) : 5;
+}
+
 // Lane-dependent byte offsets (within a stage) of this wavefront's fragment reads, fixed for the
 // whole kernel.  [k][mn] operands: offset of the first of the two transpose reads at k = 0; the
 // second read is 4 rows on and the k = 16 slice 16 rows on, both constants.  [mn][k] operand:
 // one offset per 16-wide slice (the chunk swizzle differs between them).
-template <int MT, int NT, bool AKMN>
+template <class C>
 struct FragOffsets {
-  uint32_t a[MT][AKMN ? 1 : 2];
-  uint32_t b[NT];
+  uint32_t a[C::MT][C::AKMN ? 1 : 2];
+  uint32_t b[C::NT];
 };
 
 template <int BMN>
@@ -154,14 +161,13 @@ __device__ __forceinline__ uint32_t kmn_offset(int base, int lane) {
   return (uint32_t)swz_kmn<BMN>(row, col) * 2;
 }
 
-template <int MT, int NT, bool AKMN>
-__device__ __forceinline__ FragOffsets<MT, NT, AKMN> frag_offsets(int wm, int wn, int lane) {
-  using C = Tile<MT, NT, AKMN>;
-  FragOffsets<MT, NT, AKMN> f;
+template <class C>
+__device__ __forceinline__ FragOffsets<C> frag_offsets(int wm, int wn, int lane) {
+  FragOffsets<C> f;
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int base = wm * 32 * MT + i * 32;
-    if constexpr (AKMN) {
+  for (int i = 0; i < C::MT; ++i) {
+    const int base = wm * 32 * C::MT + i * 32;
+    if constexpr (C::AKMN) {
       f.a[i][0] = kmn_offset<C::BM>(base, lane);
     } else {
 #pragma unroll
@@ -170,32 +176,65 @@ __device__ __forceinline__ FragOffsets<MT, NT, AKMN> frag_offsets(int wm, int wn
     }
   }
 #pragma unroll
-  for (int j = 0; j < NT; ++j) f.b[j] = C::SA * 2 + kmn_offset<C::BN>(wn * 32 * NT + j * 32, lane);
+  for (int j = 0; j < C::NT; ++j)
+    f.b[j] = C::SA * 2 + kmn_offset<C::BN>(wn * 32 * C::NT + j * 32, lane);
   return f;
 }
 
-// Fragments of 16-wide slice H (0: k 0..15, 1: k 16..31) of the stage at LDS byte address `st`.
-template <int MT, int NT, bool AKMN, int H>
-__device__ __forceinline__ void read_frags(uint32_t st, const FragOffsets<MT, NT, AKMN>& f,
-                                           bf16x8 (&a)[MT], bf16x8 (&b)[NT]) {
-  using C = Tile<MT, NT, AKMN>;
+// Single fragments of 16-wide slice H (0: k 0..15, 1: k 16..31) of the stage at LDS byte
+// address `st`.
+template <class C, int H>
+__device__ __forceinline__ bf16x8 read_a(uint32_t st, const FragOffsets<C>& f, int i) {
+  if constexpr (C::AKMN) {
+    const uint32_t p = st + f.a[i][0];
+    const s16x4 lo = ds_tr16_at<H * 16 * C::BM * 2>(p);
+    const s16x4 hi = ds_tr16_at<(H * 16 + 4) * C::BM * 2>(p);
+    return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else {
+    return ds_b128_at<0>(st + f.a[i][H]);
+  }
+}
+
+template <class C, int H>
+__device__ __forceinline__ bf16x8 read_b(uint32_t st, const FragOffsets<C>& f, int j) {
+  const uint32_t p = st + f.b[j];
+  const s16x4 lo = ds_tr16_at<H * 16 * C::BN * 2>(p);
+  const s16x4 hi = ds_tr16_at<(H * 16 + 4) * C::BN * 2>(p);
+  return __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// One half step, row-streamed: the MFMAs of the current slice (B fragments bc and the first A
+// fragment a0c already in registers), reading the current slice's later A rows just ahead of their
+// use and the next slice's fragments (bn, a0n) along the way, so at most 2 NT + 2 fragments are
+// live.  Scheduling groups alternate one MFMA with LDS reads, so the reads hide behind the matrix
+// work.
+template <class C, int HC, int HN>
+__device__ __forceinline__ void half_step(uint32_t sc, uint32_t sn, const FragOffsets<C>& fo,
+                                          const bf16x8 (&bc)[C::NT], const bf16x8& a0c,
+                                          bf16x8 (&bn)[C::NT], bf16x8& a0n,
+                                          f32x16 (&acc)[C::MT][C::NT]) {
+  constexpr int MT = C::MT, NT = C::NT;
+  bf16x8 a = a0c;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    if constexpr (AKMN) {
-      const uint32_t p = st + f.a[i][0];
-      const s16x4 lo = ds_tr16_at<H * 16 * C::BM * 2>(p);
-      const s16x4 hi = ds_tr16_at<(H * 16 + 4) * C::BM * 2>(p);
-      a[i] = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    } else {
-      a[i] = ds_b128_at<0>(st + f.a[i][H]);
-    }
-  }
+    bf16x8 an;
+    if (i + 1 < MT) an = read_a<C, HC>(sc, fo, i + 1);
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const uint32_t p = st + f.b[j];
-    const s16x4 lo = ds_tr16_at<H * 16 * C::BN * 2>(p);
-    const s16x4 hi = ds_tr16_at<(H * 16 + 4) * C::BN * 2>(p);
-    b[j] = __builtin_bit_cast(bf16x8, (s16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int j = 0; j < NT; ++j)
+      if (j * MT / NT == i) bn[j] = read_b<C, HN>(sn, fo, j);
+    if (i == MT - 1) a0n = read_a<C, HN>(sn, fo, 0);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bc[j], acc[i][j], 0, 0, 0);
+    if (i + 1 < MT) a = an;
+  }
+  constexpr int kReads = (C::AKMN ? 2 : 1) * MT + 2 * NT;  // LDS read instructions per slice
+  constexpr int kMfma = MT * NT;
+  constexpr int per = (kReads + kMfma - 1) / kMfma;
+#pragma unroll
+  for (int q = 0; q < kMfma; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
   }
 }
 
@@ -222,31 +261,6 @@ __device__ __forceinline__ void dma_offs_mnk(int64_t ld, int w, int lane, uint32
     const int c = (q % 4) ^ ((row >> 2) & 3);
     kc[j] = 8 * c;
     o[j] = (uint32_t)((row * ld + 8 * c) * 2);
-  }
-}
-
-template <int MT, int NT>
-__device__ __forceinline__ void mfmas(const bf16x8 (&a)[MT], const bf16x8 (&b)[NT],
-                                      f32x16 (&acc)[MT][NT]) {
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-}
-
-// Scheduling pattern of one half step: the MT x NT MFMAs of the fragments already in registers,
-// each followed by its share of the LDS reads of the next fragments, so the reads hide behind the
-// matrix work and no MFMA waits for a read issued in the same half.
-template <int MT, int NT, bool AKMN>
-__device__ __forceinline__ void interleave_reads() {
-  constexpr int kReads = (AKMN ? 2 : 1) * MT + 2 * NT;  // LDS read instructions per slice
-  constexpr int kMfma = MT * NT;
-  constexpr int per = (kReads + kMfma - 1) / kMfma;
-#pragma unroll
-  for (int q = 0; q < kMfma; ++q) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
   }
 }
 
@@ -293,9 +307,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Issues the DMA loads of one K step.  kmn operands move their buffer window down the K rows; the
 // [mn][k] operand moves its window along the rows and masks the chunks past kend when the step is
 // partial.  Past the end of the K range every load falls outside its window and writes zeros.
-template <int MT, int NT, bool AKMN>
+template <class C>
 struct Loader {
-  using C = Tile<MT, NT, AKMN>;
   uint32_t oa[C::IA], ob[C::IB];
   int kca[C::IA];
   const char* pa;  // window starts for the next step
@@ -305,7 +318,7 @@ struct Loader {
   int k0, kend;
 
   __device__ __forceinline__ void init(const Operands& o, int w, int lane) {
-    if constexpr (AKMN) {
+    if constexpr (C::AKMN) {
       dma_offs_kmn<C::BM, C::IA>(o.lda, o.a_mn0, o.a_mnend, w, lane, oa);
       pa = (const char*)(o.A + (int64_t)o.kbeg * o.lda);
       ra = (int64_t)(o.kend - o.kbeg) * o.lda * 2;
@@ -328,7 +341,7 @@ struct Loader {
   __device__ __forceinline__ void issue(uint32_t wa, uint32_t wb) {
     const __amdgpu_buffer_rsrc_t r_a = make_rsrc((const uint16_t*)pa, ra);
     const __amdgpu_buffer_rsrc_t r_b = make_rsrc((const uint16_t*)pb, rb);
-    if (AKMN || k0 + kBK <= kend) {
+    if (C::AKMN || k0 + kBK <= kend) {
       static_for<C::IA>([&](auto j) { dma16<decltype(j)::value * 1024>(r_a, wa, oa[decltype(j)::value]); });
     } else {
       static_for<C::IA>([&](auto j) {
@@ -356,17 +369,15 @@ struct Loader {
 // the K range too (they fall outside their windows and write zeros), so the number of loads in
 // flight at each wait is the same constant.  Ends with every load drained and a barrier, so the
 // ring may be reused right away.
-template <int MT, int NT, bool AKMN, int S>
-__device__ __forceinline__ void mainloop(const Operands& o, uint32_t ring,
-                                         const FragOffsets<MT, NT, AKMN>& fo, int w, int lane,
-                                         f32x16 (&acc)[MT][NT]) {
-  using C = Tile<MT, NT, AKMN>;
-  using R = Ring<MT, NT, AKMN, S>;
+template <class C, int S>
+__device__ __forceinline__ void mainloop(const Operands& o, uint32_t ring, const FragOffsets<C>& fo,
+                                         int w, int lane, f32x16 (&acc)[C::MT][C::NT]) {
+  using R = Ring<C, S>;
   constexpr int I = C::IA + C::IB;
   static_assert(S >= 3 && (S - 2) * I < 64, "vmcnt range");
   const int nk = o.kend > o.kbeg ? (o.kend - o.kbeg + kBK - 1) / kBK : 0;
   if (nk == 0) return;
-  Loader<MT, NT, AKMN> ld;
+  Loader<C> ld;
   ld.init(o, w, lane);
   // this wave's first DMA block inside a stage, for the A and the B part
   const uint32_t blk_a = w * C::IA * 1024, blk_b = R::A_BYTES + w * C::IB * 1024;
@@ -376,26 +387,25 @@ __device__ __forceinline__ void mainloop(const Operands& o, uint32_t ring,
   lds_barrier();
   uint32_t rd = ring;                        // stage kt
   uint32_t wr = ring + (S - 1) * R::STG;     // stage kt - 1 (the DMA target)
-  bf16x8 a0[MT], b0[NT], a1[MT], b1[NT];
-  read_frags<MT, NT, AKMN, 0>(rd, fo, a0, b0);
+  bf16x8 bA[C::NT], bB[C::NT], aA, aB;
+  aA = read_a<C, 0>(rd, fo, 0);
+#pragma unroll
+  for (int j = 0; j < C::NT; ++j) bA[j] = read_b<C, 0>(rd, fo, j);
   for (int kt = 0; kt < nk; ++kt) {
-    // first half
-    read_frags<MT, NT, AKMN, 1>(rd, fo, a1, b1);
-    mfmas<MT, NT>(a0, b0, acc);
-    interleave_reads<MT, NT, AKMN>();
+    // first half: slice 0 of stage kt; reads slice 1 of the same stage
+    half_step<C, 0, 1>(rd, rd, fo, bA, aA, bB, aB, acc);
     __builtin_amdgcn_sched_barrier(0);
     // middle: stage kt+1 complete for every wave; stage kt-1 free
     wait_vm<(S - 3) * I>();
     lds_barrier();
     ld.issue(wr + blk_a, wr + blk_b);
-    rd = rd + R::STG == ring + R::BYTES ? ring : rd + R::STG;
+    const uint32_t rn = rd + R::STG == ring + R::BYTES ? ring : rd + R::STG;
     wr = wr + R::STG == ring + R::BYTES ? ring : wr + R::STG;
     __builtin_amdgcn_sched_barrier(0);
-    // second half (after the last step the reads fetch a stage that is not used)
-    read_frags<MT, NT, AKMN, 0>(rd, fo, a0, b0);
-    mfmas<MT, NT>(a1, b1, acc);
-    interleave_reads<MT, NT, AKMN>();
+    // second half: slice 1 of stage kt; reads slice 0 of stage kt+1 (unused after the last step)
+    half_step<C, 1, 0>(rd, rn, fo, bB, aB, bA, aA, acc);
     __builtin_amdgcn_sched_barrier(0);
+    rd = rn;
   }
   wait_vm<0>();
   lds_barrier();
@@ -433,25 +443,24 @@ __device__ __forceinline__ void store_acc(float* __restrict__ out, int64_t ldo, 
 // dW: persistent.  sched[x] = number of experts dealt to die x; sched[kMaxXcd + x * (E_loc + 1)
 // + g] = its g-th expert.  The nb workgroups of die x take units u = i, i + nb, ... of that die's
 // list (unit = expert-major, tile-minor), so they sweep one expert's tiles together.
-template <int MT, int NT, int S>
-__global__ __launch_bounds__(kThreads) void dw_bf16(const uint16_t* __restrict__ Gc,
-                                                   const uint16_t* __restrict__ Phic,
-                                                   const int32_t* __restrict__ cmp_off,
-                                                   const int32_t* __restrict__ sched, int nxcd,
-                                                   int E_loc, int K_cap, int h, int d,
-                                                   float* __restrict__ dW) {
-  using C = Tile<MT, NT, true>;
-  using R = Ring<MT, NT, true, S>;
+template <class C, int S>
+__global__ __launch_bounds__(C::THREADS) void dw_bf16(const uint16_t* __restrict__ Gc,
+                                                     const uint16_t* __restrict__ Phic,
+                                                     const int32_t* __restrict__ cmp_off,
+                                                     const int32_t* __restrict__ sched, int nxcd,
+                                                     int E_loc, int K_cap, int h, int d,
+                                                     float* __restrict__ dW) {
+  using R = Ring<C, S>;
   __shared__ __attribute__((aligned(1024))) uint16_t ring[R::BYTES / 2];
   const int tn = (d + C::BN - 1) / C::BN, tm = (h + C::BM - 1) / C::BM, tpe = tm * tn;
   const int x = blockIdx.x % nxcd, i = blockIdx.x / nxcd, nb = gridDim.x / nxcd;
   const int units = sched[x] * tpe;
   const int32_t* list = sched + kMaxXcd + x * (E_loc + 1);
-  const int tid = threadIdx.x, lane = lane_id(), wm = (tid / kWave) >> 1, wn = (tid / kWave) & 1;
-  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), wm = w / C::WN, wn = w % C::WN;
   const uint32_t ring_addr = lds_addr(ring);
-  const FragOffsets<MT, NT, true> fo = frag_offsets<MT, NT, true>(wm, wn, lane);
-  f32x16 acc[MT][NT];
+  const FragOffsets<C> fo = frag_offsets<C>(wm, wn, lane);
+  f32x16 acc[C::MT][C::NT];
   for (int u = i; u < units; u += nb) {
     const int e = list[u / tpe], local = u % tpe;
     const int m0 = (local / tn) * C::BM, n0 = (local % tn) * C::BN;
@@ -460,32 +469,31 @@ __global__ __launch_bounds__(kThreads) void dw_bf16(const uint16_t* __restrict__
     t = t < s ? s : (t > K_cap ? K_cap : t);
     const Operands o{Gc, h, m0, h, Phic, d, n0, d, s, t};
     zero_acc(acc);
-    mainloop<MT, NT, true, S>(o, ring_addr, fo, w, lane, acc);
-    store_acc<MT, NT>(dW + (int64_t)e * h * d, d, m0, h, n0, d, wm, wn, lane, acc);
+    mainloop<C, S>(o, ring_addr, fo, w, lane, acc);
+    store_acc(dW + (int64_t)e * h * d, d, m0, h, n0, d, wm, wn, lane, acc);
   }
 }
 
 // dphi: persistent.  Units = (row tile from the tile table, column tile), columns fastest; die x
 // owns the contiguous unit range [x * per, (x + 1) * per).
-template <int MT, int NT, int S>
-__global__ __launch_bounds__(kThreads) void dx_bf16(const uint16_t* __restrict__ Gc,
-                                                   const uint16_t* __restrict__ W,
-                                                   const int32_t* __restrict__ cmp_off,
-                                                   const int32_t* __restrict__ tiles, int nxcd,
-                                                   int K_cap, int h, int d,
-                                                   float* __restrict__ dphi) {
-  using C = Tile<MT, NT, false>;
-  using R = Ring<MT, NT, false, S>;
+template <class C, int S>
+__global__ __launch_bounds__(C::THREADS) void dx_bf16(const uint16_t* __restrict__ Gc,
+                                                     const uint16_t* __restrict__ W,
+                                                     const int32_t* __restrict__ cmp_off,
+                                                     const int32_t* __restrict__ tiles, int nxcd,
+                                                     int K_cap, int h, int d,
+                                                     float* __restrict__ dphi) {
+  using R = Ring<C, S>;
   __shared__ __attribute__((aligned(1024))) uint16_t ring[R::BYTES / 2];
   const int tn = (d + C::BN - 1) / C::BN;
   const int total = tiles[0] * tn, per = (total + nxcd - 1) / nxcd;
   const int x = blockIdx.x % nxcd, i = blockIdx.x / nxcd, nb = gridDim.x / nxcd;
   const int u0 = x * per, u1 = u0 + per < total ? u0 + per : total;
-  const int tid = threadIdx.x, lane = lane_id(), wm = (tid / kWave) >> 1, wn = (tid / kWave) & 1;
-  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), wm = w / C::WN, wn = w % C::WN;
   const uint32_t ring_addr = lds_addr(ring);
-  const FragOffsets<MT, NT, false> fo = frag_offsets<MT, NT, false>(wm, wn, lane);
-  f32x16 acc[MT][NT];
+  const FragOffsets<C> fo = frag_offsets<C>(wm, wn, lane);
+  f32x16 acc[C::MT][C::NT];
   for (int u = u0 + i; u < u1; u += nb) {
     const int mt = u / tn, n0 = (u % tn) * C::BN;
     const int e = tiles[1 + 2 * mt], m0 = tiles[2 + 2 * mt];
@@ -493,8 +501,8 @@ __global__ __launch_bounds__(kThreads) void dx_bf16(const uint16_t* __restrict__
     mend = mend > K_cap ? K_cap : mend;
     const Operands o{Gc, h, m0, mend, W + (int64_t)e * h * d, d, n0, d, 0, h};
     zero_acc(acc);
-    mainloop<MT, NT, false, S>(o, ring_addr, fo, w, lane, acc);
-    store_acc<MT, NT>(dphi, d, m0, mend, n0, d, wm, wn, lane, acc);
+    mainloop<C, S>(o, ring_addr, fo, w, lane, acc);
+    store_acc(dphi, d, m0, mend, n0, d, wm, wn, lane, acc);
   }
 }
 
@@ -602,7 +610,7 @@ __device__ __forceinline__ void mma_step_f32(const float* __restrict__ sa,
   }
 }
 
-__global__ __launch_bounds__(kThreads) void dw_f32(const float* __restrict__ Gc,
+__global__ __launch_bounds__(kF32Threads) void dw_f32(const float* __restrict__ Gc,
                                                   const float* __restrict__ Phic,
                                                   const int32_t* __restrict__ cmp_off, int K_cap,
                                                   int h, int d, float* __restrict__ dW) {
@@ -642,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void dw_f32(const float* __restrict__ Gc,
   store_acc<2, 2>(dW + (int64_t)e * h * d, d, m0, h, n0, d, wm, wn, lane, acc);
 }
 
-__global__ __launch_bounds__(kThreads) void dx_f32(const float* __restrict__ Gc,
+__global__ __launch_bounds__(kF32Threads) void dx_f32(const float* __restrict__ Gc,
                                                   const float* __restrict__ W,
                                                   const int32_t* __restrict__ cmp_off,
                                                   const int32_t* __restrict__ tiles, int K_cap,
@@ -757,28 +765,42 @@ Grid persistent_grid() {
   return Grid{n / nxcd * nxcd, nxcd};
 }
 
-// Column-tile widths (measured on the Qwen3 share).  dW: 192 when it divides d (the 768-wide FFN
-// then has 4 column tiles, so an expert's dW is 8 x 4 = 32 tiles, one per CU of a die), else 256,
-// else 128.  dphi: 256 when it divides d (fewer, larger tiles), else 192, else 128.
-int pick_nt_dw(int d) { return d % 192 == 0 ? 3 : (d % 256 == 0 ? 4 : 2); }
-int pick_nt_dx(int d) { return d % 256 == 0 ? 4 : (d % 192 == 0 ? 3 : 2); }
+// Tile shapes.  Wide: 8 wavefronts (2 per SIMD), each 128 x 96, workgroup tile 256 x 384 -- the
+// most output per byte staged (the L2-to-CU path, about 20 bytes per clock per CU, is what bounds
+// these kernels).  Narrow fallbacks for d that 384-wide tiles would leave mostly empty.
+using TileW_dW = Tile<4, 3, 4, true>;
+using TileW_dX = Tile<4, 3, 4, false>;
+using Tile192_dW = Tile<4, 3, 2, true>;
+using Tile256_dW = Tile<4, 4, 2, true>;
+using Tile128_dW = Tile<4, 2, 2, true>;
+using Tile192_dX = Tile<4, 3, 2, false>;
+using Tile256_dX = Tile<4, 4, 2, false>;
+using Tile128_dX = Tile<4, 2, 2, false>;
 
-// LDS stages: as many as fit in 160 KiB, at most 5.
-template <int NT>
-constexpr int stages_for() { return (160 * 1024) / ((256 + 64 * NT) * kBK * 2) < 5 ? (160 * 1024) / ((256 + 64 * NT) * kBK * 2) : 5; }
-
-template <int NT>
-void launch_dw_nt(const lrm_problem& p, const void* Gc, const void* Phic, const int32_t* cmp_off,
-                  const int32_t* sched, float* dW, const Grid& g, hipStream_t s) {
-  hipLaunchKernelGGL((dw_bf16<4, NT, stages_for<NT>()>), dim3(g.blocks), dim3(kThreads), 0, s, (const uint16_t*)Gc,
-                     (const uint16_t*)Phic, cmp_off, sched, g.nxcd, p.E_loc, p.K_cap, p.h, p.d, dW);
+// 0: 384-wide, 1: 256, 2: 192, 3: 128.  384 whenever at most a sixth of its columns would be
+// empty; else the widest that divides d.
+int pick_width(int d) {
+  const int t384 = (d + 383) / 384;
+  if (d >= 384 && t384 * 384 - d <= t384 * 64) return 0;
+  if (d % 256 == 0) return 1;
+  if (d % 192 == 0) return 2;
+  return 3;
 }
 
-template <int NT>
-void launch_dx_nt(const lrm_problem& p, const void* Gc, const void* W, const int32_t* cmp_off,
-                  const int32_t* tiles, float* dphi, const Grid& g, hipStream_t s) {
-  hipLaunchKernelGGL((dx_bf16<4, NT, stages_for<NT>()>), dim3(g.blocks), dim3(kThreads), 0, s, (const uint16_t*)Gc,
-                     (const uint16_t*)W, cmp_off, tiles, g.nxcd, p.K_cap, p.h, p.d, dphi);
+template <class C>
+void launch_dw_t(const lrm_problem& p, const void* Gc, const void* Phic, const int32_t* cmp_off,
+                 const int32_t* sched, float* dW, const Grid& g, hipStream_t s) {
+  hipLaunchKernelGGL((dw_bf16<C, stages_for<C>()>), dim3(g.blocks), dim3(C::THREADS), 0, s,
+                     (const uint16_t*)Gc, (const uint16_t*)Phic, cmp_off, sched, g.nxcd, p.E_loc,
+                     p.K_cap, p.h, p.d, dW);
+}
+
+template <class C>
+void launch_dx_t(const lrm_problem& p, const void* Gc, const void* W, const int32_t* cmp_off,
+                 const int32_t* tiles, float* dphi, const Grid& g, hipStream_t s) {
+  hipLaunchKernelGGL((dx_bf16<C, stages_for<C>()>), dim3(g.blocks), dim3(C::THREADS), 0, s,
+                     (const uint16_t*)Gc, (const uint16_t*)W, cmp_off, tiles, g.nxcd, p.K_cap, p.h,
+                     p.d, dphi);
 }
 
 }  // namespace
@@ -790,14 +812,15 @@ hipError_t launch_dw(const lrm_problem& p, const void* Gc, const void* Phic, con
     int32_t* sched = (int32_t*)(ws + wl.order);
     hipLaunchKernelGGL(dw_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, g.nxcd,
                        sched);
-    switch (pick_nt_dw(p.d)) {
-      case 3: launch_dw_nt<3>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
-      case 4: launch_dw_nt<4>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
-      default: launch_dw_nt<2>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
+    switch (pick_width(p.d)) {
+      case 0: launch_dw_t<TileW_dW>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
+      case 1: launch_dw_t<Tile256_dW>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
+      case 2: launch_dw_t<Tile192_dW>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
+      default: launch_dw_t<Tile128_dW>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
     }
   } else {
     const dim3 grid((p.d + FBN - 1) / FBN, (p.h + FBM - 1) / FBM, p.E_loc);
-    hipLaunchKernelGGL(dw_f32, grid, dim3(kThreads), 0, s, (const float*)Gc, (const float*)Phic,
+    hipLaunchKernelGGL(dw_f32, grid, dim3(kF32Threads), 0, s, (const float*)Gc, (const float*)Phic,
                        cmp_off, p.K_cap, p.h, p.d, dW);
   }
   return hipGetLastError();
@@ -808,20 +831,22 @@ hipError_t launch_dx(const lrm_problem& p, const void* Gc, const void* W, const 
   int32_t* tiles = (int32_t*)(ws + wl.tiles);
   if (p.dtype == LRM_BF16) {
     const Grid g = persistent_grid();
-    constexpr int BM = Tile<4, 2, false>::BM;
+    constexpr int BM = TileW_dX::BM;
+    static_assert(BM == Tile128_dX::BM && BM >= kDxTileM, "one row tile for every width");
     const int64_t max_tiles = ((int64_t)p.K_cap + BM - 1) / BM + p.E_loc;
     hipLaunchKernelGGL(dx_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, BM,
                        max_tiles, tiles);
-    switch (pick_nt_dx(p.d)) {
-      case 3: launch_dx_nt<3>(p, Gc, W, cmp_off, tiles, dphi, g, s); break;
-      case 4: launch_dx_nt<4>(p, Gc, W, cmp_off, tiles, dphi, g, s); break;
-      default: launch_dx_nt<2>(p, Gc, W, cmp_off, tiles, dphi, g, s); break;
+    switch (pick_width(p.d)) {
+      case 0: launch_dx_t<TileW_dX>(p, Gc, W, cmp_off, tiles, dphi, g, s); break;
+      case 1: launch_dx_t<Tile256_dX>(p, Gc, W, cmp_off, tiles, dphi, g, s); break;
+      case 2: launch_dx_t<Tile192_dX>(p, Gc, W, cmp_off, tiles, dphi, g, s); break;
+      default: launch_dx_t<Tile128_dX>(p, Gc, W, cmp_off, tiles, dphi, g, s); break;
     }
   } else {
     hipLaunchKernelGGL(dx_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, FBM,
                        wl.max_tiles, tiles);
     const dim3 grid((unsigned)wl.max_tiles, (p.d + FBN - 1) / FBN);
-    hipLaunchKernelGGL(dx_f32, grid, dim3(kThreads), 0, s, (const float*)Gc, (const float*)W,
+    hipLaunchKernelGGL(dx_f32, grid, dim3(kF32Threads), 0, s, (const float*)Gc, (const float*)W,
                        cmp_off, tiles, p.K_cap, p.h, p.d, dphi);
   }
   return hipGetLastError();
