@@ -411,6 +411,53 @@ def _compact_with(P, bufs, inp, sel_host, rp_host, K):
     return lrm.lrm_read_device_error(bufs.ws)
 
 
+GEMM_SHAPES = [
+    # (retained rows per expert, h, d): tile widths 192 / 256 / 384 (with a partial column tile),
+    # one or several row tiles, an empty expert, and a run of full rounds followed by a leftover
+    # round whose units are split along K (130 row tiles x 2 column tiles on 256 workgroups)
+    ([32], 256, 192),
+    ([300], 512, 768),
+    ([100], 256, 1408),
+    ([70, 0, 130], 4096, 1408),
+    ([40, 0, 0, 200], 256, 256),
+    ([16500, 16524], 256, 768),
+]
+
+
+@pytest.mark.parametrize("Ke,h,d", GEMM_SHAPES, ids=[f"K{sum(k)}-h{h}-d{d}" for k, h, d in GEMM_SHAPES])
+def test_grouped_gemms_shapes(Ke, h, d):
+    """lrm_grouped_dw / lrm_grouped_dx on seeded bf16 segments against the float64 oracle."""
+    torch = _torch()
+    from backward_token_expert_amd import lrm
+    from backward_token_expert_amd.path import to_device, to_host
+    rng = np.random.default_rng(sum(Ke) + h + d)
+    K, E_loc = sum(Ke), len(Ke)
+    co = np.concatenate([[0], np.cumsum(Ke)]).astype(np.int32)
+    Gc = O.f32_to_bf16_rne(rng.standard_normal((K, h)).astype(np.float32))
+    Ph = O.f32_to_bf16_rne(rng.standard_normal((K, d)).astype(np.float32))
+    W = O.f32_to_bf16_rne((rng.standard_normal((E_loc, h, d)) / np.sqrt(d)).astype(np.float32))
+    P = lrm.make_problem(max(K, 1), 1, E_loc, 0, E_loc, h, d, "bf16", max(K, 1), max(K, 1))
+    ws = torch.zeros(lrm.lrm_workspace_bytes(P), dtype=torch.uint8, device="cuda")
+    dW = torch.full((E_loc, h, d), 7.0, device="cuda")
+    dphi = torch.zeros((K, d), device="cuda")
+    print(f"[case] grouped GEMMs Ke={Ke} h={h} d={d}", flush=True)
+    cod = to_device(co)
+    lrm.lrm_grouped_dw(P, to_device(Gc), to_device(Ph), cod, dW, ws)
+    lrm.lrm_grouped_dx(P, to_device(Gc), to_device(W), cod, dphi, ws)
+    torch.cuda.synchronize()
+    gW, gx = to_host(dW), to_host(dphi)
+    rW = O.grouped_dw(Gc, Ph, co, "bf16")
+    rx = O.grouped_dx(Gc, W, co, "bf16")
+    tol = C.tol_for("bf16")
+    for e in range(E_loc):
+        if Ke[e] == 0:
+            assert not gW[e].any(), f"expert {e} has no rows but nonzero dW"
+            continue
+        assert C.rel_fro(gW[e], rW[e]) <= tol, (e, C.rel_fro(gW[e], rW[e]))
+        s, t = co[e], co[e + 1]
+        assert C.rel_fro(gx[s:t], rx[s:t]) <= tol, (e, C.rel_fro(gx[s:t], rx[s:t]))
+
+
 def test_compaction_ignores_map_entries_of_earlier_calls():
     """The pair -> row map in the workspace is never cleared: calls with different selections on
     one workspace must each match the oracle's compaction of their own selection."""
