@@ -26,8 +26,9 @@ import re
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 
-# C-ABI entry point -> (device kernel name prefix, translation unit)
-GEMM_KERNELS = {"lrm_grouped_dw": ("dw_", "gemm.hip"), "lrm_grouped_dx": ("dx_", "gemm.hip")}
+# C-ABI entry point -> (names of its GEMM kernels, translation unit)
+GEMM_KERNELS = {"lrm_grouped_dw": (("dw_bf16", "dw_f32"), "gemm.hip"),
+                "lrm_grouped_dx": (("dx_bf16", "dx_f32"), "gemm.hip")}
 _SHARED = ("lrm_device.hpp", "lrm_internal.hpp")
 
 
@@ -117,8 +118,8 @@ def counters_report(root: str, copy_bytes: int, workload: str):
         lines.append(f"| {k} | {n} | {f(mfp)} | {f(100 * wi / wc if wi is not None and wc else None)} | "
                      f"{f(100 * hit / (hit + miss) if hit is not None and miss is not None else None)} | "
                      f"{f(conf, 0)} | {f(fe, 0)} | {f(wr, 0)} | {f(mb)} |")
-        for call, (prefix, _) in GEMM_KERNELS.items():
-            if k.startswith(prefix) and mb is not None:
+        for call, (names, _) in GEMM_KERNELS.items():
+            if k.startswith(names) and mb is not None:
                 rec["kernels"][call] = {"kernel": k, "traffic_bytes": mb * 1e6,
                                         "fetch_bytes": fe * 1024 * fs, "write_bytes": wr * 1024 * ws,
                                         "source_sha256": source_digest(call)}
