@@ -11,16 +11,17 @@
 //   dphi    (K_e x d) = Gc[seg e] (K_e x h) * W[e] (h x d)            reduction over h
 //
 // bf16 (the production path): v_mfma_f32_32x32x16_bf16 with fp32 accumulation, workgroup tiles of
-// 256 rows x 128/192/256 columns, K step 64.  Operands are staged in LDS in their memory
-// orientation and transposed on the LDS read (see the bf16 section).  The kernels are persistent:
-// one workgroup per CU, and the work is laid out per XCD (the MI355X has 8 dies of 32 CUs, each
-// with its own L2; workgroup ids are dealt to dies round-robin):
+// 256 rows x 384 columns (8 wavefronts) or 256 x 256/192/128 (4 wavefronts), K step 32.  Operands
+// are staged in LDS in their memory orientation by LDS-DMA and transposed on the LDS read (see the
+// bf16 section).  The kernels are persistent: one workgroup per CU, and the work is laid out per
+// XCD (the MI355X has 8 dies of 32 CUs, each with its own L2; workgroup ids are dealt to dies
+// round-robin):
 //   dW   whole experts are dealt to dies (largest first, in a snake order), and the 32 workgroups
 //        of a die walk the tiles of their experts together, so every row of Gc/Phic is fetched
 //        from HBM once per die and the other tiles of that expert hit in L2;
 //   dphi each die takes a contiguous range of (row tile, column tile) units, columns fastest, so
 //        a row tile's Gc rows and the expert's W stay in that die's L2.
-// Global loads run one K step ahead of the MFMAs (one register stage, two LDS stages).
+// Global loads run three K steps ahead of the MFMAs through a ring of LDS stages.
 // fp32: v_mfma_f32_32x32x2f32 on 128 x 128 tiles, plain grids.
 // Expert sizes stay on the device: schedules are built by one-workgroup kernels from cmp_off; a
 // zero-length segment writes zeros.  No atomics: every output element is owned by one workgroup,

@@ -32,14 +32,23 @@ GEMM_KERNELS = {"lrm_grouped_dw": (("dw_bf16", "dw_f32"), "gemm.hip"),
 _SHARED = ("lrm_device.hpp", "lrm_internal.hpp")
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank space, so that comment edits keep the digest."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(call: str) -> str:
-    """sha256 over the sources and build flags the kernel of C-ABI entry `call` is built from."""
+    """sha256 over the code (comments dropped) of the sources and build flags the kernel of C-ABI
+    entry `call` is built from."""
     tu = GEMM_KERNELS[call][1]
     h = hashlib.sha256()
     for f in (os.path.join(CSRC, tu), *(os.path.join(CSRC, s) for s in _SHARED),
               os.path.join(PKG, "build.py")):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+        with open(f, encoding="utf-8") as fh:
+            code = fh.read() if f.endswith(".py") else _code_only(fh.read())
+        h.update(os.path.basename(f).encode() + b"\0" + code.encode())
     return h.hexdigest()
 
 
