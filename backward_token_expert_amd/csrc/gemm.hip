@@ -39,6 +39,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kF32Threads = 256;  // fp32 path: 4 wavefronts in 2 x 2
 constexpr int kBK = 32;           // bf16 K step
+constexpr int kThreadsPerSchedule = 1024;
 
 // ------------------------------------------------------------------------------------------------
 // bf16 path
@@ -441,37 +442,63 @@ __device__ __forceinline__ void store_acc(float* __restrict__ out, int64_t ldo, 
     }
 }
 
-// dW: persistent.  sched[x] = number of experts dealt to die x; sched[kMaxXcd + x * (E_loc + 1)
-// + g] = its g-th expert.  The nb workgroups of die x take units u = i, i + nb, ... of that die's
-// list (unit = expert-major, tile-minor), so they sweep one expert's tiles together.
+// dW: persistent.  The workgroups of a die form gpx groups of gs = nb / gpx; group g has a list of
+// jobs (expert, K range, output) built by dw_schedule, and its workgroups take the units
+// u = j, j + gs, ... of that list (unit = job-major, tile-minor), so they sweep one job's tiles
+// together and its rows come from HBM once per group.  A job whose output is a slot writes a
+// partial sum of a split expert there (dw_fixup adds it); otherwise it writes dW directly.
 template <class C, int S>
 __global__ __launch_bounds__(C::THREADS) void dw_bf16(const uint16_t* __restrict__ Gc,
                                                      const uint16_t* __restrict__ Phic,
-                                                     const int32_t* __restrict__ cmp_off,
                                                      const int32_t* __restrict__ sched, int nxcd,
-                                                     int E_loc, int K_cap, int h, int d,
-                                                     float* __restrict__ dW) {
+                                                     int E_loc, int h, int d,
+                                                     float* __restrict__ dW,
+                                                     float* __restrict__ slots) {
   using R = Ring<C, S>;
   __shared__ __attribute__((aligned(1024))) uint16_t ring[R::BYTES / 2];
   const int tn = (d + C::BN - 1) / C::BN, tm = (h + C::BM - 1) / C::BM, tpe = tm * tn;
   const int x = blockIdx.x % nxcd, i = blockIdx.x / nxcd, nb = gridDim.x / nxcd;
-  const int units = sched[x] * tpe;
-  const int32_t* list = sched + kMaxXcd + x * (E_loc + 1);
+  const int gpx = sched[1], gs = nb / gpx, grp = x * gpx + i / gs, j = i % gs;
+  const int units = sched[4 + 3 * kMaxDwSlots + grp] * tpe;
+  const int32_t* jobs = sched + kDwHeader + (int64_t)grp * dw_jobs_per_group(E_loc) * 4;
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), wm = w / C::WN, wn = w % C::WN;
   const uint32_t ring_addr = lds_addr(ring);
   const FragOffsets<C> fo = frag_offsets<C>(wm, wn, lane);
   f32x16 acc[C::MT][C::NT];
-  for (int u = i; u < units; u += nb) {
-    const int e = list[u / tpe], local = u % tpe;
+  for (int u = j; u < units; u += gs) {
+    const int32_t* jb = jobs + 4 * (u / tpe);
+    const int e = jb[0], kb = jb[1], ke = jb[2], slot = jb[3], local = u % tpe;
     const int m0 = (local / tn) * C::BM, n0 = (local % tn) * C::BN;
-    int s = cmp_off[e], t = cmp_off[e + 1];
-    s = s < 0 ? 0 : (s > K_cap ? K_cap : s);
-    t = t < s ? s : (t > K_cap ? K_cap : t);
-    const Operands o{Gc, h, m0, h, Phic, d, n0, d, s, t};
+    const Operands o{Gc, h, m0, h, Phic, d, n0, d, kb, ke};
     zero_acc(acc);
     mainloop<C, S>(o, ring_addr, fo, w, lane, acc);
-    store_acc(dW + (int64_t)e * h * d, d, m0, h, n0, d, wm, wn, lane, acc);
+    float* out = slot < 0 ? dW + (int64_t)e * h * d : slots + (int64_t)slot * h * d;
+    store_acc(out, d, m0, h, n0, d, wm, wn, lane, acc);
+  }
+}
+
+// dW of each split expert += its partial slots, in piece order (kFixupBlocks blocks per expert).
+constexpr int kFixupBlocks = 512;
+
+__global__ __launch_bounds__(256) void dw_fixup(const int32_t* __restrict__ sched, int h, int d,
+                                                const float* __restrict__ slots,
+                                                float* __restrict__ dW) {
+  const int sp = blockIdx.x / kFixupBlocks, part = blockIdx.x % kFixupBlocks;
+  if (sp >= sched[2]) return;
+  const int e = sched[4 + 3 * sp], first = sched[5 + 3 * sp], extra = sched[6 + 3 * sp];
+  const int64_t n4 = (int64_t)h * d / 4;
+  float4* out = (float4*)(dW + (int64_t)e * h * d);
+  for (int64_t q = (int64_t)part * 256 + threadIdx.x; q < n4; q += (int64_t)kFixupBlocks * 256) {
+    float4 v = out[q];
+    for (int k = 0; k < extra; ++k) {
+      const float4 a = ((const float4*)(slots + (int64_t)(first + k) * h * d))[q];
+      v.x += a.x;
+      v.y += a.y;
+      v.z += a.z;
+      v.w += a.w;
+    }
+    out[q] = v;
   }
 }
 
@@ -507,37 +534,122 @@ __global__ __launch_bounds__(C::THREADS) void dx_bf16(const uint16_t* __restrict
   }
 }
 
-// dW schedule: experts ranked by retained rows (descending, ties by id) and dealt to the dies in
-// a snake order (0, 1, .., n-1, n-1, .., 0, 0, ..), which balances the dies' total rows.
+// dW schedule (one workgroup).  G = nxcd * gpx groups; T = ceil(total rows / G) is a group's fair
+// share.  Experts are ranked by retained rows (descending, ties by id).  Two plans:
+//  * whole experts dealt to the groups in snake order (0..G-1, G-1..0, ..);
+//  * when that leaves some group more than 5T/4 rows (one expert far above the share) and the
+//    slots suffice, a contiguous fill: the ranked experts are concatenated and cut into G runs of
+//    T rows (cuts on K-step multiples), so an expert may span several groups; its first piece
+//    writes dW and every later piece a partial slot, which dw_fixup adds in piece order.
+// Empty experts are jobs too (they write zeros), dealt round-robin.
 __global__ __launch_bounds__(1024) void dw_schedule(const int32_t* __restrict__ cmp_off, int E_loc,
-                                                    int K_cap, int nxcd,
+                                                    int K_cap, int groups, int gpx,
                                                     int32_t* __restrict__ sched) {
-  __shared__ int ke[1024];
-  const int tid = threadIdx.x;
+  __shared__ int ke[1024], ks[1024], by_rank[1024];
+  __shared__ int load[kMaxXcd * kMaxGroupsPerXcd], count[kMaxXcd * kMaxGroupsPerXcd];
+  __shared__ int sh[40];
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  int mine = 0;
   if (tid < E_loc) {
-    int s = cmp_off[tid], t = cmp_off[tid + 1];
-    s = s < 0 ? 0 : (s > K_cap ? K_cap : s);
-    t = t < s ? s : (t > K_cap ? K_cap : t);
-    ke[tid] = t - s;
+    int a = cmp_off[tid], b = cmp_off[tid + 1];
+    a = a < 0 ? 0 : (a > K_cap ? K_cap : a);
+    b = b < a ? a : (b > K_cap ? K_cap : b);
+    ke[tid] = b - a;
+    ks[tid] = a;
+    mine = b - a;
   }
+  if (tid < kMaxXcd * kMaxGroupsPerXcd) {
+    load[tid] = 0;
+    count[tid] = 0;
+  }
+  const int wsum = wave_sum_int(mine);
+  if (lane == 0) sh[w] = wsum;
   __syncthreads();
-  const int n2 = 2 * nxcd;
+  int total = 0;
+  for (int x = 0; x < kThreadsPerSchedule / kWave; ++x) total += sh[x];
+  const int T = total > 0 ? (total + groups - 1) / groups : 1;
   if (tid < E_loc) {
-    const int mine = ke[tid];
     int rank = 0;
     for (int y = 0; y < E_loc; ++y) {
       const int o = ke[y];
       rank += (o > mine) || (o == mine && y < tid);
     }
-    const int r = rank % n2, cyc = rank / n2;
-    const int bin = r < nxcd ? r : n2 - 1 - r;
-    const int pos = 2 * cyc + (r < nxcd ? 0 : 1);
-    sched[kMaxXcd + bin * (E_loc + 1) + pos] = tid;
+    by_rank[rank] = tid;
   }
-  if (tid < nxcd) {
-    const int full = E_loc / n2, rem = E_loc % n2;
-    sched[tid] = 2 * full + (rem > tid) + (rem > n2 - 1 - tid);
+  __syncthreads();
+  if (tid == 0) {
+    const int64_t jpg = dw_jobs_per_group(E_loc);
+    auto push = [&](int g, int e, int kb, int kend, int slot) {
+      int32_t* jb = sched + kDwHeader + (int64_t)g * jpg * 4 + 4 * count[g];
+      jb[0] = e;
+      jb[1] = kb;
+      jb[2] = kend;
+      jb[3] = slot;
+      ++count[g];
+    };
+    // plan 1: whole experts, snake order
+    const int n2 = 2 * groups;
+    int worst = 0;
+    for (int r = 0; r < E_loc; ++r) {
+      const int q = r % n2, g = q < groups ? q : n2 - 1 - q;
+      load[g] += ke[by_rank[r]];
+      worst = worst > load[g] ? worst : load[g];
+    }
+    const bool fill = (int64_t)worst * 4 > (int64_t)T * 5 && groups - 1 <= kMaxDwSlots;
+    int nsplit = 0, slots = 0;
+    if (!fill) {
+      for (int r = 0; r < E_loc; ++r) {
+        const int q = r % n2, g = q < groups ? q : n2 - 1 - q, e = by_rank[r];
+        push(g, e, ks[e], ks[e] + ke[e], -1);
+      }
+    } else {
+      // plan 2: contiguous fill of T rows per group
+      int g = 0, filled = 0, zero = 0;
+      for (int r = 0; r < E_loc; ++r) {
+        const int e = by_rank[r], n = ke[e], s = ks[e];
+        if (n == 0) {
+          push(zero % groups, e, s, s, -1);
+          ++zero;
+          continue;
+        }
+        int off = 0, first = -1;
+        while (off < n) {
+          int take = n - off;
+          if (g < groups - 1 && filled + take > T) {
+            take = (T - filled) / kBK * kBK;
+            if (take <= 0) {  // this group is full: move on
+              ++g;
+              filled = 0;
+              continue;
+            }
+          }
+          int slot = -1;
+          if (off > 0) {
+            if (first < 0) first = slots;
+            slot = slots++;
+          }
+          push(g, e, s + off, s + off + take, slot);
+          off += take;
+          filled += take;
+          if (g < groups - 1 && filled >= T - kBK + 1) {
+            ++g;
+            filled = 0;
+          }
+        }
+        if (first >= 0) {
+          sched[4 + 3 * nsplit] = e;
+          sched[5 + 3 * nsplit] = first;
+          sched[6 + 3 * nsplit] = slots - first;
+          ++nsplit;
+        }
+      }
+    }
+    sched[0] = groups;
+    sched[1] = gpx;
+    sched[2] = nsplit;
   }
+  __syncthreads();
+  if (tid < groups) sched[4 + 3 * kMaxDwSlots + tid] = count[tid];
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -790,10 +902,23 @@ int pick_width(int d) {
 
 template <class C>
 void launch_dw_t(const lrm_problem& p, const void* Gc, const void* Phic, const int32_t* cmp_off,
-                 const int32_t* sched, float* dW, const Grid& g, hipStream_t s) {
+                 int32_t* sched, float* dW, float* slots, const Grid& g, hipStream_t s) {
+  // groups per die: as many as keep every group at least one job's tiles wide
+  const int tpe = ((p.h + C::BM - 1) / C::BM) * ((p.d + C::BN - 1) / C::BN);
+  const int nb = g.blocks / g.nxcd;
+  int gpx = 1;
+  for (int c = kMaxGroupsPerXcd; c > 1; c /= 2)
+    if (nb % c == 0 && tpe * c <= nb) {
+      gpx = c;
+      break;
+    }
+  hipLaunchKernelGGL(dw_schedule, dim3(1), dim3(kThreadsPerSchedule), 0, s, cmp_off, p.E_loc,
+                     p.K_cap, g.nxcd * gpx, gpx, sched);
   hipLaunchKernelGGL((dw_bf16<C, stages_for<C>()>), dim3(g.blocks), dim3(C::THREADS), 0, s,
-                     (const uint16_t*)Gc, (const uint16_t*)Phic, cmp_off, sched, g.nxcd, p.E_loc,
-                     p.K_cap, p.h, p.d, dW);
+                     (const uint16_t*)Gc, (const uint16_t*)Phic, sched, g.nxcd, p.E_loc, p.h, p.d,
+                     dW, slots);
+  hipLaunchKernelGGL(dw_fixup, dim3(kMaxDwSlots * kFixupBlocks), dim3(256), 0, s, sched, p.h, p.d,
+                     slots, dW);
 }
 
 template <class C>
@@ -811,13 +936,12 @@ hipError_t launch_dw(const lrm_problem& p, const void* Gc, const void* Phic, con
   if (p.dtype == LRM_BF16) {
     const Grid g = persistent_grid();
     int32_t* sched = (int32_t*)(ws + wl.order);
-    hipLaunchKernelGGL(dw_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, g.nxcd,
-                       sched);
+    float* slots = (float*)(ws + wl.dwslots);
     switch (pick_width(p.d)) {
-      case 0: launch_dw_t<TileW_dW>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
-      case 1: launch_dw_t<Tile256_dW>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
-      case 2: launch_dw_t<Tile192_dW>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
-      default: launch_dw_t<Tile128_dW>(p, Gc, Phic, cmp_off, sched, dW, g, s); break;
+      case 0: launch_dw_t<TileW_dW>(p, Gc, Phic, cmp_off, sched, dW, slots, g, s); break;
+      case 1: launch_dw_t<Tile256_dW>(p, Gc, Phic, cmp_off, sched, dW, slots, g, s); break;
+      case 2: launch_dw_t<Tile192_dW>(p, Gc, Phic, cmp_off, sched, dW, slots, g, s); break;
+      default: launch_dw_t<Tile128_dW>(p, Gc, Phic, cmp_off, sched, dW, slots, g, s); break;
     }
   } else {
     const dim3 grid((p.d + FBN - 1) / FBN, (p.h + FBM - 1) / FBM, p.E_loc);

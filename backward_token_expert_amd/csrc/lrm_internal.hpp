@@ -15,6 +15,15 @@ constexpr int kPlanChunk = 1024;
 constexpr int kDxTileM = 128;
 // Upper bound on the accelerator dies (XCDs) the GEMM schedules spread work over.
 constexpr int kMaxXcd = 8;
+// dW schedule: at most kMaxGroupsPerXcd groups of workgroups per die share a job list; experts far
+// larger than a group's share are split along K into pieces whose partial sums (kMaxDwSlots at
+// most, h x d float32 each) are added by a fix-up kernel.
+constexpr int kMaxGroupsPerXcd = 4;
+constexpr int kMaxDwSlots = 16;
+// Header (ints) of the dW schedule: groups, groups per die, split experts, then 3 ints per split
+// expert (expert, first slot, extra pieces), then the job count of every group.
+constexpr int kDwHeader = 4 + 3 * kMaxDwSlots + kMaxXcd * kMaxGroupsPerXcd;
+__host__ __device__ inline int64_t dw_jobs_per_group(int E_loc) { return (int64_t)E_loc + kMaxDwSlots; }
 
 // Layout of the caller-provided workspace (byte offsets, all 256-byte aligned).
 struct WsLayout {
@@ -23,7 +32,8 @@ struct WsLayout {
                   //                      counts expert ids outside [0, E)
   size_t gnorm;   // double [T]           ||g_t||^2
   size_t tiles;   // int32 [1 + 2*max_tiles] dx tile table: count, then (expert, row0) pairs
-  size_t order;   // int32 [kMaxXcd + kMaxXcd * (E_loc + 1)] dW schedule: per-XCD expert lists
+  size_t order;   // int32 [kDwHeader + groups * jobs * 4] dW schedule: header, per-group job lists
+  size_t dwslots; // float [kMaxDwSlots][h][d] partial dW of split experts
   size_t inv;     // int32 [T*k]          compaction: pair id -> compacted row (validated on use)
   size_t total;
   int64_t nchunks;
@@ -47,9 +57,12 @@ inline WsLayout ws_layout(const lrm_problem& p) {
   w.tiles = off;
   off = align_up(off + (size_t)(1 + 2 * w.max_tiles) * 4, 256);
   w.order = off;
-  off = align_up(off + (size_t)(kMaxXcd + kMaxXcd * (p.E_loc + 1)) * 4, 256);
+  off = align_up(off + (size_t)(kDwHeader + (int64_t)kMaxXcd * kMaxGroupsPerXcd *
+                                             dw_jobs_per_group(p.E_loc) * 4) * 4, 256);
   w.inv = off;
   off = align_up(off + (size_t)P * 4, 256);
+  w.dwslots = off;
+  if (p.dtype == LRM_BF16) off = align_up(off + (size_t)kMaxDwSlots * p.h * p.d * 4, 256);
   w.total = off;
   return w;
 }
