@@ -141,6 +141,10 @@ SPECS = {
     # Whole layer on one GPU (128 local experts), rho = 0.4, cap 1.25*T*k/E, 1 % duplicated tokens.
     4: Spec("qwen3 whole-layer E128/128 top8 T16384 h2048 d768", 16384, 8, 128, 0, 128, 2048, 768,
             "bf16", 1.2, 2, 5, cap_abs=(5 * 16384 * 8) // (4 * 128), dup_frac=0.01, seed=1004),
+    # DeepSeek-V2 expert shape (160 experts, top-6, hidden 5120, expert FFN 1536), one GPU's share
+    # of an 8-way expert-parallel layer (20 local experts), rho = 0.5.
+    5: Spec("deepseek-v2 share E160/20 top6 T16384 h5120 d1536", 16384, 6, 160, 0, 20, 5120, 1536,
+            "bf16", 1.2, 1, 2, seed=1005),
 }
 
 # The retention sweep of the extreme-skew workload.

@@ -198,6 +198,7 @@ SMALL = [
     ("tiny-fp32", 0, {}),
     ("qwen3-T2048", 1, {"T": 2048}),
     ("glm45-T1024", 2, {"T": 1024}),
+    ("deepseek-v2-T1024", 5, {"T": 1024}),
     ("skew-T4096", 3, {"T": 4096}),
     ("layer-T2048", 4, {"T": 2048}),
 ]
@@ -555,7 +556,7 @@ def test_bitwise_determinism_and_graph_replay():
 # ------------------------------------------------------------------------------------------------
 
 FULL = [(0, None), (1, None), (2, None), (3, (1, 1)), (3, (3, 4)), (3, (1, 2)), (3, (1, 4)),
-        (4, None)]
+        (4, None), (5, None)]
 
 
 @pytest.mark.parametrize("full", [False, True], ids=["cfg-rho", "rho1"])

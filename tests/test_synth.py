@@ -25,8 +25,9 @@ def test_rows_duplicates_and_rounding():
     np.testing.assert_array_equal(r, ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16))
 
 
-def test_small_workload_routing_invariants():
-    w = synth.make(1, T=512)
+@pytest.mark.parametrize("cfg", [1, 5])
+def test_small_workload_routing_invariants(cfg):
+    w = synth.make(cfg, T=512)
     sp = w.spec
     idx = w.topk_idx.reshape(sp.T, sp.k)
     assert all(len(set(row)) == sp.k for row in idx.tolist())     # k distinct experts per token
@@ -37,7 +38,7 @@ def test_small_workload_routing_invariants():
     assert w.L == int(loc.sum()) == w.phi.shape[0]
     assert w.g.shape == (sp.T, sp.h) and w.W.shape == (sp.E_loc, sp.h, sp.d)
     # determinism
-    w2 = synth.make(1, T=512)
+    w2 = synth.make(cfg, T=512)
     assert np.array_equal(w.topk_idx, w2.topk_idx) and w.phi.tobytes() == w2.phi.tobytes()
 
 
