@@ -23,6 +23,15 @@ leave a step open:
   * quota policy q_e = n_e (full retention) or min(n_e, floor(num*L / (den*E_loc)), cap) in
     integer arithmetic, where L is the number of local routed pairs (the pages leave open how the
     retained total is split across experts, Sec. 3.2; this is the capacity form of [EPMath]);
+    two further policies split a retained total B = min(L, floor(num*L/den)) across experts:
+    proportional shares B*n_e/L rounded by largest remainder (lower expert first on equal
+    remainders), the split that turns Fig. 4's loads [4,2,3] into [3,1,2] at B = 6, and a
+    water-fill min(n_e, cap, level) whose leftover units go to the lowest-indexed experts above
+    the level;
+  * Table 2's alternative criteria: "L-2 norm for grad" is ||g_t||_2^2 and "absolute value for
+    grad" is ||g_t||_1 = sum_i |g_t,i|, both of the upstream gradient without the routing weight
+    (Sec. 4.7: a gradient-only rule sees neither the routing weight nor the saved activation);
+    "random drop" ranks by keys drawn by the caller, one per pair;
   * selection is decided on float32 scores (the precision the GPU stores), ranking by score
     descending and then pair index ascending; kept rows are written in ascending forward-row
     order;
@@ -32,6 +41,8 @@ leave a step open:
   * dW and dphi are produced in float64 here (fp32 on the GPU).
 """
 from __future__ import annotations
+
+from fractions import Fraction
 
 import numpy as np
 
@@ -106,29 +117,107 @@ def forward_layout(topk_idx: np.ndarray, e_lo: int, E_loc: int):
 # ------------------------------------------------------------------------------------------------
 
 
+QUOTA_KINDS = ("cap", "proportional", "waterfill")
+
+
+def retained_total(L: int, num: int, den: int) -> int:
+    """B = min(L, floor(num*L/den)): the retained count K = rho*N of [LRMoE] Sec. 3.1 for a
+    retention fraction rho = num/den, in integers."""
+    if den <= 0 or num < 0:
+        raise ValueError("bad retention fraction")
+    return min(L, (num * L) // den)
+
+
+def proportional_quotas(n, B: int):
+    """Split B retained rows across experts in proportion to their loads (largest remainder).
+
+    [LRMoE] Sec. 3.3 asks for quotas with 0 <= K_e <= N_e summing to the retained count and
+    leaves the split open; Fig. 4 reduces loads [4,2,3] to [3,1,2], which is the proportional
+    split of B = 6: exact shares B*n_e/L are rounded down and the B - sum of floors leftover rows
+    go to the experts with the largest fractional parts, the lower expert index first on equal
+    fractions.
+    """
+    L = sum(n)
+    if L == 0:
+        return [0] * len(n)
+    share = [Fraction(B * v, L) for v in n]
+    q = [int(x) for x in share]                          # floor (shares are non-negative)
+    left = B - sum(q)
+    order = sorted(range(len(n)), key=lambda e: (-(share[e] - q[e]), e))
+    for e in order[:left]:
+        q[e] += 1
+    return q
+
+
+def waterfill_quotas(n, B: int, cap: int):
+    """Water-fill B retained rows: q_e = min(n_e, cap, level) at the highest integer level whose
+    total stays within B, then one more row each to the lowest-indexed experts still above the
+    level until the total is B (or q_e = min(n_e, cap) everywhere when that total is <= B).
+
+    The reading of a retained total B with a per-expert cap ([LRMoE] Sec. 3.1/3.3 quotas
+    0 <= K_e <= N_e; the cap of [EPMath] "Capacity and the exact drop-rate formula"): experts
+    below the level keep every row, the others are levelled.
+    """
+    m = [v if cap < 0 else min(v, cap) for v in n]
+    if sum(m) <= B:
+        return m
+
+    def total(level):
+        return sum(min(v, level) for v in m)
+
+    lo, hi = 0, max(m)                  # total(lo) <= B < total(hi); bisect for the last level
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if total(mid) <= B:
+            lo = mid
+        else:
+            hi = mid
+    q = [min(v, lo) for v in m]
+    left = B - sum(q)
+    for e in range(len(m)):
+        if left == 0:
+            break
+        if m[e] > lo:
+            q[e] += 1
+            left -= 1
+    return q
+
+
 def plan_quotas(n_loc: np.ndarray, policy: dict):
     """Retention quotas q_e and compacted-segment offsets.
 
     [LRMoE] Sec. 3.1/3.3: quotas satisfy 0 <= K_e <= N_e and are fixed for the invocation;
-    "starting with full retention" means K_e = N_e.  The cap form follows [EPMath] "Capacity and
-    the exact drop-rate formula": an expert keeps min(n_e, C) rows with C = CF * (mean load),
-    here C = floor(num*L / (den*E_loc)) computed exactly in integers, optionally also capped at an
-    absolute cap.  cmp_off is the exclusive prefix sum of q with the total appended, so segment e
-    occupies rows [cmp_off[e], cmp_off[e+1]) ([LRMoE] Fig. 4: counts R=[3,1,2] give offsets
-    [0,3,4,6]).
+    "starting with full retention" means K_e = N_e.  The cap form (policy kind "cap", the
+    default) follows [EPMath] "Capacity and the exact drop-rate formula": an expert keeps
+    min(n_e, C) rows with C = CF * (mean load), here C = floor(num*L / (den*E_loc)) computed
+    exactly in integers, optionally also capped at an absolute cap.  Kinds "proportional" and
+    "waterfill" split B = retained_total(L, num, den) (see proportional_quotas, waterfill_quotas;
+    "proportional" takes no cap).  cmp_off is the exclusive prefix sum of q with the total
+    appended, so segment e occupies rows [cmp_off[e], cmp_off[e+1]) ([LRMoE] Fig. 4: counts
+    R=[3,1,2] give offsets [0,3,4,6]).
     """
     n = [int(v) for v in np.asarray(n_loc).reshape(-1)]
     E_loc = len(n)
     L = sum(n)
+    kind = policy.get("kind", "cap")
+    if kind not in QUOTA_KINDS:
+        raise ValueError(f"unknown quota policy kind {kind!r}")
+    cap = int(policy.get("cap_abs", -1))
     if policy.get("full", 0):
         q = list(n)
-    else:
+    elif kind == "cap":
         num, den = int(policy["rho_num"]), int(policy["rho_den"])
         if den <= 0 or num < 0:
             raise ValueError("bad retention fraction")
         c = (num * L) // (den * E_loc) if E_loc > 0 else 0
-        cap = int(policy.get("cap_abs", -1))
         q = [min(v, c) if cap < 0 else min(v, c, cap) for v in n]
+    elif kind == "proportional":
+        if cap >= 0:
+            raise ValueError("the proportional policy takes no cap")
+        q = proportional_quotas(n, retained_total(L, int(policy["rho_num"]), int(policy["rho_den"])))
+    else:
+        q = waterfill_quotas(n, retained_total(L, int(policy["rho_num"]), int(policy["rho_den"])),
+                             cap)
     off = [0]
     for v in q:
         off.append(off[-1] + v)
@@ -159,6 +248,52 @@ def lrm_scores(topk_w, g, phi, row_pair, k: int, dtype: str, chunk: int = 65536)
         pw = widen(phi[s:s + chunk], dtype)
         psq[s:s + chunk] = (pw * pw).sum(axis=1)
     return a * a * gsq[t] * psq
+
+
+def _token_rows(g, dtype, chunk, f):
+    """f(widened rows) for every token row of g, in float64, chunk by chunk."""
+    out = np.empty(g.shape[0], np.float64)
+    for s in range(0, g.shape[0], chunk):
+        out[s:s + chunk] = f(widen(g[s:s + chunk], dtype))
+    return out
+
+
+def grad_sq_scores(g, row_pair, k: int, dtype: str, chunk: int = 65536) -> np.ndarray:
+    """||g_t||_2^2 of the pair's token for every local forward row ([LRMoE] Table 2, "L-2 norm
+    for grad"; the upstream gradient alone, Sec. 4.7)."""
+    t = np.asarray(row_pair, np.int64) // k
+    return _token_rows(g, dtype, chunk, lambda x: (x * x).sum(axis=1))[t]
+
+
+def grad_abs_scores(g, row_pair, k: int, dtype: str, chunk: int = 65536) -> np.ndarray:
+    """||g_t||_1 = sum_i |g_t,i| of the pair's token for every local forward row ([LRMoE]
+    Table 2, "absolute value for grad")."""
+    t = np.asarray(row_pair, np.int64) // k
+    return _token_rows(g, dtype, chunk, lambda x: np.abs(x).sum(axis=1))[t]
+
+
+def random_scores(keys, row_pair) -> np.ndarray:
+    """keys[p] for every local forward row ([LRMoE] Table 2, "random drop"): with independent
+    uniform keys per pair, the top-q of each expert is a uniformly random q-subset."""
+    return np.asarray(keys, np.float32).astype(np.float64)[np.asarray(row_pair, np.int64)]
+
+
+CRITERIA = ("lrm", "grad_sq", "grad_abs", "random")
+
+
+def scores(criterion: str, topk_w, g, phi, row_pair, k: int, dtype: str, keys=None) -> np.ndarray:
+    """Selection score of every local forward row under one of [LRMoE] Table 2's criteria."""
+    if criterion == "lrm":
+        return lrm_scores(topk_w, g, phi, row_pair, k, dtype)
+    if criterion == "grad_sq":
+        return grad_sq_scores(g, row_pair, k, dtype)
+    if criterion == "grad_abs":
+        return grad_abs_scores(g, row_pair, k, dtype)
+    if criterion == "random":
+        if keys is None:
+            raise ValueError("the random criterion needs one key per pair")
+        return random_scores(keys, row_pair)
+    raise ValueError(f"unknown criterion {criterion!r}")
 
 
 # ------------------------------------------------------------------------------------------------
@@ -287,12 +422,12 @@ def dx_rows(Gc, W, cmp_off, rows_i, dtype: str) -> np.ndarray:
 
 
 def run(topk_idx, topk_w, g, phi, W, *, T, k, E, e_lo, E_loc, dtype, policy,
-        gemms: bool = True) -> dict:
+        gemms: bool = True, criterion: str = "lrm", keys=None) -> dict:
     """Run every step of the path on the CPU and return all intermediate results."""
     n = routed_counts(topk_idx, E)
     row_pair, fwd_off = forward_layout(topk_idx, e_lo, E_loc)
     quota, cmp_off = plan_quotas(n[e_lo:e_lo + E_loc], policy)
-    R = lrm_scores(topk_w, g, phi, row_pair, k, dtype)
+    R = scores(criterion, topk_w, g, phi, row_pair, k, dtype, keys)
     score32 = R.astype(np.float32)
     sel_row = select_top_quota(score32, fwd_off, quota, row_pair)
     Gc, Phic, sel_pair = compact(sel_row, row_pair, topk_w, g, phi, k, dtype)

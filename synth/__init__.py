@@ -31,7 +31,7 @@ _SO = os.path.join(_HERE, "libsynth.so")
 _LIB = None
 
 # Stream ids of the counter-based generator.
-S_X, S_WR, S_G, S_A, S_C, S_W, S_GSCALE, S_PHISCALE, S_TIES = range(1, 10)
+S_X, S_WR, S_G, S_A, S_C, S_W, S_GSCALE, S_PHISCALE, S_TIES, S_KEYS = range(1, 11)
 
 _KIND = {"f64": 0, "f32": 1, "bf16": 2}
 
@@ -58,6 +58,7 @@ def _lib():
         lib.synth_stream_key.argtypes = [u64, u64]
         lib.synth_stream_key.restype = u64
         lib.synth_normals.argtypes = [u64, u64, i64, i64, vp]
+        lib.synth_uniforms_f32.argtypes = [u64, u64, i64, i64, vp]
         lib.synth_rows.argtypes = [u64, u64, vp, i64, i64, i64, dbl, dbl, u64, ctypes.c_int, vp]
         lib.synth_swiglu_rows.argtypes = [u64, u64, u64, vp, i64, i64, dbl, u64, ctypes.c_int, vp]
         _LIB = lib
@@ -72,6 +73,18 @@ def normals(seed: int, stream: int, start: int, n: int) -> np.ndarray:
     out = np.empty(n, np.float64)
     _lib().synth_normals(seed, stream, start, n, _ptr(out))
     return out
+
+
+def uniforms_f32(seed: int, stream: int, start: int, n: int) -> np.ndarray:
+    out = np.empty(n, np.float32)
+    _lib().synth_uniforms_f32(seed, stream, start, n, _ptr(out))
+    return out
+
+
+def pair_keys(sp: "Spec") -> np.ndarray:
+    """One uniform key per pair p in [0, T*k), float32: the random draws of a random-drop
+    selection, generated here and handed to both sides."""
+    return uniforms_f32(sp.seed, S_KEYS, 0, sp.T * sp.k)
 
 
 def rows(seed, stream, nrows, ncols, *, scale=1.0, src_row=None, row0=0, row_sigma=0.0,

@@ -70,6 +70,14 @@ void synth_normals(uint64_t seed, uint64_t stream, int64_t start, int64_t n, dou
   for (int64_t i = 0; i < n; ++i) out[i] = normal_at(key, (uint64_t)(start + i));
 }
 
+/* Uniforms in (0, 1) of one stream, identities [start, start+n), rounded to fp32 (which can
+ * reach 1.0f for the very largest draws). */
+void synth_uniforms_f32(uint64_t seed, uint64_t stream, int64_t start, int64_t n, float* out) {
+  const uint64_t key = synth_stream_key(seed, stream);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = (float)unif(key, (uint64_t)(start + i));
+}
+
 /*
  * Dense rows: out[r*cols + c] = scale * N(stream, src_row[r]*cols + c)
  *                               * (row_sigma != 0 ? exp(row_sigma * N(row_stream, src_row[r])) : 1)

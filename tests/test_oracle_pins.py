@@ -125,6 +125,77 @@ def test_quota_integer_floor_and_caps():
         assert np.array_equal(qf, n)
 
 
+def test_fig4_proportional_quotas():
+    # Fig. 4: loads [4, 2, 3] reduced to [3, 1, 2]; a retained total of 6 of 9 (rho = 2/3) split
+    # in proportion to the loads gives exactly that, and no cap C reproduces it
+    gx = _gold("lrmoe_fig4_pack.json")
+    loads = np.asarray(gx["loads"])
+    q, off = O.plan_quotas(loads, {"full": 0, "kind": "proportional", "rho_num": 2, "rho_den": 3,
+                                   "cap_abs": -1})
+    assert q.tolist() == gx["retained"] and off.tolist() == gx["offsets"]
+    for c in range(0, 5):
+        assert np.minimum(loads, c).tolist() != gx["retained"]
+    with pytest.raises(ValueError):
+        O.plan_quotas(loads, {"kind": "proportional", "rho_num": 1, "rho_den": 2, "cap_abs": 3})
+
+
+def _brute_split(bounds, total, cost):
+    """All integer vectors 0 <= q <= bounds with sum(q) == total; minimise cost(q) exactly, ties
+    to the lexicographically largest q (the lower expert first)."""
+    best = None
+    for q in itertools.product(*(range(b + 1) for b in bounds)):
+        if sum(q) != total:
+            continue
+        key = (cost(q), tuple(-v for v in q))
+        if best is None or key < best[0]:
+            best = (key, list(q))
+    return best[1]
+
+
+def test_proportional_quotas_are_closest_integer_split():
+    # largest remainder = the integer split with sum B closest (in squared distance) to the exact
+    # shares B*n_e/L; brute force over every split in exact rationals
+    rng = np.random.default_rng(21)
+    for trial in range(150):
+        n = [int(v) for v in rng.integers(0, 7, size=int(rng.integers(1, 5)))]
+        L = sum(n)
+        num, den = int(rng.integers(0, 5)), int(rng.integers(1, 5))
+        B = min(L, num * L // den)
+        pol = {"full": 0, "kind": "proportional", "rho_num": num, "rho_den": den, "cap_abs": -1}
+        q, off = O.plan_quotas(np.asarray(n), pol)
+        assert int(q.sum()) == B and off[-1] == B
+        if L == 0:
+            assert not q.any()
+            continue
+        share = [Fraction(B * v, L) for v in n]
+        ref = _brute_split(n, B, lambda qq: sum((a - b) ** 2 for a, b in zip(qq, share)))
+        assert q.tolist() == ref, (n, B)
+        for v, x in zip(q.tolist(), share):              # quota property: floor <= q <= ceil
+            assert x - 1 < v < x + 1
+
+
+def test_waterfill_quotas_are_most_level_split():
+    # water-fill = the split of min(B, sum m) with 0 <= q <= m = min(n, cap) that minimises the
+    # sum of squares (the most level one); brute force over every split
+    rng = np.random.default_rng(22)
+    for trial in range(150):
+        n = [int(v) for v in rng.integers(0, 8, size=int(rng.integers(1, 5)))]
+        cap = int(rng.choice([-1, 2, 4]))
+        num, den = int(rng.integers(0, 5)), int(rng.integers(1, 5))
+        L = sum(n)
+        B = min(L, num * L // den)
+        m = [v if cap < 0 else min(v, cap) for v in n]
+        pol = {"full": 0, "kind": "waterfill", "rho_num": num, "rho_den": den, "cap_abs": cap}
+        q, _ = O.plan_quotas(np.asarray(n), pol)
+        ref = _brute_split(m, min(B, sum(m)), lambda qq: sum(v * v for v in qq))
+        assert q.tolist() == ref, (n, cap, B)
+    # a level below the cap, and the cap binding with budget to spare
+    pol = {"full": 0, "kind": "waterfill", "rho_num": 1, "rho_den": 2, "cap_abs": -1}
+    assert O.plan_quotas(np.array([50, 5, 0, 45]), pol)[0].tolist() == [23, 5, 0, 22]
+    pol = {"full": 0, "kind": "waterfill", "rho_num": 1, "rho_den": 1, "cap_abs": 30}
+    assert O.plan_quotas(np.array([50, 5, 0, 45]), pol)[0].tolist() == [30, 5, 0, 30]
+
+
 # ---------------------------------------------------------------------------------------------
 # scores: rank-one identity (Prop. 3.1 / Appendix 7.1 Eq. (11)-(12))
 # ---------------------------------------------------------------------------------------------
@@ -168,6 +239,82 @@ def test_scores_scale_homogeneity_and_token_sharing():
     gn = R / (a * a * pn)
     gt = (P["g"].astype(np.float64) ** 2).sum(1)[rp // P["k"]]
     np.testing.assert_allclose(gn, gt, rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------------------------
+# Table 2's alternative criteria
+# ---------------------------------------------------------------------------------------------
+
+def test_gradient_criteria_closed_forms():
+    # rows of known norms: (3, -4, 0...) -> ||.||_2^2 = 25, ||.||_1 = 7; a constant row of +-c
+    # reaches ||g||_1^2 = h ||g||_2^2; one non-zero entry gives ||g||_1 = ||g||_2
+    h, k = 16, 2
+    g = np.zeros((4, h), np.float32)
+    g[0, :2] = [3, -4]
+    g[1] = 0.5 * np.where(np.arange(h) % 2 == 0, 1.0, -1.0)
+    g[2, 7] = -2.0
+    row_pair = np.array([0, 1, 2, 3, 4, 5, 6, 7])
+    sq = O.grad_sq_scores(g, row_pair, k, "f32")
+    ab = O.grad_abs_scores(g, row_pair, k, "f32")
+    assert sq.tolist() == [25, 25, 4, 4, 4, 4, 0, 0]
+    assert ab.tolist() == [7, 7, 8, 8, 2, 2, 0, 0]
+    assert ab[2] ** 2 == h * sq[2] and ab[4] ** 2 == sq[4]
+    gb = _bf16_bits(g)                                    # exact in bf16 as well
+    assert O.grad_sq_scores(gb, row_pair, k, "bf16").tolist() == sq.tolist()
+    assert O.grad_abs_scores(gb, row_pair, k, "bf16").tolist() == ab.tolist()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gradient_criteria_ignore_weight_and_activation(dtype):
+    # gradient-only rules (Sec. 4.7): independent of alpha and phi; norm inequalities
+    # ||g||_2 <= ||g||_1 <= sqrt(h) ||g||_2; ||g||_2^2 is the LRM score at alpha = 1, ||phi|| = 1
+    rng = np.random.default_rng(23)
+    P = _tiny_problem(rng, dtype=dtype)
+    rp, k, h = P["row_pair"], P["k"], P["h"]
+    for crit in ("grad_sq", "grad_abs"):
+        a = O.scores(crit, P["w"], P["g"], P["phi"], rp, k, dtype)
+        b = O.scores(crit, P["w"] * np.float32(3), P["g"], P["phi"][::-1].copy(), rp, k, dtype)
+        np.testing.assert_array_equal(a, b)
+    sq = O.grad_sq_scores(P["g"], rp, k, dtype)
+    ab = O.grad_abs_scores(P["g"], rp, k, dtype)
+    assert np.all(np.sqrt(sq) <= ab * (1 + 1e-15)) and np.all(ab <= np.sqrt(h * sq) * (1 + 1e-15))
+    unit = np.zeros_like(P["phi"])
+    unit[:, 0] = _bf16_bits([1.0])[0] if dtype == "bf16" else 1.0
+    R = O.lrm_scores(np.ones_like(P["w"]), P["g"], unit, rp, k, dtype)
+    np.testing.assert_array_equal(R, sq)
+    t = rp // k                                           # pairs of one token share the score
+    for tt in np.unique(t):
+        assert np.unique(sq[t == tt]).size == 1
+
+
+def test_random_criterion_keeps_uniform_subsets():
+    # random drop: with independent uniform keys, each of an expert's n rows is kept with
+    # probability q/n; over 4000 draws every row's count stays within 5 sigma of 4000 q/n, and
+    # the kept set never depends on g or phi
+    rng = np.random.default_rng(24)
+    n_e, q_e = [10, 7], [3, 6]
+    off = [0, 10, 17]
+    rp = np.arange(17) * 2
+    hits = np.zeros(17)
+    draws = 4000
+    for _ in range(draws):
+        keys = rng.random(40).astype(np.float32)
+        s = O.random_scores(keys, rp).astype(np.float32)
+        sel = O.select_top_quota(s, off, q_e, rp)
+        hits[sel] += 1
+    for e in range(2):
+        pr = q_e[e] / n_e[e]
+        sd = np.sqrt(draws * pr * (1 - pr))
+        assert np.all(np.abs(hits[off[e]:off[e + 1]] - draws * pr) <= 5 * sd)
+    P = _tiny_problem(rng, dtype="bf16")
+    keys = rng.random(P["T"] * P["k"]).astype(np.float32)
+    a = O.scores("random", P["w"], P["g"], P["phi"], P["row_pair"], P["k"], "bf16", keys)
+    b = O.scores("random", P["w"], P["g"][::-1].copy(), P["phi"] * 0, P["row_pair"], P["k"], "bf16",
+                 keys)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(a.astype(np.float32), keys[P["row_pair"]])
+    with pytest.raises(ValueError):
+        O.scores("random", P["w"], P["g"], P["phi"], P["row_pair"], P["k"], "bf16")
 
 
 # ---------------------------------------------------------------------------------------------

@@ -15,6 +15,18 @@ def test_counter_rng_is_layout_independent_and_standard():
     assert not np.array_equal(a[:1000], c)                  # seed changes values
 
 
+def test_uniform_keys():
+    a = synth.uniforms_f32(7, synth.S_KEYS, 0, 200000)
+    b = synth.uniforms_f32(7, synth.S_KEYS, 5000, 100)
+    np.testing.assert_array_equal(a[5000:5100], b)
+    assert a.dtype == np.float32 and a.min() > 0.0 and a.max() <= 1.0
+    assert abs(a.mean() - 0.5) < 0.005 and abs(a.var() - 1 / 12) < 0.005
+    sp = synth.spec(1, T=64)
+    k = synth.pair_keys(sp)
+    assert k.shape == (64 * sp.k,)
+    np.testing.assert_array_equal(k, synth.uniforms_f32(sp.seed, synth.S_KEYS, 0, 64 * sp.k))
+
+
 def test_rows_duplicates_and_rounding():
     src = np.array([0, 1, 0, 2])
     r = synth.rows(5, synth.S_G, 4, 16, src_row=src, kind="bf16")
