@@ -58,6 +58,8 @@ lrm_status lrm_plan_quotas(const lrm_problem* problem, const lrm_quota_policy* p
     return LRM_ERR_INVALID_ARGUMENT;
   if (!policy->full && (policy->rho_den <= 0 || policy->rho_num < 0))
     return LRM_ERR_INVALID_ARGUMENT;
+  if (policy->kind < LRM_QUOTA_CAP || policy->kind > LRM_QUOTA_WATERFILL) return LRM_ERR_INVALID_ARGUMENT;
+  if (policy->kind == LRM_QUOTA_PROPORTIONAL && policy->cap_abs >= 0) return LRM_ERR_INVALID_ARGUMENT;
   WsLayout wl;
   LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
   return from_hip(lrm::launch_plan(*problem, *policy, topk_idx, counts, fwd_off, row_pair, quota,
@@ -74,6 +76,24 @@ lrm_status lrm_score(const lrm_problem* problem, const float* topk_w, const void
   LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
   return from_hip(lrm::launch_score(*problem, topk_w, g, phi, row_pair, fwd_off, score, (char*)ws,
                                     wl, stream));
+}
+
+lrm_status lrm_score_criterion(const lrm_problem* problem, int32_t criterion, const float* topk_w,
+                               const void* g, const void* phi, const float* keys,
+                               const int32_t* row_pair, const int32_t* fwd_off, float* score,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (criterion == LRM_CRIT_LRM)
+    return lrm_score(problem, topk_w, g, phi, row_pair, fwd_off, score, ws, ws_bytes, stream);
+  LRM_TRY(check_problem(problem));
+  if (criterion != LRM_CRIT_GRAD_SQ && criterion != LRM_CRIT_GRAD_ABS && criterion != LRM_CRIT_RANDOM)
+    return LRM_ERR_INVALID_ARGUMENT;
+  if (!row_pair || !fwd_off || !score) return LRM_ERR_INVALID_ARGUMENT;
+  if (criterion == LRM_CRIT_RANDOM ? !keys : !g) return LRM_ERR_INVALID_ARGUMENT;
+  if (criterion != LRM_CRIT_RANDOM && !aligned16(g)) return LRM_ERR_UNSUPPORTED;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_score_criterion(*problem, criterion, g, keys, row_pair, fwd_off,
+                                              score, (char*)ws, wl, stream));
 }
 
 lrm_status lrm_select(const lrm_problem* problem, const float* score, const int32_t* fwd_off,

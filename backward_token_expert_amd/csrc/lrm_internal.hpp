@@ -74,6 +74,10 @@ hipError_t launch_plan(const lrm_problem& p, const lrm_quota_policy& pol, const 
 hipError_t launch_score(const lrm_problem& p, const float* topk_w, const void* g, const void* phi,
                         const int32_t* row_pair, const int32_t* fwd_off, float* score, char* ws,
                         const WsLayout& wl, hipStream_t s);
+hipError_t launch_score_criterion(const lrm_problem& p, int criterion, const void* g,
+                                  const float* keys, const int32_t* row_pair,
+                                  const int32_t* fwd_off, float* score, char* ws,
+                                  const WsLayout& wl, hipStream_t s);
 hipError_t launch_select(const lrm_problem& p, const float* score, const int32_t* fwd_off,
                          const int32_t* quota, const int32_t* cmp_off, int32_t* sel_row, char* ws,
                          const WsLayout& wl, hipStream_t s);

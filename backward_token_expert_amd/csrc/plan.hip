@@ -77,6 +77,84 @@ __device__ int block_exclusive_scan_1024(int v, int* sh /* >= 17 ints */, int* t
   return res;
 }
 
+// Largest value over the 1024 threads of a workgroup.
+__device__ int block_max_1024(int v, int* sh /* >= 17 ints */) {
+  const int w = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    const int u = __shfl_xor(v, o, kWave);
+    v = u > v ? u : v;
+  }
+  if (lane_id() == 0) sh[w] = v;
+  __syncthreads();
+  int m = sh[0];
+  for (int i = 1; i < 16; ++i) m = sh[i] > m ? sh[i] : m;
+  __syncthreads();
+  return m;
+}
+
+// Proportional split of B rows over the E_loc experts (thread i holds expert i's load n, the
+// loads sum to L): floor(B * n / L) each, then one more row to the B - sum(floors) experts with
+// the largest remainders (B * n) mod L, the lower expert first on equal remainders.  Remainders
+// of different experts share the denominator L, so comparing them as integers is exact.
+__device__ int proportional_quota(int n, int L, int B, int E_loc, int* rem, int* sh) {
+  const int tid = threadIdx.x;
+  int fl = 0, r = 0;
+  if (tid < E_loc && L > 0) {
+    const int64_t prod = (int64_t)B * n;
+    fl = (int)(prod / L);
+    r = (int)(prod % L);
+  }
+  int sum_fl = 0;
+  block_exclusive_scan_1024(fl, sh, &sum_fl);
+  if (tid < E_loc) rem[tid] = r;
+  __syncthreads();
+  const int left = B - sum_fl;
+  int rank = 0;  // experts ahead of this one in the (remainder desc, index asc) order
+  if (tid < E_loc && left > 0)
+    for (int f = 0; f < E_loc; ++f) {
+      const int rf = rem[f];
+      rank += (rf > r) | ((rf == r) & (f < tid));
+    }
+  __syncthreads();
+  return fl + (tid < E_loc && rank < left ? 1 : 0);
+}
+
+// Water-fill of B rows under m = min(n, cap): every expert keeps min(m, level) at the highest
+// integer level whose total is <= B, then the lowest-indexed experts with m > level get one row
+// more until the total is B; q = m when the m sum to at most B.  The level is found exactly: the
+// total T(x) = sum_f min(m_f, x) is piecewise linear with breakpoints at the m_f, so the last
+// breakpoint v with T(v) <= B (v = 0 if none) and the slope c = #{f : m_f > v} give
+// level = v + (B - T(v)) / c, which stays below the next breakpoint because T there exceeds B.
+__device__ int waterfill_quota(int n, int cap, int B, int E_loc, int* mv, int* sh) {
+  const int tid = threadIdx.x;
+  const int m = tid < E_loc ? (cap >= 0 && n > cap ? cap : n) : 0;
+  int S = 0;
+  block_exclusive_scan_1024(m, sh, &S);
+  if (S <= B) return m;
+  if (tid < E_loc) mv[tid] = m;
+  __syncthreads();
+  int64_t at_m = 0;  // T(m) at this expert's breakpoint
+  if (tid < E_loc)
+    for (int f = 0; f < E_loc; ++f) {
+      const int x = mv[f];
+      at_m += x < m ? x : m;
+    }
+  const int v = block_max_1024(tid < E_loc && at_m <= B ? m : 0, sh);
+  int Tv = 0, c = 0;
+  block_exclusive_scan_1024(m < v ? m : v, sh, &Tv);
+  block_exclusive_scan_1024(m > v ? 1 : 0, sh, &c);
+  const int level = v + (B - Tv) / c;  // c >= 1: T(max m) = S > B
+  int q = m < level ? m : level;
+  int total = 0;
+  block_exclusive_scan_1024(q, sh, &total);
+  const int above = m > level ? 1 : 0;
+  int n_above = 0;
+  const int before = block_exclusive_scan_1024(above, sh, &n_above);
+  if (above && before < B - total) ++q;
+  return q;
+}
+
 constexpr int kScanBatch = 8;
 
 __global__ __launch_bounds__(1024) void plan_scan(int32_t* __restrict__ hist, int64_t nchunks,
@@ -88,6 +166,7 @@ __global__ __launch_bounds__(1024) void plan_scan(int32_t* __restrict__ hist, in
                                                   int32_t* __restrict__ err) {
   __shared__ int part[16][64];
   __shared__ int nloc[1024];
+  __shared__ int rem[1024];
   __shared__ int sh[32];
   __shared__ int nbad;
   const int tid = threadIdx.x, sub = tid & 63, grp = tid >> 6;
@@ -155,15 +234,20 @@ __global__ __launch_bounds__(1024) void plan_scan(int32_t* __restrict__ hist, in
   if (tid < E_loc) fwd_off[tid] = f0;
   if (tid == 0) fwd_off[E_loc] = Lc;
   int q = 0;
-  if (tid < E_loc) {
-    if (pol.full) {
-      q = seg;
-    } else {
+  if (pol.full) {
+    q = tid < E_loc ? seg : 0;
+  } else if (pol.kind == LRM_QUOTA_CAP) {
+    if (tid < E_loc) {
       const int64_t c = ((int64_t)pol.rho_num * Lc) / ((int64_t)pol.rho_den * E_loc);
       int64_t qq = seg < c ? seg : c;
       if (pol.cap_abs >= 0 && qq > pol.cap_abs) qq = pol.cap_abs;
       q = (int)qq;
     }
+  } else {
+    const int64_t bb = ((int64_t)pol.rho_num * Lc) / pol.rho_den;
+    const int B = (int)(bb < Lc ? bb : Lc);
+    q = pol.kind == LRM_QUOTA_PROPORTIONAL ? proportional_quota(seg, Lc, B, E_loc, rem, sh)
+                                           : waterfill_quota(seg, pol.cap_abs, B, E_loc, rem, sh);
   }
   int K = 0;
   const int cpre = block_exclusive_scan_1024(q, sh, &K);

@@ -6,12 +6,16 @@
 // evaluated without materialising it (rank-one identity, Appendix 7.1 Eq. (11)-(12)).
 //
 // Two streaming launches, HBM-bound (about 2 flops per loaded element):
-//   token_sqnorm  ||g_t||^2 for all T tokens (one wavefront per row, 16-byte loads)
+//   token_norm    ||g_t||^2 for all T tokens (one wavefront per row, 16-byte loads)
 //   row_score     ||phi_r||^2 per forward row (16 lanes per row, 4 rows per wavefront), then the
 //                 product with alpha^2 and ||g_t||^2
 // Squares of bf16/fp32 values are exact in float64, and the sums are accumulated in float64 with
 // a fixed lane assignment and a fixed butterfly, so two rows with equal contents give bitwise
 // equal scores wherever they sit; the final product is rounded once to float32.
+//
+// The ablation criteria of Table 2 (launch_score_criterion) reuse the token pass with squares or
+// absolute values, then copy each row's token norm, or the caller's key for random drop, into
+// the row's score (row_gather).
 #include "lrm_device.hpp"
 #include "lrm_internal.hpp"
 
@@ -21,66 +25,50 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 
-// Sum of squares of one row of `chunks` 16-byte chunks, accumulated by this lane, in float64.
-template <bool kBF16>
-__device__ __forceinline__ double lane_sqsum(const uint4* __restrict__ row, int chunks) {
-  double acc = 0.0;
-  const int lane = lane_id();
-  int c = lane;
-  // Two chunks in flight per lane per step.
-  for (; c + kWave < chunks; c += 2 * kWave) {
-    const uint4 a = load_nt(row + c);
-    const uint4 b = load_nt(row + c + kWave);
-    const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
-    const uint32_t wb[4] = {b.x, b.y, b.z, b.w};
+// One 16-byte chunk added to a float64 accumulator: squares (kAbs = false) or absolute values,
+// the chunk's elements in memory order.
+template <bool kBF16, bool kAbs>
+__device__ __forceinline__ double add_chunk(double acc, uint4 a) {
+  const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (kBF16) {
-        const double x0 = bf16_lo(wa[i]), x1 = bf16_hi(wa[i]);
-        acc += x0 * x0;
-        acc += x1 * x1;
-      } else {
-        const double x = __uint_as_float(wa[i]);
-        acc += x * x;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (kBF16) {
-        const double x0 = bf16_lo(wb[i]), x1 = bf16_hi(wb[i]);
-        acc += x0 * x0;
-        acc += x1 * x1;
-      } else {
-        const double x = __uint_as_float(wb[i]);
-        acc += x * x;
-      }
-    }
-  }
-  if (c < chunks) {
-    const uint4 a = load_nt(row + c);
-    const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (kBF16) {
-        const double x0 = bf16_lo(wa[i]), x1 = bf16_hi(wa[i]);
-        acc += x0 * x0;
-        acc += x1 * x1;
-      } else {
-        const double x = __uint_as_float(wa[i]);
-        acc += x * x;
-      }
+  for (int i = 0; i < 4; ++i) {
+    if (kBF16) {
+      const double x0 = bf16_lo(wa[i]), x1 = bf16_hi(wa[i]);
+      acc += kAbs ? fabs(x0) : x0 * x0;
+      acc += kAbs ? fabs(x1) : x1 * x1;
+    } else {
+      const double x = __uint_as_float(wa[i]);
+      acc += kAbs ? fabs(x) : x * x;
     }
   }
   return acc;
 }
 
-template <bool kBF16>
-__global__ __launch_bounds__(kBlock) void token_sqnorm(const uint4* __restrict__ g, int T,
-                                                       int chunks, double* __restrict__ gnorm) {
+// This lane's share (chunks lane, lane + 64, ...) of the sum over one row of `chunks` 16-byte
+// chunks, in float64.
+template <bool kBF16, bool kAbs>
+__device__ __forceinline__ double lane_sum(const uint4* __restrict__ row, int chunks) {
+  double acc = 0.0;
+  int c = lane_id();
+  // Two chunks in flight per lane per step.
+  for (; c + kWave < chunks; c += 2 * kWave) {
+    const uint4 a = load_nt(row + c);
+    const uint4 b = load_nt(row + c + kWave);
+    acc = add_chunk<kBF16, kAbs>(acc, a);
+    acc = add_chunk<kBF16, kAbs>(acc, b);
+  }
+  if (c < chunks) acc = add_chunk<kBF16, kAbs>(acc, load_nt(row + c));
+  return acc;
+}
+
+// Per-token norm of g: ||g_t||_2^2 (kAbs = false) or ||g_t||_1, one wavefront per row.
+template <bool kBF16, bool kAbs>
+__global__ __launch_bounds__(kBlock) void token_norm(const uint4* __restrict__ g, int T,
+                                                     int chunks, double* __restrict__ gnorm) {
   const int lane = lane_id();
   const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
   for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave; t < T; t += nw) {
-    const double s = wave_sum(lane_sqsum<kBF16>(g + t * chunks, chunks));
+    const double s = wave_sum(lane_sum<kBF16, kAbs>(g + t * chunks, chunks));
     if (lane == 0) gnorm[t] = s;
   }
 }
@@ -89,23 +77,6 @@ __global__ __launch_bounds__(kBlock) void token_sqnorm(const uint4* __restrict__
 // every 16th chunk of its row, then a 16-lane butterfly (the same shape for every row).
 constexpr int kLanesPerRow = 16;
 constexpr int kRowsPerWave = kWave / kLanesPerRow;
-
-template <bool kBF16>
-__device__ __forceinline__ double add_chunk(double acc, uint4 a) {
-  const uint32_t wa[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (kBF16) {
-      const double x0 = bf16_lo(wa[i]), x1 = bf16_hi(wa[i]);
-      acc += x0 * x0;
-      acc += x1 * x1;
-    } else {
-      const double x = __uint_as_float(wa[i]);
-      acc += x * x;
-    }
-  }
-  return acc;
-}
 
 template <bool kBF16>
 __global__ __launch_bounds__(kBlock) void row_score(const uint4* __restrict__ phi, int chunks,
@@ -133,12 +104,12 @@ __global__ __launch_bounds__(kBlock) void row_score(const uint4* __restrict__ ph
     for (; c + 3 * kLanesPerRow < chunks; c += 4 * kLanesPerRow) {
       const uint4 a0 = load_nt(row + c), a1 = load_nt(row + c + kLanesPerRow);
       const uint4 a2 = load_nt(row + c + 2 * kLanesPerRow), a3 = load_nt(row + c + 3 * kLanesPerRow);
-      acc = add_chunk<kBF16>(acc, a0);
-      acc = add_chunk<kBF16>(acc, a1);
-      acc = add_chunk<kBF16>(acc, a2);
-      acc = add_chunk<kBF16>(acc, a3);
+      acc = add_chunk<kBF16, false>(acc, a0);
+      acc = add_chunk<kBF16, false>(acc, a1);
+      acc = add_chunk<kBF16, false>(acc, a2);
+      acc = add_chunk<kBF16, false>(acc, a3);
     }
-    for (; c < chunks; c += kLanesPerRow) acc = add_chunk<kBF16>(acc, load_nt(row + c));
+    for (; c < chunks; c += kLanesPerRow) acc = add_chunk<kBF16, false>(acc, load_nt(row + c));
 #pragma unroll
     for (int o = kLanesPerRow / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
     if (live && sub == 0) {
@@ -157,7 +128,71 @@ __global__ __launch_bounds__(kBlock) void row_score(const uint4* __restrict__ ph
   if (bad) set_error(err, bad);
 }
 
+// Score of the ablation criteria: the pair's token norm (kKeys = false) or its caller-drawn key,
+// one row per thread.  -0 is taken as +0 (the selection ranks by the bit pattern).
+template <bool kKeys>
+__global__ __launch_bounds__(kBlock) void row_gather(const int32_t* __restrict__ fwd_off, int E_loc,
+                                                     int L_cap, const int32_t* __restrict__ row_pair,
+                                                     int k, int64_t P,
+                                                     const double* __restrict__ gnorm,
+                                                     const float* __restrict__ keys,
+                                                     float* __restrict__ score,
+                                                     int32_t* __restrict__ err) {
+  int L = fwd_off[E_loc];
+  L = L < 0 ? 0 : (L > L_cap ? L_cap : L);
+  int bad = 0;
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t r = (int64_t)blockIdx.x * kBlock + threadIdx.x; r < L; r += stride) {
+    const int p = row_pair[r];
+    float out = 0.0f;
+    if (p < 0 || p >= P) {
+      bad |= LRM_DEVERR_INDEX;
+    } else {
+      out = kKeys ? keys[p] + 0.0f : (float)gnorm[p / k];
+      if (!(out >= 0.0f && out <= 3.402823466e38f)) bad |= LRM_DEVERR_NONFINITE;
+    }
+    score[r] = out;
+  }
+  if (bad) set_error(err, bad);
+}
+
 }  // namespace
+
+hipError_t launch_score_criterion(const lrm_problem& p, int criterion, const void* g,
+                                  const float* keys, const int32_t* row_pair,
+                                  const int32_t* fwd_off, float* score, char* ws,
+                                  const WsLayout& wl, hipStream_t s) {
+  int32_t* err = (int32_t*)(ws + wl.err);
+  double* gnorm = (double*)(ws + wl.gnorm);
+  const int esz = p.dtype == LRM_BF16 ? 2 : 4;
+  const int gch = p.h * esz / 16;
+  const int64_t tb = ((int64_t)p.T + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t lb = ((int64_t)p.L_cap + kBlock - 1) / kBlock;
+  const unsigned gblk = (unsigned)(tb < 4096 ? tb : 4096);
+  const unsigned lblk = (unsigned)(lb < 2048 ? lb : 2048);
+  const int64_t P = (int64_t)p.T * p.k;
+  if (criterion == LRM_CRIT_RANDOM) {
+    hipLaunchKernelGGL(row_gather<true>, dim3(lblk), dim3(kBlock), 0, s, fwd_off, p.E_loc, p.L_cap,
+                       row_pair, p.k, P, gnorm, keys, score, err);
+    return hipGetLastError();
+  }
+  const bool abs = criterion == LRM_CRIT_GRAD_ABS;
+  const uint4* g4 = (const uint4*)g;
+  if (p.dtype == LRM_BF16) {
+    if (abs)
+      hipLaunchKernelGGL((token_norm<true, true>), dim3(gblk), dim3(kBlock), 0, s, g4, p.T, gch, gnorm);
+    else
+      hipLaunchKernelGGL((token_norm<true, false>), dim3(gblk), dim3(kBlock), 0, s, g4, p.T, gch, gnorm);
+  } else {
+    if (abs)
+      hipLaunchKernelGGL((token_norm<false, true>), dim3(gblk), dim3(kBlock), 0, s, g4, p.T, gch, gnorm);
+    else
+      hipLaunchKernelGGL((token_norm<false, false>), dim3(gblk), dim3(kBlock), 0, s, g4, p.T, gch, gnorm);
+  }
+  hipLaunchKernelGGL(row_gather<false>, dim3(lblk), dim3(kBlock), 0, s, fwd_off, p.E_loc, p.L_cap,
+                     row_pair, p.k, P, gnorm, keys, score, err);
+  return hipGetLastError();
+}
 
 hipError_t launch_score(const lrm_problem& p, const float* topk_w, const void* g, const void* phi,
                         const int32_t* row_pair, const int32_t* fwd_off, float* score, char* ws,
@@ -173,12 +208,12 @@ hipError_t launch_score(const lrm_problem& p, const float* topk_w, const void* g
   const unsigned lblk = (unsigned)(lb < 4096 ? lb : 4096);
   const int64_t P = (int64_t)p.T * p.k;
   if (p.dtype == LRM_BF16) {
-    hipLaunchKernelGGL(token_sqnorm<true>, dim3(gblk), dim3(kBlock), 0, s, (const uint4*)g, p.T,
+    hipLaunchKernelGGL((token_norm<true, false>), dim3(gblk), dim3(kBlock), 0, s, (const uint4*)g, p.T,
                        gch, gnorm);
     hipLaunchKernelGGL(row_score<true>, dim3(lblk), dim3(kBlock), 0, s, (const uint4*)phi, pch,
                        fwd_off, p.E_loc, p.L_cap, row_pair, topk_w, p.k, P, gnorm, score, err);
   } else {
-    hipLaunchKernelGGL(token_sqnorm<false>, dim3(gblk), dim3(kBlock), 0, s, (const uint4*)g, p.T,
+    hipLaunchKernelGGL((token_norm<false, false>), dim3(gblk), dim3(kBlock), 0, s, (const uint4*)g, p.T,
                        gch, gnorm);
     hipLaunchKernelGGL(row_score<false>, dim3(lblk), dim3(kBlock), 0, s, (const uint4*)phi, pch,
                        fwd_off, p.E_loc, p.L_cap, row_pair, topk_w, p.k, P, gnorm, score, err);

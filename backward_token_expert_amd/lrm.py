@@ -18,8 +18,12 @@ LIB_PATH = os.environ.get("LRM_LIBRARY") or os.path.join(_PKG, "liblrm.so")
 LRM_F32, LRM_BF16 = 0, 1
 DEVERR = {1: "EXPERT_ID", 2: "L_CAP", 4: "K_CAP", 8: "QUOTA", 16: "NONFINITE", 32: "INDEX"}
 
-EXPORTS = ("lrm_workspace_bytes", "lrm_plan_quotas", "lrm_score", "lrm_select", "lrm_compact",
-           "lrm_grouped_dw", "lrm_grouped_dx", "lrm_read_device_error", "lrm_status_string")
+EXPORTS = ("lrm_workspace_bytes", "lrm_plan_quotas", "lrm_score", "lrm_score_criterion",
+           "lrm_select", "lrm_compact", "lrm_grouped_dw", "lrm_grouped_dx",
+           "lrm_read_device_error", "lrm_status_string")
+
+QUOTA_KINDS = {"cap": 0, "proportional": 1, "waterfill": 2}
+CRITERIA = {"lrm": 0, "grad_sq": 1, "grad_abs": 2, "random": 3}
 
 
 class Problem(ctypes.Structure):
@@ -28,7 +32,7 @@ class Problem(ctypes.Structure):
 
 
 class QuotaPolicy(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int32) for n in ("full", "rho_num", "rho_den", "cap_abs")]
+    _fields_ = [(n, ctypes.c_int32) for n in ("full", "rho_num", "rho_den", "cap_abs", "kind")]
 
 
 class LrmError(RuntimeError):
@@ -54,12 +58,13 @@ def load_library(path: Optional[str] = None):
     lib.lrm_workspace_bytes.restype = sz
     lib.lrm_plan_quotas.argtypes = [PP, QP] + [vp] * 7 + [sz, vp]
     lib.lrm_score.argtypes = [PP] + [vp] * 7 + [sz, vp]
+    lib.lrm_score_criterion.argtypes = [PP, i32] + [vp] * 8 + [sz, vp]
     lib.lrm_select.argtypes = [PP] + [vp] * 6 + [sz, vp]
     lib.lrm_compact.argtypes = [PP] + [vp] * 10 + [sz, vp]
     lib.lrm_grouped_dw.argtypes = [PP] + [vp] * 5 + [sz, vp]
     lib.lrm_grouped_dx.argtypes = [PP] + [vp] * 5 + [sz, vp]
     lib.lrm_read_device_error.argtypes = [vp, ctypes.POINTER(i32), i32, vp]
-    for f in ("lrm_plan_quotas", "lrm_score", "lrm_select", "lrm_compact", "lrm_grouped_dw",
+    for f in ("lrm_plan_quotas", "lrm_score", "lrm_score_criterion", "lrm_select", "lrm_compact", "lrm_grouped_dw",
               "lrm_grouped_dx", "lrm_read_device_error"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lrm_status_string.argtypes = [ctypes.c_int]
@@ -95,8 +100,9 @@ def make_problem(T, k, E, e_lo, E_loc, h, d, dtype, L_cap, K_cap) -> Problem:
     return Problem(T, k, E, e_lo, E_loc, h, d, dt, L_cap, K_cap)
 
 
-def make_policy(full=0, rho_num=1, rho_den=1, cap_abs=-1) -> QuotaPolicy:
-    return QuotaPolicy(int(full), int(rho_num), int(rho_den), int(cap_abs))
+def make_policy(full=0, rho_num=1, rho_den=1, cap_abs=-1, kind="cap") -> QuotaPolicy:
+    kd = QUOTA_KINDS[kind] if isinstance(kind, str) else int(kind)
+    return QuotaPolicy(int(full), int(rho_num), int(rho_den), int(cap_abs), kd)
 
 
 def lrm_workspace_bytes(problem: Problem) -> int:
@@ -117,6 +123,16 @@ def lrm_score(problem, topk_w, g, phi, row_pair, fwd_off, score, ws, stream=None
     _check(lib, lib.lrm_score(ctypes.byref(problem), _ptr(topk_w), _ptr(g), _ptr(phi),
                               _ptr(row_pair), _ptr(fwd_off), _ptr(score), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)), "lrm_score")
+
+
+def lrm_score_criterion(problem, criterion, topk_w, g, phi, keys, row_pair, fwd_off, score, ws,
+                        stream=None):
+    lib = load_library()
+    crit = CRITERIA[criterion] if isinstance(criterion, str) else int(criterion)
+    _check(lib, lib.lrm_score_criterion(ctypes.byref(problem), crit, _ptr(topk_w), _ptr(g),
+                                        _ptr(phi), _ptr(keys), _ptr(row_pair), _ptr(fwd_off),
+                                        _ptr(score), _ptr(ws), ws.numel() * ws.element_size(),
+                                        _stream(stream)), "lrm_score_criterion")
 
 
 def lrm_select(problem, score, fwd_off, quota, cmp_off, sel_row, ws, stream=None):

@@ -1,7 +1,7 @@
 """Device buffers and the six-call sequence of the hot path (marshalling only).
 
 ``DeviceBuffers`` allocates, with PyTorch, every output and the workspace of one problem; ``run``
-enqueues lrm_plan_quotas -> lrm_score -> lrm_select -> lrm_compact -> lrm_grouped_dw ->
+enqueues lrm_plan_quotas -> lrm_score (or lrm_score_criterion) -> lrm_select -> lrm_compact -> lrm_grouped_dw ->
 lrm_grouped_dx on one stream.  No step of the path is computed here.
 """
 from __future__ import annotations
@@ -54,12 +54,19 @@ class DeviceBuffers:
         self.ws = torch.zeros(nws, dtype=torch.uint8, device=device)
 
 
-def run(problem, policy, topk_idx, topk_w, g, phi, W, bufs: DeviceBuffers, stream=None):
-    """Enqueue the whole hot path on `stream` (default: torch's current stream)."""
+def run(problem, policy, topk_idx, topk_w, g, phi, W, bufs: DeviceBuffers, stream=None,
+        criterion: str = "lrm", keys=None):
+    """Enqueue the whole hot path on `stream` (default: torch's current stream).  `criterion`
+    picks the selection score (lrm_score for "lrm", else lrm_score_criterion; "random" ranks by
+    `keys`, one float32 per pair)."""
     b = bufs
     lrm.lrm_plan_quotas(problem, policy, topk_idx, b.counts, b.fwd_off, b.row_pair, b.quota,
                         b.cmp_off, b.ws, stream)
-    lrm.lrm_score(problem, topk_w, g, phi, b.row_pair, b.fwd_off, b.score, b.ws, stream)
+    if criterion == "lrm":
+        lrm.lrm_score(problem, topk_w, g, phi, b.row_pair, b.fwd_off, b.score, b.ws, stream)
+    else:
+        lrm.lrm_score_criterion(problem, criterion, topk_w, g, phi, keys, b.row_pair, b.fwd_off,
+                                b.score, b.ws, stream)
     lrm.lrm_select(problem, b.score, b.fwd_off, b.quota, b.cmp_off, b.sel_row, b.ws, stream)
     lrm.lrm_compact(problem, b.sel_row, b.row_pair, b.cmp_off, topk_w, g, phi, b.Gc, b.Phic,
                     b.sel_pair, b.ws, stream)

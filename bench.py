@@ -8,6 +8,7 @@ Default workload: the Qwen3-30B-A3B-shaped share of one GPU (128 experts, 16 loc
 32768 tokens, h=2048, d_ffn=768, bf16, retention rho = 0.5).  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 1] [--no-cpu-baseline]
+                  [--criterion lrm|grad_sq|grad_abs|random] [--quota cap|proportional|waterfill]
 """
 from __future__ import annotations
 
@@ -32,6 +33,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--criterion", default="lrm", choices=["lrm", "grad_sq", "grad_abs", "random"],
+                    help="selection score: the LRM, or one of the ablation criteria")
+    ap.add_argument("--quota", default="cap", choices=["cap", "proportional", "waterfill"],
+                    help="quota split of the retained total")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-experts", type=int, default=16)
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
@@ -44,7 +49,7 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic(w, oracle_like):
+def algorithmic(w, oracle_like, criterion="lrm"):
     """Algorithmic bytes / flops of each stage (what the method must move or compute)."""
     sp = w.spec
     b = 2 if sp.dtype == "bf16" else 4
@@ -55,9 +60,13 @@ def algorithmic(w, oracle_like):
     T_ret = oracle_like["T_ret"]
     Ke = oracle_like["Ke"]
     h, d, E_loc = sp.h, sp.d, sp.E_loc
+    score = {"lrm": T_loc * h * b + L * d * b + 12 * L,      # g rows, phi rows, alpha/map/score
+             "grad_sq": T_loc * h * b + 8 * L,               # g rows, map/score
+             "grad_abs": T_loc * h * b + 8 * L,
+             "random": 12 * L}[criterion]                    # map, key, score
     return {
         "plan": 4 * sp.T * k + 4 * L + 16 * E_loc,
-        "score": T_loc * h * b + L * d * b + 12 * L,
+        "score": score,
         "select": 4 * L + 4 * K,
         "compact": 16 * K + T_ret * h * b + K * d * b + K * (h + d) * b,
         "dw": K * (h + d) * b + 4 * E_loc * h * d,
@@ -67,7 +76,7 @@ def algorithmic(w, oracle_like):
     }
 
 
-def gpu_bench(w, pol_dict, steps, warmup):
+def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm"):
     import torch
     from backward_token_expert_amd import lrm, path
     from backward_token_expert_amd.path import to_device, to_host
@@ -75,11 +84,12 @@ def gpu_bench(w, pol_dict, steps, warmup):
     L_cap = sp.T * min(sp.k, sp.E_loc)
     P = lrm.make_problem(sp.T, sp.k, sp.E, sp.e_lo, sp.E_loc, sp.h, sp.d, sp.dtype, L_cap, L_cap)
     pol = lrm.make_policy(pol_dict["full"], pol_dict["rho_num"], pol_dict["rho_den"],
-                          pol_dict["cap_abs"])
+                          pol_dict["cap_abs"], pol_dict.get("kind", "cap"))
     phi = w.phi
     if phi.shape[0] < L_cap:
         phi = np.concatenate([phi, np.zeros((L_cap - phi.shape[0], sp.d), phi.dtype)])
     idx, tw, g, ph, W = (to_device(a) for a in (w.topk_idx, w.topk_w, w.g, phi, w.W))
+    keys = to_device(synth_keys(sp)) if criterion == "random" else None
     b = path.DeviceBuffers(P)
     s = torch.cuda.current_stream()
 
@@ -89,7 +99,11 @@ def gpu_bench(w, pol_dict, steps, warmup):
         lrm.lrm_plan_quotas(P, pol, idx, b.counts, b.fwd_off, b.row_pair, b.quota, b.cmp_off, b.ws, s)
         if ev is not None:
             ev[1].record(s)
-        lrm.lrm_score(P, tw, g, ph, b.row_pair, b.fwd_off, b.score, b.ws, s)
+        if criterion == "lrm":
+            lrm.lrm_score(P, tw, g, ph, b.row_pair, b.fwd_off, b.score, b.ws, s)
+        else:
+            lrm.lrm_score_criterion(P, criterion, tw, g, ph, keys, b.row_pair, b.fwd_off, b.score,
+                                    b.ws, s)
         if ev is not None:
             ev[2].record(s)
         lrm.lrm_select(P, b.score, b.fwd_off, b.quota, b.cmp_off, b.sel_row, b.ws, s)
@@ -137,12 +151,18 @@ def gpu_bench(w, pol_dict, steps, warmup):
     return ms_total / steps, wall / steps * 1e3, stage_ms, info
 
 
-def cpu_baseline(w, pol_dict, n_experts, min_seconds):
+def synth_keys(sp):
+    import synth
+    return synth.pair_keys(sp)
+
+
+def cpu_baseline(w, pol_dict, n_experts, min_seconds, criterion="lrm"):
     """The oracle, as it stands, on a bounded sample: all counting/planning plus scoring,
     selection, compaction and both GEMMs of the first `n_experts` local experts, repeated until
     `min_seconds` have passed (at least once); the rate is over all repetitions."""
     import oracle as O
     sp = w.spec
+    keys = synth_keys(sp) if criterion == "random" else None
     threads = None
     try:
         import threadpoolctl
@@ -157,7 +177,7 @@ def cpu_baseline(w, pol_dict, n_experts, min_seconds):
         quota, cmp_off = O.plan_quotas(n[sp.e_lo:sp.e_lo + sp.E_loc], pol_dict)
         ne = min(n_experts, sp.E_loc)
         rows = slice(0, int(fwd_off[ne]))
-        R = O.lrm_scores(w.topk_w, w.g, w.phi[rows], row_pair[rows], sp.k, sp.dtype)
+        R = O.scores(criterion, w.topk_w, w.g, w.phi[rows], row_pair[rows], sp.k, sp.dtype, keys)
         sel = O.select_top_quota(R.astype(np.float32), fwd_off[:ne + 1], quota[:ne], row_pair)
         Gc, Phic, _ = O.compact(sel, row_pair, w.topk_w, w.g, w.phi, sp.k, sp.dtype)
         off = cmp_off[:ne + 1]
@@ -209,16 +229,17 @@ def main():
     import synth
     w = synth.make(args.config)
     sp = w.spec
-    pol = synth.policy(sp)
-    ms, wall_ms, stages, info = gpu_bench(w, pol, args.steps, args.warmup)
-    alg = algorithmic(w, info)
+    pol = synth.policy(sp, kind=args.quota, cap=-1 if args.quota == "proportional" else None)
+    crit = args.criterion
+    ms, wall_ms, stages, info = gpu_bench(w, pol, args.steps, args.warmup, crit)
+    alg = algorithmic(w, info, crit)
     L, K = info["L"], info["K"]
     # rho = 1 (full retention) on the same input
     n1 = max(3, args.steps // 2) if args.rho1_steps is None else args.rho1_steps
     if n1 > 0:
         pol_full = synth.policy(sp, full=True)
-        ms1, _, stages1, info1 = gpu_bench(w, pol_full, n1, 2)
-        alg1 = algorithmic(w, info1)
+        ms1, _, stages1, info1 = gpu_bench(w, pol_full, n1, 2, crit)
+        alg1 = algorithmic(w, info1, crit)
 
     def fractions(st, a, dtype):
         t_ssc = (st["score"] + st["select"] + st["compact"]) * 1e-3
@@ -249,7 +270,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": sp.name, "T": sp.T, "top_k": sp.k, "experts": sp.E,
                    "local_experts": sp.E_loc, "h": sp.h, "d_ffn": sp.d,
-                   "rho": f"{pol['rho_num']}/{pol['rho_den']}", "L_pairs": L, "K_retained": K},
+                   "rho": f"{pol['rho_num']}/{pol['rho_den']}", "quota": args.quota,
+                   "criterion": crit, "L_pairs": L, "K_retained": K},
         "roofline": {"bound": "mfma", "kernel": dom_call,
                      "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
                      "traffic": recorded_traffic(dom_call, sp.name)},
@@ -273,7 +295,7 @@ def main():
         out["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, pol, args.cpu_sample_experts,
-                                           args.cpu_min_seconds)
+                                           args.cpu_min_seconds, crit)
     print(json.dumps(out))
 
 

@@ -10,6 +10,7 @@
  *                    formula")
  *   lrm_score        Load Recalibration Metric R_u = alpha_u^2 ||g_t||^2 ||phi_u||^2
  *                    (Sec. 3.2, Prop. 3.1, Eq. (3); Algorithm 1 step 13)
+ *   lrm_score_criterion  the same or one of the ablation criteria of Table 2
  *   lrm_select       per-expert TopK(q_e) (Algorithm 1 step 14; Sec. 3.3; Appendix 7.2 Prop. 7.1)
  *   lrm_compact      physical compaction into contiguous expert-major segments
  *                    (Sec. 3.3, Sec. 3.4, Fig. 4; Appendix 7.1 Eq. (5))
@@ -44,7 +45,8 @@
  *    16-byte aligned.  Its first word is a sticky device error word (LRM_DEVERR_* bits) that
  *    lrm_plan_quotas clears and every call may set; read it with lrm_read_device_error.
  *  - Host-side validation returns LRM_ERR_INVALID_ARGUMENT (null pointer, non-positive sizes,
- *    k > E, e_lo + E_loc > E, rho_den <= 0, caps too small for the problem) or
+ *    k > E, e_lo + E_loc > E, rho_den <= 0, an unknown quota kind or criterion, caps too small
+ *    for the problem) or
  *    LRM_ERR_UNSUPPORTED (pointer not 16-byte aligned, h or d not a multiple of 8, unknown dtype,
  *    E > 4096 or E_loc > 1024).  Launch failures return LRM_ERR_HIP.  Nothing is enqueued when a
  *    call returns an error.
@@ -95,17 +97,33 @@ typedef struct {
 } lrm_problem;
 
 /*
- * Quota policy (the pages leave the allocation policy open, LRMoE Sec. 3.2; this is the capacity
- * form C = CF * mean load of "Expert Parallel Math Deep"):
- *   full != 0 :  q_i = n_i                                  (full retention, rho = 1)
- *   otherwise :  q_i = min(n_i, floor(rho_num * L / (rho_den * E_loc)), cap_abs if cap_abs >= 0)
- * computed exactly in 64-bit integers, with n_i the routed count of local expert e_lo + i.
+ * Quota policy.  The pages fix the constraints 0 <= q_i <= n_i and leave the split of the
+ * retained total across experts open (LRMoE Sec. 3.2, Sec. 3.3); `kind` picks one of three
+ * readings.  With n_i the routed count of local expert e_lo + i and L = sum of n_i:
+ *   full != 0 :  q_i = n_i  for every kind                 (full retention, rho = 1)
+ *   LRM_QUOTA_CAP (0, the default of a zeroed struct): the capacity form C = CF * mean load of
+ *                "Expert Parallel Math Deep" ("Capacity and the exact drop-rate formula"):
+ *                q_i = min(n_i, floor(rho_num * L / (rho_den * E_loc)), cap_abs if cap_abs >= 0)
+ *   LRM_QUOTA_PROPORTIONAL (1): a retained total B = min(L, floor(rho_num * L / rho_den)) split
+ *                in proportion to the loads, shares B * n_i / L rounded by largest remainder
+ *                (equal remainders: lower i first); sum q_i = B.  This is the split of LRMoE
+ *                Fig. 4, where loads [4,2,3] keep [3,1,2].  cap_abs must be negative.
+ *   LRM_QUOTA_WATERFILL (2): the same B water-filled under m_i = min(n_i, cap_abs if >= 0):
+ *                q_i = min(m_i, level) at the highest integer level whose total is <= B, then
+ *                one more row to each of the lowest-indexed experts with m_i > level until the
+ *                total is B; q_i = m_i when sum m_i <= B.
+ * Everything is computed exactly in integers on the device.
  */
+#define LRM_QUOTA_CAP 0
+#define LRM_QUOTA_PROPORTIONAL 1
+#define LRM_QUOTA_WATERFILL 2
+
 typedef struct {
   int32_t full;
   int32_t rho_num;
   int32_t rho_den;
   int32_t cap_abs;
+  int32_t kind;   /* LRM_QUOTA_* */
 } lrm_quota_policy;
 
 /* Bytes of device scratch the calls need for this problem (0 if the problem is invalid). */
@@ -140,6 +158,39 @@ lrm_status lrm_plan_quotas(const lrm_problem* problem, const lrm_quota_policy* p
 lrm_status lrm_score(const lrm_problem* problem, const float* topk_w, const void* g,
                      const void* phi, const int32_t* row_pair, const int32_t* fwd_off,
                      float* score, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Selection criteria (LRMoE Table 2 and Sec. 4.7 ablation).  The LRM criterion is lrm_score; the
+ * others are the gradient-only rules and random drop the ablation compares it with:
+ *   LRM_CRIT_LRM      (0)  score[r] = fl32(alpha_p^2 ||g_t||^2 ||phi_r||^2)   (as lrm_score)
+ *   LRM_CRIT_GRAD_SQ  (1)  score[r] = fl32(||g_t||_2^2)        ("L-2 norm for grad")
+ *   LRM_CRIT_GRAD_ABS (2)  score[r] = fl32(sum_i |g_t,i|)      ("absolute value for grad")
+ *   LRM_CRIT_RANDOM   (3)  score[r] = keys[p]                  ("random drop")
+ * with p = row_pair[r], t = p / k.  The gradient-only rules use the upstream gradient g_t alone,
+ * without the routing weight (a gradient-only rule cannot tell apart pairs whose routing weights
+ * or saved activations differ, Sec. 4.7).  Sums are accumulated in float64 in a fixed order and
+ * rounded once.  Random drop ranks by caller-drawn keys, one float32 per pair; independent
+ * uniform keys make each expert's kept set a uniformly random quota-sized subset, and the tie
+ * rule of lrm_select decides equal keys.
+ */
+#define LRM_CRIT_LRM 0
+#define LRM_CRIT_GRAD_SQ 1
+#define LRM_CRIT_GRAD_ABS 2
+#define LRM_CRIT_RANDOM 3
+
+/*
+ * Score of every local forward row under `criterion` (LRM_CRIT_*).
+ *  in : topk_w float32 [T*k] (LRM only); g [T][h] (all but RANDOM); phi [L_cap][d] (LRM only);
+ *       keys float32 [T*k] (RANDOM only); row_pair int32 [L_cap]; fwd_off int32 [E_loc+1]
+ *       (only fwd_off[E_loc] = L is read).  Inputs a criterion does not read may be NULL.
+ *  out: score float32 [L_cap] (first L written)
+ * An unknown criterion or a NULL input the criterion reads returns LRM_ERR_INVALID_ARGUMENT.
+ * Non-finite or negative results (a NaN or negative key included) set LRM_DEVERR_NONFINITE.
+ */
+lrm_status lrm_score_criterion(const lrm_problem* problem, int32_t criterion, const float* topk_w,
+                               const void* g, const void* phi, const float* keys,
+                               const int32_t* row_pair, const int32_t* fwd_off, float* score,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Per-expert top-q selection (LRMoE Algorithm 1 step 14; Appendix 7.2 Prop. 7.1).  In each

@@ -316,7 +316,10 @@ def make(cfg, **overrides) -> Workload:
                     layout_pairs, bias, src_tok)
 
 
-def policy(sp: Spec, *, full: bool = False, rho=None) -> dict:
-    """Quota policy of a workload: q_e = n_e if full, else min(n_e, floor(num*L/(den*E_loc)), cap)."""
+def policy(sp: Spec, *, full: bool = False, rho=None, kind: str = "cap", cap=None) -> dict:
+    """Quota policy of a workload (its retention fraction and cap unless overridden); `kind`
+    names the split ("cap", "proportional" or "waterfill")."""
     num, den = (sp.rho_num, sp.rho_den) if rho is None else rho
-    return {"full": int(full), "rho_num": int(num), "rho_den": int(den), "cap_abs": int(sp.cap_abs)}
+    c = sp.cap_abs if cap is None else cap
+    return {"full": int(full), "rho_num": int(num), "rho_den": int(den), "cap_abs": int(c),
+            "kind": kind}

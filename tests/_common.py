@@ -23,7 +23,8 @@ def problem(sp, K_cap=None):
 
 def policy_obj(pol):
     from backward_token_expert_amd import lrm
-    return lrm.make_policy(pol["full"], pol["rho_num"], pol["rho_den"], pol["cap_abs"])
+    return lrm.make_policy(pol["full"], pol["rho_num"], pol["rho_den"], pol["cap_abs"],
+                           pol.get("kind", "cap"))
 
 
 @functools.lru_cache(maxsize=4)
@@ -31,10 +32,11 @@ def workload(cfg, **over):
     return synth.make(cfg, **dict(over))
 
 
-def oracle_run(w, pol, gemms=True):
+def oracle_run(w, pol, gemms=True, criterion="lrm", keys=None):
     sp = w.spec
     return O.run(w.topk_idx, w.topk_w, w.g, w.phi, w.W, T=sp.T, k=sp.k, E=sp.E, e_lo=sp.e_lo,
-                 E_loc=sp.E_loc, dtype=sp.dtype, policy=pol, gemms=gemms)
+                 E_loc=sp.E_loc, dtype=sp.dtype, policy=pol, gemms=gemms, criterion=criterion,
+                 keys=keys)
 
 
 def upload(w, device="cuda"):

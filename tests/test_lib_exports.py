@@ -61,6 +61,17 @@ def test_workspace_bytes_and_validation_on_host():
     pol0 = bte.make_policy(0, 1, 0, -1)
     assert lib.lrm_plan_quotas(P, ctypes.byref(pol0), fake, fake, fake, fake, fake, fake, fake, n,
                                None) == 1
+    # quota kinds: unknown kind, or a cap with the proportional split
+    for kp in (bte.make_policy(0, 1, 2, -1, kind=3), bte.make_policy(0, 1, 2, 5, kind="proportional")):
+        assert lib.lrm_plan_quotas(P, ctypes.byref(kp), fake, fake, fake, fake, fake, fake, fake, n,
+                                   None) == 1
+    # criteria: unknown criterion; a NULL input the criterion reads; a misaligned g
+    sc = lib.lrm_score_criterion
+    assert sc(P, 4, fake, fake, fake, fake, fake, fake, fake, fake, n, None) == 1
+    assert sc(P, 3, None, None, None, None, fake, fake, fake, fake, n, None) == 1   # no keys
+    assert sc(P, 1, None, None, None, None, fake, fake, fake, fake, n, None) == 1   # no g
+    assert sc(P, 2, None, fake + 2, None, None, fake, fake, fake, fake, n, None) == 2
+    assert sc(P, 0, None, fake, fake, None, fake, fake, fake, fake, n, None) == 1   # LRM: no topk_w
     assert lib.lrm_status_string(3) == b"workspace too small"
 
 
