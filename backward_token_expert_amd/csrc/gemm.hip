@@ -451,7 +451,7 @@ template <class C, int S>
 __global__ __launch_bounds__(C::THREADS) void dw_bf16(const uint16_t* __restrict__ Gc,
                                                      const uint16_t* __restrict__ Phic,
                                                      const int32_t* __restrict__ sched, int nxcd,
-                                                     int E_loc, int h, int d,
+                                                     int E_loc, int K_cap, int h, int d,
                                                      float* __restrict__ dW,
                                                      float* __restrict__ slots) {
   using R = Ring<C, S>;
@@ -469,6 +469,10 @@ __global__ __launch_bounds__(C::THREADS) void dw_bf16(const uint16_t* __restrict
   for (int u = j; u < units; u += gs) {
     const int32_t* jb = jobs + 4 * (u / tpe);
     const int e = jb[0], kb = jb[1], ke = jb[2], slot = jb[3], local = u % tpe;
+    if (slot == -2) continue;  // an empty piece of a split expert
+    // a record outside the buffers (never written so by dw_schedule) is skipped, not followed
+    if (e < 0 || e >= E_loc || kb < 0 || ke < kb || ke > K_cap || slot < -1 || slot >= kMaxDwSlots)
+      continue;
     const int m0 = (local / tn) * C::BM, n0 = (local % tn) * C::BN;
     const Operands o{Gc, h, m0, h, Phic, d, n0, d, kb, ke};
     zero_acc(acc);
@@ -481,12 +485,14 @@ __global__ __launch_bounds__(C::THREADS) void dw_bf16(const uint16_t* __restrict
 // dW of each split expert += its partial slots, in piece order (kFixupBlocks blocks per expert).
 constexpr int kFixupBlocks = 512;
 
-__global__ __launch_bounds__(256) void dw_fixup(const int32_t* __restrict__ sched, int h, int d,
+__global__ __launch_bounds__(256) void dw_fixup(const int32_t* __restrict__ sched, int E_loc,
+                                                int h, int d,
                                                 const float* __restrict__ slots,
                                                 float* __restrict__ dW) {
   const int sp = blockIdx.x / kFixupBlocks, part = blockIdx.x % kFixupBlocks;
   if (sp >= sched[2]) return;
   const int e = sched[4 + 3 * sp], first = sched[5 + 3 * sp], extra = sched[6 + 3 * sp];
+  if (e < 0 || e >= E_loc || first < 0 || extra < 0 || first + extra > kMaxDwSlots) return;
   const int64_t n4 = (int64_t)h * d / 4;
   float4* out = (float4*)(dW + (int64_t)e * h * d);
   for (int64_t q = (int64_t)part * 256 + threadIdx.x; q < n4; q += (int64_t)kFixupBlocks * 256) {
@@ -534,121 +540,135 @@ __global__ __launch_bounds__(C::THREADS) void dx_bf16(const uint16_t* __restrict
   }
 }
 
-// dW schedule (one workgroup).  G = nxcd * gpx groups; T = ceil(total rows / G) is a group's fair
-// share.  Experts are ranked by retained rows (descending, ties by id).  Two plans:
+// dW schedule (one workgroup, one thread per expert rank).  A job (one expert, or a piece of one
+// along K) costs its K steps plus kDwJobCost (the fixed price of a job: the store of its fp32 tile,
+// prologue and drain); G = nxcd * gpx groups share the total cost, T = ceil(total / G) each.
+// Experts are ranked by retained rows (descending, ties by id).  Two plans:
 //  * whole experts dealt to the groups in snake order (0..G-1, G-1..0, ..);
-//  * when that leaves some group more than 5T/4 rows (one expert far above the share) and the
-//    slots suffice, a contiguous fill: the ranked experts are concatenated and cut into G runs of
-//    T rows (cuts on K-step multiples), so an expert may span several groups; its first piece
-//    writes dW and every later piece a partial slot, which dw_fixup adds in piece order.
-// Empty experts are jobs too (they write zeros), dealt round-robin.
+//  * when that leaves a group above 5T/4 and the slots suffice, a contiguous fill: the ranked
+//    experts' costs are laid end to end and cut into G runs of T, an expert crossing a cut is
+//    split there (cuts on K-step multiples, in proportion to its cost).  The first non-empty
+//    piece writes dW, every later non-empty piece a partial slot that dw_fixup adds in piece
+//    order; an empty piece is a skip record (slot -2).  An expert without rows writes zeros.
+// Every step is a closed form or a workgroup scan, so the schedule costs a few barriers.
+constexpr int kDwJobCost = 8;
+
 __global__ __launch_bounds__(1024) void dw_schedule(const int32_t* __restrict__ cmp_off, int E_loc,
                                                     int K_cap, int groups, int gpx,
                                                     int32_t* __restrict__ sched) {
-  __shared__ int ke[1024], ks[1024], by_rank[1024];
-  __shared__ int load[kMaxXcd * kMaxGroupsPerXcd], count[kMaxXcd * kMaxGroupsPerXcd];
+  constexpr int kG = kMaxXcd * kMaxGroupsPerXcd;
+  __shared__ int rows[1024], by_rank[1024];
+  __shared__ int load[kG], first[kG], count[kG];
   __shared__ int sh[40];
-  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  const int tid = threadIdx.x;
   int mine = 0;
   if (tid < E_loc) {
     int a = cmp_off[tid], b = cmp_off[tid + 1];
     a = a < 0 ? 0 : (a > K_cap ? K_cap : a);
     b = b < a ? a : (b > K_cap ? K_cap : b);
-    ke[tid] = b - a;
-    ks[tid] = a;
     mine = b - a;
+    rows[tid] = mine;
   }
-  if (tid < kMaxXcd * kMaxGroupsPerXcd) {
+  if (tid < kG) {
     load[tid] = 0;
+    first[tid] = 0;
     count[tid] = 0;
   }
-  const int wsum = wave_sum_int(mine);
-  if (lane == 0) sh[w] = wsum;
   __syncthreads();
-  int total = 0;
-  for (int x = 0; x < kThreadsPerSchedule / kWave; ++x) total += sh[x];
-  const int T = total > 0 ? (total + groups - 1) / groups : 1;
   if (tid < E_loc) {
     int rank = 0;
     for (int y = 0; y < E_loc; ++y) {
-      const int o = ke[y];
+      const int o = rows[y];
       rank += (o > mine) || (o == mine && y < tid);
     }
     by_rank[rank] = tid;
   }
   __syncthreads();
-  if (tid == 0) {
-    const int64_t jpg = dw_jobs_per_group(E_loc);
-    auto push = [&](int g, int e, int kb, int kend, int slot) {
-      int32_t* jb = sched + kDwHeader + (int64_t)g * jpg * 4 + 4 * count[g];
-      jb[0] = e;
-      jb[1] = kb;
-      jb[2] = kend;
-      jb[3] = slot;
-      ++count[g];
+  // From here thread r handles the expert of rank r.
+  const int r = tid;
+  const int e = r < E_loc ? by_rank[r] : -1;
+  int s = 0, n = 0;
+  if (e >= 0) {
+    s = cmp_off[e];
+    s = s < 0 ? 0 : (s > K_cap ? K_cap : s);
+    n = rows[e];
+  }
+  const int st = (n + kBK - 1) / kBK;
+  const int c = e >= 0 ? st + kDwJobCost : 0;
+  int total = 0;
+  const int P = block_exclusive_scan_1024(c, sh, &total);
+  const int T = total > 0 ? (total + groups - 1) / groups : 1;
+  const int n2 = 2 * groups, q = r % n2, gs = q < groups ? q : n2 - 1 - q;
+  if (e >= 0) atomicAdd(&load[gs], c);
+  __syncthreads();
+  int worst = 0;
+  for (int g = 0; g < groups; ++g) worst = load[g] > worst ? load[g] : worst;
+  const bool fill = (int64_t)worst * 4 > (int64_t)T * 5 && groups - 1 <= kMaxDwSlots;
+  const int64_t jpg = dw_jobs_per_group(E_loc);
+  auto put = [&](int g, int idx, int kb, int kend, int slot) {
+    int32_t* jb = sched + kDwHeader + (int64_t)g * jpg * 4 + 4 * idx;
+    jb[0] = e;
+    jb[1] = kb;
+    jb[2] = kend;
+    jb[3] = slot;
+  };
+  if (!fill) {
+    // rank r is the (2 * (r / 2G) + [q >= G])-th job of its group
+    if (e >= 0) put(gs, 2 * (r / n2) + (q >= groups ? 1 : 0), s, s + n, -1);
+    if (tid < groups) {
+      const int full = E_loc / n2, rem = E_loc % n2;
+      count[tid] = 2 * full + (tid < rem ? 1 : 0) + (n2 - 1 - tid < rem ? 1 : 0);
+    }
+    if (tid == 0) sched[2] = 0;
+  } else {
+    // the run [P, P + c) meets groups g0..g1; a group's jobs are the ranks whose runs meet it
+    const int g0 = P / T;
+    int g1 = c > 0 ? (P + c - 1) / T : g0;
+    g1 = g1 < groups - 1 ? g1 : groups - 1;
+    if (e >= 0)
+      for (int g = g0; g <= g1; ++g)
+        if ((int64_t)g * T >= P) first[g] = r;  // this run holds the group's first cost unit
+    // cut k (between piece k-1 and k) in K steps, proportional to the cost consumed before it
+    auto cut = [&](int k) -> int {
+      if (k == 0) return 0;
+      if (k > g1 - g0) return st;
+      const int64_t v = ((int64_t)(g0 + k) * T - P) * st / c;
+      return (int)(v < 0 ? 0 : (v > st ? st : v));
     };
-    // plan 1: whole experts, snake order
-    const int n2 = 2 * groups;
-    int worst = 0;
-    for (int r = 0; r < E_loc; ++r) {
-      const int q = r % n2, g = q < groups ? q : n2 - 1 - q;
-      load[g] += ke[by_rank[r]];
-      worst = worst > load[g] ? worst : load[g];
-    }
-    const bool fill = (int64_t)worst * 4 > (int64_t)T * 5 && groups - 1 <= kMaxDwSlots;
-    int nsplit = 0, slots = 0;
-    if (!fill) {
-      for (int r = 0; r < E_loc; ++r) {
-        const int q = r % n2, g = q < groups ? q : n2 - 1 - q, e = by_rank[r];
-        push(g, e, ks[e], ks[e] + ke[e], -1);
+    int nonempty = 0, writer = -1;
+    if (e >= 0)
+      for (int k = 0; k <= g1 - g0; ++k)
+        if (cut(k + 1) > cut(k)) {
+          if (writer < 0) writer = k;
+          ++nonempty;
+        }
+    if (writer < 0) writer = 0;
+    const int need = nonempty > 1 ? nonempty - 1 : 0;
+    int nslots = 0, nsplit = 0;
+    const int slot0 = block_exclusive_scan_1024(need, sh, &nslots);
+    const int rec = block_exclusive_scan_1024(need > 0 ? 1 : 0, sh, &nsplit);
+    // the scans' barriers published first[]
+    if (e >= 0) {
+      int slot = slot0;
+      for (int k = 0; k <= g1 - g0; ++k) {
+        const int a = cut(k), b = cut(k + 1), g = g0 + k;
+        const int kb = s + (a * kBK < n ? a * kBK : n), kend = s + (b * kBK < n ? b * kBK : n);
+        put(g, r - first[g], kb, kend, k == writer ? -1 : (b > a ? slot++ : -2));
+        atomicAdd(&count[g], 1);
       }
-    } else {
-      // plan 2: contiguous fill of T rows per group
-      int g = 0, filled = 0, zero = 0;
-      for (int r = 0; r < E_loc; ++r) {
-        const int e = by_rank[r], n = ke[e], s = ks[e];
-        if (n == 0) {
-          push(zero % groups, e, s, s, -1);
-          ++zero;
-          continue;
-        }
-        int off = 0, first = -1;
-        while (off < n) {
-          int take = n - off;
-          if (g < groups - 1 && filled + take > T) {
-            take = (T - filled) / kBK * kBK;
-            if (take <= 0) {  // this group is full: move on
-              ++g;
-              filled = 0;
-              continue;
-            }
-          }
-          int slot = -1;
-          if (off > 0) {
-            if (first < 0) first = slots;
-            slot = slots++;
-          }
-          push(g, e, s + off, s + off + take, slot);
-          off += take;
-          filled += take;
-          if (g < groups - 1 && filled >= T - kBK + 1) {
-            ++g;
-            filled = 0;
-          }
-        }
-        if (first >= 0) {
-          sched[4 + 3 * nsplit] = e;
-          sched[5 + 3 * nsplit] = first;
-          sched[6 + 3 * nsplit] = slots - first;
-          ++nsplit;
-        }
+      if (need > 0) {
+        sched[4 + 3 * rec] = e;
+        sched[5 + 3 * rec] = slot0;
+        sched[6 + 3 * rec] = need;
       }
     }
-    sched[0] = groups;
-    sched[1] = gpx;
-    sched[2] = nsplit;
+    if (tid == 0) sched[2] = nsplit;
   }
   __syncthreads();
+  if (tid == 0) {
+    sched[0] = groups;
+    sched[1] = gpx;
+  }
   if (tid < groups) sched[4 + 3 * kMaxDwSlots + tid] = count[tid];
 }
 
@@ -915,10 +935,10 @@ void launch_dw_t(const lrm_problem& p, const void* Gc, const void* Phic, const i
   hipLaunchKernelGGL(dw_schedule, dim3(1), dim3(kThreadsPerSchedule), 0, s, cmp_off, p.E_loc,
                      p.K_cap, g.nxcd * gpx, gpx, sched);
   hipLaunchKernelGGL((dw_bf16<C, stages_for<C>()>), dim3(g.blocks), dim3(C::THREADS), 0, s,
-                     (const uint16_t*)Gc, (const uint16_t*)Phic, sched, g.nxcd, p.E_loc, p.h, p.d,
-                     dW, slots);
-  hipLaunchKernelGGL(dw_fixup, dim3(kMaxDwSlots * kFixupBlocks), dim3(256), 0, s, sched, p.h, p.d,
-                     slots, dW);
+                     (const uint16_t*)Gc, (const uint16_t*)Phic, sched, g.nxcd, p.E_loc, p.K_cap,
+                     p.h, p.d, dW, slots);
+  hipLaunchKernelGGL(dw_fixup, dim3(kMaxDwSlots * kFixupBlocks), dim3(256), 0, s, sched, p.E_loc,
+                     p.h, p.d, slots, dW);
 }
 
 template <class C>

@@ -46,6 +46,27 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// Exclusive prefix sum over the 1024 threads of a workgroup; returns the prefix, *total the sum.
+// Every thread of the workgroup must call it (it holds barriers).
+__device__ __forceinline__ int block_exclusive_scan_1024(int v, int* sh /* >= 17 ints */,
+                                                         int* total) {
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) sh[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    const int t = lane < 16 ? sh[lane] : 0;
+    const int ti = wave_inclusive_scan(t);
+    if (lane < 16) sh[lane] = ti - t;  // exclusive wave offsets
+    if (lane == 15) sh[16] = ti;
+  }
+  __syncthreads();
+  const int res = sh[w] + inc - v;
+  *total = sh[16];
+  __syncthreads();
+  return res;
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte streaming load (non-temporal hint: the data is read once).

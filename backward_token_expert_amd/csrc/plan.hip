@@ -58,25 +58,6 @@ __global__ __launch_bounds__(kPlanBlock) void plan_hist(const int32_t* __restric
   }
 }
 
-// Exclusive prefix sum over the 1024 threads of a workgroup; returns the prefix, *total the sum.
-__device__ int block_exclusive_scan_1024(int v, int* sh /* >= 17 ints */, int* total) {
-  const int w = threadIdx.x / kWave, lane = lane_id();
-  const int inc = wave_inclusive_scan(v);
-  if (lane == kWave - 1) sh[w] = inc;
-  __syncthreads();
-  if (w == 0) {
-    const int t = lane < 16 ? sh[lane] : 0;
-    const int ti = wave_inclusive_scan(t);
-    if (lane < 16) sh[lane] = ti - t;  // exclusive wave offsets
-    if (lane == 15) sh[16] = ti;
-  }
-  __syncthreads();
-  const int res = sh[w] + inc - v;
-  *total = sh[16];
-  __syncthreads();
-  return res;
-}
-
 // Largest value over the 1024 threads of a workgroup.
 __device__ int block_max_1024(int v, int* sh /* >= 17 ints */) {
   const int w = threadIdx.x / kWave;

@@ -422,10 +422,15 @@ GEMM_SHAPES = [
     ([70, 0, 130], 4096, 1408),
     ([40, 0, 0, 200], 256, 256),
     ([16500, 16524], 256, 768),
+    # many experts on 256 x 384 tiles: the dW schedule's contiguous fill with split experts,
+    # empty pieces (skip records) and empty experts
+    ([2000, 1500, 0, 3, 40, 700, 1] + [5] * 40 + [0] * 10, 2048, 768),
+    ([2500, 30, 0, 1200, 64, 0] + [33] * 20, 2048, 768),
 ]
 
 
-@pytest.mark.parametrize("Ke,h,d", GEMM_SHAPES, ids=[f"K{sum(k)}-h{h}-d{d}" for k, h, d in GEMM_SHAPES])
+@pytest.mark.parametrize("Ke,h,d", GEMM_SHAPES,
+                         ids=[f"E{len(k)}-K{sum(k)}-h{h}-d{d}" for k, h, d in GEMM_SHAPES])
 def test_grouped_gemms_shapes(Ke, h, d):
     """lrm_grouped_dw / lrm_grouped_dx on seeded bf16 segments against the float64 oracle."""
     torch = _torch()
