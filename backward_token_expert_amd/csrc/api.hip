@@ -144,6 +144,19 @@ lrm_status lrm_grouped_dx(const lrm_problem* problem, const void* Gc, const void
   return from_hip(lrm::launch_dx(*problem, Gc, W, cmp_off, dphi, (char*)ws, wl, stream));
 }
 
+lrm_status lrm_grouped_dw_dx(const lrm_problem* problem, const void* Gc, const void* Phic,
+                             const void* W, const int32_t* cmp_off, float* dW, float* dphi,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!Gc || !Phic || !W || !cmp_off || !dW || !dphi) return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(Gc) || !aligned16(Phic) || !aligned16(W) || !aligned16(dW) || !aligned16(dphi))
+    return LRM_ERR_UNSUPPORTED;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_gemms(*problem, Gc, Phic, W, cmp_off, dW, dphi, (char*)ws, wl,
+                                    stream));
+}
+
 lrm_status lrm_read_device_error(void* ws, int32_t* code, int32_t clear, hipStream_t stream) {
   if (!ws || !code) return LRM_ERR_INVALID_ARGUMENT;
   int32_t v = 0;

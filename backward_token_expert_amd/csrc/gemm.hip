@@ -448,14 +448,11 @@ __device__ __forceinline__ void store_acc(float* __restrict__ out, int64_t ldo, 
 // together and its rows come from HBM once per group.  A job whose output is a slot writes a
 // partial sum of a split expert there (dw_fixup adds it); otherwise it writes dW directly.
 template <class C, int S>
-__global__ __launch_bounds__(C::THREADS) void dw_bf16(const uint16_t* __restrict__ Gc,
-                                                     const uint16_t* __restrict__ Phic,
-                                                     const int32_t* __restrict__ sched, int nxcd,
-                                                     int E_loc, int K_cap, int h, int d,
-                                                     float* __restrict__ dW,
-                                                     float* __restrict__ slots) {
-  using R = Ring<C, S>;
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[R::BYTES / 2];
+__device__ __forceinline__ void dw_jobs(const uint16_t* __restrict__ Gc,
+                                        const uint16_t* __restrict__ Phic,
+                                        const int32_t* __restrict__ sched, int nxcd, int E_loc,
+                                        int K_cap, int h, int d, float* __restrict__ dW,
+                                        float* __restrict__ slots, uint32_t ring_addr) {
   const int tn = (d + C::BN - 1) / C::BN, tm = (h + C::BM - 1) / C::BM, tpe = tm * tn;
   const int x = blockIdx.x % nxcd, i = blockIdx.x / nxcd, nb = gridDim.x / nxcd;
   const int gpx = sched[1], gs = nb / gpx, grp = x * gpx + i / gs, j = i % gs;
@@ -463,7 +460,6 @@ __global__ __launch_bounds__(C::THREADS) void dw_bf16(const uint16_t* __restrict
   const int32_t* jobs = sched + kDwHeader + (int64_t)grp * dw_jobs_per_group(E_loc) * 4;
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), wm = w / C::WN, wn = w % C::WN;
-  const uint32_t ring_addr = lds_addr(ring);
   const FragOffsets<C> fo = frag_offsets<C>(wm, wn, lane);
   f32x16 acc[C::MT][C::NT];
   for (int u = j; u < units; u += gs) {
@@ -480,6 +476,18 @@ __global__ __launch_bounds__(C::THREADS) void dw_bf16(const uint16_t* __restrict
     float* out = slot < 0 ? dW + (int64_t)e * h * d : slots + (int64_t)slot * h * d;
     store_acc(out, d, m0, h, n0, d, wm, wn, lane, acc);
   }
+}
+
+template <class C, int S>
+__global__ __launch_bounds__(C::THREADS) void dw_bf16(const uint16_t* __restrict__ Gc,
+                                                     const uint16_t* __restrict__ Phic,
+                                                     const int32_t* __restrict__ sched, int nxcd,
+                                                     int E_loc, int K_cap, int h, int d,
+                                                     float* __restrict__ dW,
+                                                     float* __restrict__ slots) {
+  using R = Ring<C, S>;
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[R::BYTES / 2];
+  dw_jobs<C, S>(Gc, Phic, sched, nxcd, E_loc, K_cap, h, d, dW, slots, lds_addr(ring));
 }
 
 // dW of each split expert += its partial slots, in piece order (kFixupBlocks blocks per expert).
@@ -508,8 +516,30 @@ __global__ __launch_bounds__(256) void dw_fixup(const int32_t* __restrict__ sche
   }
 }
 
-// dphi: persistent.  Units = (row tile from the tile table, column tile), columns fastest; die x
-// owns the contiguous unit range [x * per, (x + 1) * per).
+// dphi units = (row tile from the tile table, column tile), columns fastest: unit u covers rows
+// [m0, min(m0 + BM, end of its expert's segment)) and columns [n0, n0 + BN).
+template <class C, int S>
+__device__ __forceinline__ void dx_unit(const uint16_t* __restrict__ Gc,
+                                        const uint16_t* __restrict__ W,
+                                        const int32_t* __restrict__ cmp_off,
+                                        const int32_t* __restrict__ tiles, int u, int K_cap, int h,
+                                        int d, float* __restrict__ dphi, uint32_t ring_addr,
+                                        f32x16 (&acc)[C::MT][C::NT]) {
+  const int tn = (d + C::BN - 1) / C::BN;
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), wm = w / C::WN, wn = w % C::WN;
+  const FragOffsets<C> fo = frag_offsets<C>(wm, wn, lane);
+  const int mt = u / tn, n0 = (u % tn) * C::BN;
+  const int e = tiles[1 + 2 * mt], m0 = tiles[2 + 2 * mt];
+  int mend = cmp_off[e + 1];
+  mend = mend > K_cap ? K_cap : mend;
+  const Operands o{Gc, h, m0, mend, W + (int64_t)e * h * d, d, n0, d, 0, h};
+  zero_acc(acc);
+  mainloop<C, S>(o, ring_addr, fo, w, lane, acc);
+  store_acc(dphi, d, m0, mend, n0, d, wm, wn, lane, acc);
+}
+
+// dphi: persistent, die x owns the contiguous unit range [x * per, (x + 1) * per).
 template <class C, int S>
 __global__ __launch_bounds__(C::THREADS) void dx_bf16(const uint16_t* __restrict__ Gc,
                                                      const uint16_t* __restrict__ W,
@@ -523,20 +553,58 @@ __global__ __launch_bounds__(C::THREADS) void dx_bf16(const uint16_t* __restrict
   const int total = tiles[0] * tn, per = (total + nxcd - 1) / nxcd;
   const int x = blockIdx.x % nxcd, i = blockIdx.x / nxcd, nb = gridDim.x / nxcd;
   const int u0 = x * per, u1 = u0 + per < total ? u0 + per : total;
-  const int lane = lane_id();
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), wm = w / C::WN, wn = w % C::WN;
-  const uint32_t ring_addr = lds_addr(ring);
-  const FragOffsets<C> fo = frag_offsets<C>(wm, wn, lane);
   f32x16 acc[C::MT][C::NT];
-  for (int u = u0 + i; u < u1; u += nb) {
-    const int mt = u / tn, n0 = (u % tn) * C::BN;
-    const int e = tiles[1 + 2 * mt], m0 = tiles[2 + 2 * mt];
-    int mend = cmp_off[e + 1];
-    mend = mend > K_cap ? K_cap : mend;
-    const Operands o{Gc, h, m0, mend, W + (int64_t)e * h * d, d, n0, d, 0, h};
-    zero_acc(acc);
-    mainloop<C, S>(o, ring_addr, fo, w, lane, acc);
-    store_acc(dphi, d, m0, mend, n0, d, wm, wn, lane, acc);
+  for (int u = u0 + i; u < u1; u += nb)
+    dx_unit<C, S>(Gc, W, cmp_off, tiles, u, K_cap, h, d, dphi, lds_addr(ring), acc);
+}
+
+// dW and dphi in one persistent launch (same tile shape, CW and CX differ only in the row
+// operand's orientation).  Each workgroup first runs its share of the dW jobs exactly as dw_bf16
+// does, then claims dphi units one at a time: from its own die's contiguous range (a counter per
+// die in the workspace, reset by dx_schedule), and once that is exhausted from the other dies' in
+// turn.  The workgroups whose dW share ends early (light groups) thus take more dphi units, and
+// dphi's last partial round is spread over whoever is free.  Each unit is computed whole by the
+// workgroup that claims it, in the same order as in dx_bf16, so results do not depend on which
+// workgroup runs it.  A claim tries every die once, so every workgroup leaves when all ranges are
+// exhausted.
+template <class CW, class CX, int S>
+__global__ __launch_bounds__(CW::THREADS) void gemm_fused(
+    const uint16_t* __restrict__ Gc, const uint16_t* __restrict__ Phic,
+    const uint16_t* __restrict__ W, const int32_t* __restrict__ cmp_off,
+    const int32_t* __restrict__ sched, const int32_t* __restrict__ tiles, int32_t* __restrict__ queue,
+    int nxcd, int E_loc, int K_cap, int h, int d, float* __restrict__ dW,
+    float* __restrict__ slots, float* __restrict__ dphi) {
+  static_assert(CW::BM == CX::BM && CW::BN == CX::BN && CW::THREADS == CX::THREADS, "one shape");
+  using R = Ring<CW, S>;
+  static_assert(Ring<CX, S>::BYTES == R::BYTES, "one ring");
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[R::BYTES / 2];
+  // the claimed unit is broadcast through the ring's first word: every mainloop ends with its
+  // loads drained and a barrier, and the next one starts writing the ring only after the second
+  // barrier below
+  volatile int* claimed = (volatile int*)ring;
+  const uint32_t ring_addr = lds_addr(ring);
+  dw_jobs<CW, S>(Gc, Phic, sched, nxcd, E_loc, K_cap, h, d, dW, slots, ring_addr);
+  const int tn = (d + CX::BN - 1) / CX::BN;
+  const int total = tiles[0] * tn, per = (total + nxcd - 1) / nxcd;
+  const int x = blockIdx.x % nxcd;
+  f32x16 acc[CX::MT][CX::NT];
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int u = -1;
+      for (int k = 0; k < nxcd && u < 0; ++k) {
+        const int y = x + k < nxcd ? x + k : x + k - nxcd;
+        const int lo = y * per, cnt = (lo + per < total ? lo + per : total) - lo;
+        if (cnt <= 0) continue;
+        const int v = atomicAdd(&queue[y], 1);
+        if (v < cnt) u = lo + v;
+      }
+      *claimed = u;
+    }
+    __syncthreads();
+    const int u = __builtin_amdgcn_readfirstlane(*claimed);
+    __syncthreads();
+    if (u < 0) break;
+    dx_unit<CX, S>(Gc, W, cmp_off, tiles, u, K_cap, h, d, dphi, ring_addr, acc);
   }
 }
 
@@ -840,9 +908,11 @@ __global__ __launch_bounds__(kF32Threads) void dx_f32(const float* __restrict__ 
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void dx_schedule(const int32_t* __restrict__ cmp_off, int E_loc,
                                                     int K_cap, int tm, int64_t max_tiles,
-                                                    int32_t* __restrict__ tiles) {
+                                                    int32_t* __restrict__ tiles,
+                                                    int32_t* __restrict__ queue) {
   __shared__ int sh[32];
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  if (queue && tid < kMaxXcd) queue[tid] = 0;  // unit counters of the fused launch
   int base_tiles = 0;
   for (int e0 = 0; e0 < E_loc; e0 += 1024) {
     const int e = e0 + tid;
@@ -921,22 +991,41 @@ int pick_width(int d) {
 }
 
 template <class C>
-void launch_dw_t(const lrm_problem& p, const void* Gc, const void* Phic, const int32_t* cmp_off,
-                 int32_t* sched, float* dW, float* slots, const Grid& g, hipStream_t s) {
-  // groups per die: as many as keep every group at least one job's tiles wide
+int groups_per_die(const lrm_problem& p, const Grid& g) {
+  // as many groups per die as keep every group at least one job's tiles wide
   const int tpe = ((p.h + C::BM - 1) / C::BM) * ((p.d + C::BN - 1) / C::BN);
   const int nb = g.blocks / g.nxcd;
-  int gpx = 1;
   for (int c = kMaxGroupsPerXcd; c > 1; c /= 2)
-    if (nb % c == 0 && tpe * c <= nb) {
-      gpx = c;
-      break;
-    }
+    if (nb % c == 0 && tpe * c <= nb) return c;
+  return 1;
+}
+
+template <class C>
+void launch_dw_t(const lrm_problem& p, const void* Gc, const void* Phic, const int32_t* cmp_off,
+                 int32_t* sched, float* dW, float* slots, const Grid& g, hipStream_t s) {
+  const int gpx = groups_per_die<C>(p, g);
   hipLaunchKernelGGL(dw_schedule, dim3(1), dim3(kThreadsPerSchedule), 0, s, cmp_off, p.E_loc,
                      p.K_cap, g.nxcd * gpx, gpx, sched);
   hipLaunchKernelGGL((dw_bf16<C, stages_for<C>()>), dim3(g.blocks), dim3(C::THREADS), 0, s,
                      (const uint16_t*)Gc, (const uint16_t*)Phic, sched, g.nxcd, p.E_loc, p.K_cap,
                      p.h, p.d, dW, slots);
+  hipLaunchKernelGGL(dw_fixup, dim3(kMaxDwSlots * kFixupBlocks), dim3(256), 0, s, sched, p.E_loc,
+                     p.h, p.d, slots, dW);
+}
+
+template <class CW, class CX>
+void launch_fused_t(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
+                    const int32_t* cmp_off, int32_t* sched, int32_t* tiles, int32_t* queue,
+                    int64_t max_tiles, float* dW, float* slots, float* dphi, const Grid& g,
+                    hipStream_t s) {
+  const int gpx = groups_per_die<CW>(p, g);
+  hipLaunchKernelGGL(dw_schedule, dim3(1), dim3(kThreadsPerSchedule), 0, s, cmp_off, p.E_loc,
+                     p.K_cap, g.nxcd * gpx, gpx, sched);
+  hipLaunchKernelGGL(dx_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, CX::BM,
+                     max_tiles, tiles, queue);
+  hipLaunchKernelGGL((gemm_fused<CW, CX, stages_for<CW>()>), dim3(g.blocks), dim3(CW::THREADS), 0,
+                     s, (const uint16_t*)Gc, (const uint16_t*)Phic, (const uint16_t*)W, cmp_off,
+                     sched, tiles, queue, g.nxcd, p.E_loc, p.K_cap, p.h, p.d, dW, slots, dphi);
   hipLaunchKernelGGL(dw_fixup, dim3(kMaxDwSlots * kFixupBlocks), dim3(256), 0, s, sched, p.E_loc,
                      p.h, p.d, slots, dW);
 }
@@ -980,7 +1069,7 @@ hipError_t launch_dx(const lrm_problem& p, const void* Gc, const void* W, const 
     static_assert(BM == Tile128_dX::BM && BM >= kDxTileM, "one row tile for every width");
     const int64_t max_tiles = ((int64_t)p.K_cap + BM - 1) / BM + p.E_loc;
     hipLaunchKernelGGL(dx_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, BM,
-                       max_tiles, tiles);
+                       max_tiles, tiles, nullptr);
     switch (pick_width(p.d)) {
       case 0: launch_dx_t<TileW_dX>(p, Gc, W, cmp_off, tiles, dphi, g, s); break;
       case 1: launch_dx_t<Tile256_dX>(p, Gc, W, cmp_off, tiles, dphi, g, s); break;
@@ -989,10 +1078,33 @@ hipError_t launch_dx(const lrm_problem& p, const void* Gc, const void* W, const 
     }
   } else {
     hipLaunchKernelGGL(dx_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, FBM,
-                       wl.max_tiles, tiles);
+                       wl.max_tiles, tiles, nullptr);
     const dim3 grid((unsigned)wl.max_tiles, (p.d + FBN - 1) / FBN);
     hipLaunchKernelGGL(dx_f32, grid, dim3(kF32Threads), 0, s, (const float*)Gc, (const float*)W,
                        cmp_off, tiles, p.K_cap, p.h, p.d, dphi);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemms(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
+                        const int32_t* cmp_off, float* dW, float* dphi, char* ws,
+                        const WsLayout& wl, hipStream_t s) {
+  if (p.dtype != LRM_BF16) {
+    const hipError_t e = launch_dw(p, Gc, Phic, cmp_off, dW, ws, wl, s);
+    return e != hipSuccess ? e : launch_dx(p, Gc, W, cmp_off, dphi, ws, wl, s);
+  }
+  const Grid g = persistent_grid();
+  int32_t* sched = (int32_t*)(ws + wl.order);
+  int32_t* tiles = (int32_t*)(ws + wl.tiles);
+  int32_t* queue = (int32_t*)(ws + wl.err) + kQueueWord;
+  float* slots = (float*)(ws + wl.dwslots);
+  static_assert(TileW_dX::BM == Tile128_dX::BM && TileW_dX::BM >= kDxTileM, "row tile");
+  const int64_t max_tiles = ((int64_t)p.K_cap + TileW_dX::BM - 1) / TileW_dX::BM + p.E_loc;
+  switch (pick_width(p.d)) {
+    case 0: launch_fused_t<TileW_dW, TileW_dX>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
+    case 1: launch_fused_t<Tile256_dW, Tile256_dX>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
+    case 2: launch_fused_t<Tile192_dW, Tile192_dX>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
+    default: launch_fused_t<Tile128_dW, Tile128_dX>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
   }
   return hipGetLastError();
 }

@@ -25,9 +25,12 @@ constexpr int kMaxDwSlots = 16;
 constexpr int kDwHeader = 4 + 3 * kMaxDwSlots + kMaxXcd * kMaxGroupsPerXcd;
 __host__ __device__ inline int64_t dw_jobs_per_group(int E_loc) { return (int64_t)E_loc + kMaxDwSlots; }
 
+// Word of the workspace header where the fused GEMM launch keeps its kMaxXcd unit counters.
+constexpr int kQueueWord = 8;
+
 // Layout of the caller-provided workspace (byte offsets, all 256-byte aligned).
 struct WsLayout {
-  size_t err;     // int32 error word, then reserved header words
+  size_t err;     // int32 error word; words kQueueWord.. hold the fused GEMM's unit counters
   size_t hist;    // int32 [nchunks][E+1] per-chunk expert histograms / local prefixes; column E
                   //                      counts expert ids outside [0, E)
   size_t gnorm;   // double [T]           ||g_t||^2
@@ -81,6 +84,9 @@ hipError_t launch_score_criterion(const lrm_problem& p, int criterion, const voi
 hipError_t launch_select(const lrm_problem& p, const float* score, const int32_t* fwd_off,
                          const int32_t* quota, const int32_t* cmp_off, int32_t* sel_row, char* ws,
                          const WsLayout& wl, hipStream_t s);
+hipError_t launch_gemms(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
+                        const int32_t* cmp_off, float* dW, float* dphi, char* ws,
+                        const WsLayout& wl, hipStream_t s);
 hipError_t launch_compact(const lrm_problem& p, const int32_t* sel_row, const int32_t* row_pair,
                           const int32_t* cmp_off, const float* topk_w, const void* g,
                           const void* phi, void* Gc, void* Phic, int32_t* sel_pair, char* ws,

@@ -19,7 +19,7 @@ LRM_F32, LRM_BF16 = 0, 1
 DEVERR = {1: "EXPERT_ID", 2: "L_CAP", 4: "K_CAP", 8: "QUOTA", 16: "NONFINITE", 32: "INDEX"}
 
 EXPORTS = ("lrm_workspace_bytes", "lrm_plan_quotas", "lrm_score", "lrm_score_criterion",
-           "lrm_select", "lrm_compact", "lrm_grouped_dw", "lrm_grouped_dx",
+           "lrm_select", "lrm_compact", "lrm_grouped_dw", "lrm_grouped_dx", "lrm_grouped_dw_dx",
            "lrm_read_device_error", "lrm_status_string")
 
 QUOTA_KINDS = {"cap": 0, "proportional": 1, "waterfill": 2}
@@ -63,9 +63,10 @@ def load_library(path: Optional[str] = None):
     lib.lrm_compact.argtypes = [PP] + [vp] * 10 + [sz, vp]
     lib.lrm_grouped_dw.argtypes = [PP] + [vp] * 5 + [sz, vp]
     lib.lrm_grouped_dx.argtypes = [PP] + [vp] * 5 + [sz, vp]
+    lib.lrm_grouped_dw_dx.argtypes = [PP] + [vp] * 7 + [sz, vp]
     lib.lrm_read_device_error.argtypes = [vp, ctypes.POINTER(i32), i32, vp]
     for f in ("lrm_plan_quotas", "lrm_score", "lrm_score_criterion", "lrm_select", "lrm_compact", "lrm_grouped_dw",
-              "lrm_grouped_dx", "lrm_read_device_error"):
+              "lrm_grouped_dx", "lrm_grouped_dw_dx", "lrm_read_device_error"):
         getattr(lib, f).restype = ctypes.c_int
     lib.lrm_status_string.argtypes = [ctypes.c_int]
     lib.lrm_status_string.restype = ctypes.c_char_p
@@ -163,6 +164,14 @@ def lrm_grouped_dx(problem, Gc, W, cmp_off, dphi, ws, stream=None):
     _check(lib, lib.lrm_grouped_dx(ctypes.byref(problem), _ptr(Gc), _ptr(W), _ptr(cmp_off),
                                    _ptr(dphi), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)), "lrm_grouped_dx")
+
+
+def lrm_grouped_dw_dx(problem, Gc, Phic, W, cmp_off, dW, dphi, ws, stream=None):
+    lib = load_library()
+    _check(lib, lib.lrm_grouped_dw_dx(ctypes.byref(problem), _ptr(Gc), _ptr(Phic), _ptr(W),
+                                      _ptr(cmp_off), _ptr(dW), _ptr(dphi), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)),
+           "lrm_grouped_dw_dx")
 
 
 def lrm_read_device_error(ws, clear: bool = False, stream=None) -> int:

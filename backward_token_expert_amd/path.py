@@ -1,8 +1,9 @@
 """Device buffers and the six-call sequence of the hot path (marshalling only).
 
 ``DeviceBuffers`` allocates, with PyTorch, every output and the workspace of one problem; ``run``
-enqueues lrm_plan_quotas -> lrm_score (or lrm_score_criterion) -> lrm_select -> lrm_compact -> lrm_grouped_dw ->
-lrm_grouped_dx on one stream.  No step of the path is computed here.
+enqueues lrm_plan_quotas -> lrm_score (or lrm_score_criterion) -> lrm_select -> lrm_compact ->
+lrm_grouped_dw_dx (or lrm_grouped_dw -> lrm_grouped_dx) on one stream.  No step of the path is
+computed here.
 """
 from __future__ import annotations
 
@@ -55,10 +56,11 @@ class DeviceBuffers:
 
 
 def run(problem, policy, topk_idx, topk_w, g, phi, W, bufs: DeviceBuffers, stream=None,
-        criterion: str = "lrm", keys=None):
+        criterion: str = "lrm", keys=None, fused: bool = True):
     """Enqueue the whole hot path on `stream` (default: torch's current stream).  `criterion`
     picks the selection score (lrm_score for "lrm", else lrm_score_criterion; "random" ranks by
-    `keys`, one float32 per pair)."""
+    `keys`, one float32 per pair).  `fused` runs both GEMMs as lrm_grouped_dw_dx, else as
+    lrm_grouped_dw then lrm_grouped_dx."""
     b = bufs
     lrm.lrm_plan_quotas(problem, policy, topk_idx, b.counts, b.fwd_off, b.row_pair, b.quota,
                         b.cmp_off, b.ws, stream)
@@ -70,5 +72,8 @@ def run(problem, policy, topk_idx, topk_w, g, phi, W, bufs: DeviceBuffers, strea
     lrm.lrm_select(problem, b.score, b.fwd_off, b.quota, b.cmp_off, b.sel_row, b.ws, stream)
     lrm.lrm_compact(problem, b.sel_row, b.row_pair, b.cmp_off, topk_w, g, phi, b.Gc, b.Phic,
                     b.sel_pair, b.ws, stream)
-    lrm.lrm_grouped_dw(problem, b.Gc, b.Phic, b.cmp_off, b.dW, b.ws, stream)
-    lrm.lrm_grouped_dx(problem, b.Gc, W, b.cmp_off, b.dphi, b.ws, stream)
+    if fused:
+        lrm.lrm_grouped_dw_dx(problem, b.Gc, b.Phic, W, b.cmp_off, b.dW, b.dphi, b.ws, stream)
+    else:
+        lrm.lrm_grouped_dw(problem, b.Gc, b.Phic, b.cmp_off, b.dW, b.ws, stream)
+        lrm.lrm_grouped_dx(problem, b.Gc, W, b.cmp_off, b.dphi, b.ws, stream)

@@ -28,7 +28,8 @@ CSRC = os.path.join(PKG, "csrc")
 
 # C-ABI entry point -> (names of its GEMM kernels, translation unit)
 GEMM_KERNELS = {"lrm_grouped_dw": (("dw_bf16", "dw_f32"), "gemm.hip"),
-                "lrm_grouped_dx": (("dx_bf16", "dx_f32"), "gemm.hip")}
+                "lrm_grouped_dx": (("dx_bf16", "dx_f32"), "gemm.hip"),
+                "lrm_grouped_dw_dx": (("gemm_fused",), "gemm.hip")}
 _SHARED = ("lrm_device.hpp", "lrm_internal.hpp")
 
 

@@ -24,7 +24,8 @@ METRIC = "pairs/s thru LRM score+select+compact+grouped dW/dφ GEMM; % bf16 MFMA
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix-core peaks, TFLOP/s
 
-STAGES = ("plan", "score", "select", "compact", "dw", "dx")
+STAGES_FUSED = ("plan", "score", "select", "compact", "gemm")
+STAGES_SPLIT = ("plan", "score", "select", "compact", "dw", "dx")
 
 
 def parse():
@@ -37,6 +38,8 @@ def parse():
                     help="selection score: the LRM, or one of the ablation criteria")
     ap.add_argument("--quota", default="cap", choices=["cap", "proportional", "waterfill"],
                     help="quota split of the retained total")
+    ap.add_argument("--separate-gemms", action="store_true",
+                    help="lrm_grouped_dw then lrm_grouped_dx instead of lrm_grouped_dw_dx")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-experts", type=int, default=16)
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
@@ -76,7 +79,7 @@ def algorithmic(w, oracle_like, criterion="lrm"):
     }
 
 
-def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm"):
+def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True):
     import torch
     from backward_token_expert_amd import lrm, path
     from backward_token_expert_amd.path import to_device, to_host
@@ -92,6 +95,7 @@ def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm"):
     keys = to_device(synth_keys(sp)) if criterion == "random" else None
     b = path.DeviceBuffers(P)
     s = torch.cuda.current_stream()
+    stages = STAGES_FUSED if fused else STAGES_SPLIT
 
     def step(ev=None):
         if ev is not None:
@@ -113,12 +117,15 @@ def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm"):
                         b.ws, s)
         if ev is not None:
             ev[4].record(s)
-        lrm.lrm_grouped_dw(P, b.Gc, b.Phic, b.cmp_off, b.dW, b.ws, s)
+        if fused:
+            lrm.lrm_grouped_dw_dx(P, b.Gc, b.Phic, W, b.cmp_off, b.dW, b.dphi, b.ws, s)
+        else:
+            lrm.lrm_grouped_dw(P, b.Gc, b.Phic, b.cmp_off, b.dW, b.ws, s)
+            if ev is not None:
+                ev[5].record(s)
+            lrm.lrm_grouped_dx(P, b.Gc, W, b.cmp_off, b.dphi, b.ws, s)
         if ev is not None:
-            ev[5].record(s)
-        lrm.lrm_grouped_dx(P, b.Gc, W, b.cmp_off, b.dphi, b.ws, s)
-        if ev is not None:
-            ev[6].record(s)
+            ev[len(stages)].record(s)
 
     for _ in range(warmup):
         step()
@@ -129,7 +136,8 @@ def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm"):
 
     # Timed region: exactly `steps` whole-path steps.  HIP events bracket every stage on the
     # stream the kernels are launched on; they cost nothing measurable next to the stages.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -142,7 +150,7 @@ def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm"):
     wall = time.perf_counter() - t0
     ms_total = t_start.elapsed_time(t_end)
     stage_ms = {st: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
-                for j, st in enumerate(STAGES)}
+                for j, st in enumerate(stages)}
     fo = to_host(b.fwd_off)
     co = to_host(b.cmp_off)
     sel_pair = to_host(b.sel_pair)[:int(co[-1])]
@@ -231,29 +239,34 @@ def main():
     sp = w.spec
     pol = synth.policy(sp, kind=args.quota, cap=-1 if args.quota == "proportional" else None)
     crit = args.criterion
-    ms, wall_ms, stages, info = gpu_bench(w, pol, args.steps, args.warmup, crit)
+    fused = not args.separate_gemms
+    ms, wall_ms, stages, info = gpu_bench(w, pol, args.steps, args.warmup, crit, fused)
     alg = algorithmic(w, info, crit)
     L, K = info["L"], info["K"]
     # rho = 1 (full retention) on the same input
     n1 = max(3, args.steps // 2) if args.rho1_steps is None else args.rho1_steps
     if n1 > 0:
         pol_full = synth.policy(sp, full=True)
-        ms1, _, stages1, info1 = gpu_bench(w, pol_full, n1, 2, crit)
+        ms1, _, stages1, info1 = gpu_bench(w, pol_full, n1, 2, crit, fused)
         alg1 = algorithmic(w, info1, crit)
 
     def fractions(st, a, dtype):
         t_ssc = (st["score"] + st["select"] + st["compact"]) * 1e-3
         by = a["score"] + a["select"] + a["compact"]
-        t_g = (st["dw"] + st["dx"]) * 1e-3
+        t_g = (st["gemm"] if "gemm" in st else st["dw"] + st["dx"]) * 1e-3
         fl = a["flops_dw"] + a["flops_dx"]
         return {"score_select_compact_GBps": by / t_ssc / 1e9,
                 "score_select_compact_hbm_frac": by / t_ssc / 1e9 / HBM_PEAK_GBS,
                 "gemms_TFLOPs": fl / t_g / 1e12,
                 "gemms_mfma_frac": fl / t_g / 1e12 / MFMA_PEAK_TFLOPS[dtype]}
 
-    dom = max(("dw", "dx"), key=lambda s: stages[s])
-    dom_call = {"dw": "lrm_grouped_dw", "dx": "lrm_grouped_dx"}[dom]
-    ach = alg["flops_" + dom] / (stages[dom] * 1e-3) / 1e12
+    if fused:
+        dom_call = "lrm_grouped_dw_dx"
+        ach = (alg["flops_dw"] + alg["flops_dx"]) / (stages["gemm"] * 1e-3) / 1e12
+    else:
+        dom = max(("dw", "dx"), key=lambda s: stages[s])
+        dom_call = {"dw": "lrm_grouped_dw", "dx": "lrm_grouped_dx"}[dom]
+        ach = alg["flops_" + dom] / (stages[dom] * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[sp.dtype]
     out = {
         "metric": METRIC,

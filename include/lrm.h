@@ -19,6 +19,7 @@
  *   lrm_grouped_dx   variable-size grouped FC2 input gradient dphi_u = W_e^T delta_u
  *                    (Appendix 7.1 Eq. (4)-(7); Sec. 3.3: the retained count is the row dimension
  *                    of the input-gradient product)
+ *   lrm_grouped_dw_dx  both of the above in one launch
  *
  * Conventions shared by every call
  * --------------------------------
@@ -249,6 +250,19 @@ lrm_status lrm_grouped_dw(const lrm_problem* problem, const void* Gc, const void
 lrm_status lrm_grouped_dx(const lrm_problem* problem, const void* Gc, const void* W,
                           const int32_t* cmp_off, float* dphi, void* ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/*
+ * Both grouped FC2 gradients in one call: dW exactly as lrm_grouped_dw and dphi exactly as
+ * lrm_grouped_dx (same arguments, same results bit for bit), computed by one persistent launch
+ * for bf16 inputs: workgroups whose share of the weight-gradient tiles ends early take
+ * input-gradient tiles, so neither product leaves the device partly idle while the other still
+ * has work (LRMoE Sec. 3.4: all expert-backward GEMMs run over the retained rows only).  fp32
+ * inputs run the two products one after the other.  Requires Gc, Phic, W, dW, dphi 16-byte
+ * aligned.
+ */
+lrm_status lrm_grouped_dw_dx(const lrm_problem* problem, const void* Gc, const void* Phic,
+                             const void* W, const int32_t* cmp_off, float* dW, float* dphi,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Copies the device error word to *code (host).  Synchronises `stream` (tests and diagnostics

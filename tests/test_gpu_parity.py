@@ -448,10 +448,17 @@ def test_grouped_gemms_shapes(Ke, h, d):
     dphi = torch.zeros((K, d), device="cuda")
     print(f"[case] grouped GEMMs Ke={Ke} h={h} d={d}", flush=True)
     cod = to_device(co)
-    lrm.lrm_grouped_dw(P, to_device(Gc), to_device(Ph), cod, dW, ws)
-    lrm.lrm_grouped_dx(P, to_device(Gc), to_device(W), cod, dphi, ws)
+    Gd, Pd, Wd = to_device(Gc), to_device(Ph), to_device(W)
+    lrm.lrm_grouped_dw(P, Gd, Pd, cod, dW, ws)
+    lrm.lrm_grouped_dx(P, Gd, Wd, cod, dphi, ws)
+    # the one-launch form must give the same bits
+    dW2 = torch.full((E_loc, h, d), -3.0, device="cuda")
+    dphi2 = torch.full((K, d), -3.0, device="cuda")
+    lrm.lrm_grouped_dw_dx(P, Gd, Pd, Wd, cod, dW2, dphi2, ws)
     torch.cuda.synchronize()
     gW, gx = to_host(dW), to_host(dphi)
+    assert to_host(dW2).tobytes() == gW.tobytes()
+    assert to_host(dphi2).tobytes() == gx.tobytes()
     rW = O.grouped_dw(Gc, Ph, co, "bf16")
     rx = O.grouped_dx(Gc, W, co, "bf16")
     tol = C.tol_for("bf16")
@@ -528,11 +535,14 @@ def test_bitwise_determinism_and_graph_replay():
     P = C.problem(sp)
     inp = C.upload(w)
     outs = []
-    for _ in range(2):
+    for fused in (True, True, False):
         b = path.DeviceBuffers(P)
-        path.run(P, pol, inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"], inp["W"], b)
+        path.run(P, pol, inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"], inp["W"], b,
+                 fused=fused)
         torch.cuda.synchronize()
         outs.append(host(b, sp))
+    for key in outs[0]:
+        assert outs[0][key].tobytes() == outs[2][key].tobytes(), ("separate GEMM calls", key)
     for key in outs[0]:
         assert outs[0][key].tobytes() == outs[1][key].tobytes(), key
     # capture the six calls in a graph and replay it; every replay must equal the eager result
