@@ -38,7 +38,14 @@ leave a step open:
   * the compacted weighted cotangent is delta = RNE_dtype(fl32(alpha * g)): one IEEE float32
     product, then round-to-nearest-even to the storage type (Appendix 7.1, Eq. (5) allows exposing
     delta instead of g, applying alpha only once);
-  * dW and dphi are produced in float64 here (fp32 on the GPU).
+  * dW and dphi are produced in float64 here (fp32 on the GPU);
+  * the rest of the expert backward (Sec. 3.1: FC2, the activation function, FC1 and the backward
+    dispatch use the same retained identities; Sec. 3.4: all four expert-backward GEMMs shrink):
+    phi = SiLU(a) * c with a, c the gate and up halves of the saved FC1 output; the activation's
+    cotangent dH = (dphi * c * SiLU'(a), dphi * SiLU(a)) is computed in float64 and rounded once,
+    to nearest even, to the storage type; FC1 maps the token input x (h) to the 2d-wide [a; c];
+    input-gradient rows return to their tokens as a float64 sum over the token's retained slots
+    in slot order, rounded once to float32, and tokens without a retained pair get zeros.
 """
 from __future__ import annotations
 
@@ -414,6 +421,127 @@ def dx_rows(Gc, W, cmp_off, rows_i, dtype: str) -> np.ndarray:
     for j, (i, e) in enumerate(zip(rows_i, e_of)):
         out[j] = widen(Gc[i], dtype) @ widen(W[e], dtype)
     return out
+
+
+# ------------------------------------------------------------------------------------------------
+# rest of the expert backward: activation, FC1 gradients, return to the tokens
+# ------------------------------------------------------------------------------------------------
+
+
+def f64_to_bf16_rne(v: np.ndarray) -> np.ndarray:
+    """Round float64 values directly to bfloat16 (nearest, ties to even); returns uint16 bits.
+
+    bfloat16 keeps 8 significant bits with float32's exponent range.  With v = m * 2^e and
+    1/2 <= |m| < 1, the spacing of bf16 values around v is 2^(e-8), and never finer than the
+    smallest subnormal 2^-133; v is rounded at that spacing (scaling by powers of two is exact,
+    np.rint rounds halves to even).  Values that round beyond the largest finite bf16 become
+    infinities.  Finite inputs only.
+    """
+    v = np.asarray(v, np.float64)
+    _, e = np.frexp(v)
+    q = np.maximum(e - 8, -133)
+    r = np.ldexp(np.rint(np.ldexp(v, -q)), q)
+    with np.errstate(over="ignore"):
+        f = r.astype(np.float32)                   # exact, or +-inf past the finite range
+    return (np.ascontiguousarray(f).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def round_to(v: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 values rounded once, to nearest even, to the storage type."""
+    if dtype == "f32":
+        return np.asarray(v, np.float64).astype(np.float32)
+    if dtype == "bf16":
+        return f64_to_bf16_rne(v)
+    raise ValueError(dtype)
+
+
+def swiglu_backward64(dphi, a, c):
+    """Cotangents of the gate and up inputs of phi = SiLU(a) * c, in float64.
+
+    SiLU(a) = a * s with s = 1 / (1 + exp(-a)) the logistic function, whose derivative is
+    s * (1 - s); so d phi / d a = c * s * (1 + a * (1 - s)) and d phi / d c = SiLU(a), and the
+    cotangents are dA = dphi * c * SiLU'(a), dC = dphi * SiLU(a) (elementwise).
+    """
+    dphi = np.asarray(dphi, np.float64)
+    a = np.asarray(a, np.float64)
+    c = np.asarray(c, np.float64)
+    s = 1.0 / (1.0 + np.exp(-a))
+    silu = a * s
+    dsilu = s * (1.0 + a * (1.0 - s))
+    return (dphi * c) * dsilu, dphi * silu
+
+
+def swiglu_backward(dphi, ac, sel_row, dtype: str, chunk: int = 8192) -> np.ndarray:
+    """The activation's backward over the retained rows: dH[i] = [dA_i | dC_i], rounded to the
+    storage type ([LRMoE] Sec. 3.1: the activation function uses the same retained identities as
+    FC2; its saved context is the FC1 output of the forward row r = sel_row[i]: gate a in columns
+    [0, d), up c in [d, 2d)).  dphi[i] is the FC2 input gradient of retained row i (any float
+    type, taken at its exact value).
+    """
+    sel_row = np.asarray(sel_row, np.int64)
+    K = sel_row.size
+    d = np.asarray(ac).shape[1] // 2
+    out = np.empty((K, 2 * d), np.float32 if dtype == "f32" else np.uint16)
+    for s0 in range(0, K, chunk):                  # row blocks only bound the temporaries
+        rows = slice(s0, s0 + chunk)
+        ctx = widen(np.asarray(ac)[sel_row[rows]], dtype)
+        dA, dC = swiglu_backward64(np.asarray(dphi[rows], np.float64), ctx[:, :d], ctx[:, d:])
+        out[rows, :d] = round_to(dA, dtype)
+        out[rows, d:] = round_to(dC, dtype)
+    return out
+
+
+def gather_tokens(x, sel_pair, k: int) -> np.ndarray:
+    """FC1's input rows of the retained pairs: Xc[i] = x[t] with t = sel_pair[i] // k (exact copy;
+    [LRMoE] Sec. 3.1: retained rows and their matching saved states are gathered in one pair
+    order)."""
+    return np.asarray(x)[np.asarray(sel_pair, np.int64) // k].copy()
+
+
+def fc1_grouped_dw(dH, Xc, cmp_off, dtype: str) -> np.ndarray:
+    """dW1_e = sum over retained rows i of expert e of dH_i x_i^T, shape [E_loc, 2d, h]: the FC1
+    weight gradient over the retained rows only ([LRMoE] Sec. 3.4: repacking shrinks the row
+    dimension of the FC1 weight-gradient GEMM too).  Same definition as the FC2 weight gradient
+    with (dH, Xc) in place of (delta, phi)."""
+    return grouped_dw(dH, Xc, cmp_off, dtype)
+
+
+def fc1_grouped_dx(dH, W1, cmp_off, dtype: str) -> np.ndarray:
+    """dX_i = W1_e^T dH_i for every retained row i of expert e, shape [K, h]: the FC1 input
+    gradient ([LRMoE] Sec. 3.4, FC1 data gradient), W1_e in R^{2d x h} mapping x to [a; c]."""
+    return grouped_dx(dH, W1, cmp_off, dtype)
+
+
+def scatter_with_zeros(dXc, sel_pair, T: int, k: int) -> np.ndarray:
+    """Input gradient of every token: the retained rows' contributions returned to their token
+    and summed, tokens without a retained pair left at zero ([LRMoE] Sec. 3.1: returned
+    input-gradient contributions are scatter-added at their original token and routing-slot
+    positions in zero-initialised dense buffers; Algorithm 1, step 19, ScatterWithZeros).
+
+    Float64 sum per token over its slots j = 0..k-1 in order, starting from zero; shape [T, h].
+    """
+    dXc = np.asarray(dXc)
+    sel_pair = np.asarray(sel_pair, np.int64)
+    row_of = np.full(T * k, -1, np.int64)
+    row_of[sel_pair] = np.arange(sel_pair.size)
+    out = np.zeros((T, dXc.shape[1]), np.float64)
+    tok = np.arange(T, dtype=np.int64)
+    for j in range(k):
+        i = row_of[tok * k + j]
+        m = i >= 0
+        out[m] += np.asarray(dXc[i[m]], np.float64)
+    return out
+
+
+def run_layer(o: dict, dphi, ac, x, W1, *, T: int, k: int, dtype: str) -> dict:
+    """The rest of the expert backward from FC2's input gradient `dphi` (compacted order), on the
+    retained rows of the path result `o` (sel_row, sel_pair, cmp_off)."""
+    dH = swiglu_backward(dphi, ac, o["sel_row"], dtype)
+    Xc = gather_tokens(x, o["sel_pair"], k)
+    dW1 = fc1_grouped_dw(dH, Xc, o["cmp_off"], dtype)
+    dXc = fc1_grouped_dx(dH, W1, o["cmp_off"], dtype)
+    dx = scatter_with_zeros(dXc, o["sel_pair"], T, k)
+    return dict(dH=dH, Xc=Xc, dW1=dW1, dXc=dXc, dx=dx)
 
 
 # ------------------------------------------------------------------------------------------------

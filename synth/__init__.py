@@ -2,7 +2,9 @@
 
 This module builds the inputs that both the GPU library and the CPU oracle are fed: routing
 indices and gate weights from a biased random router, MoE-output gradients ``g``, saved SwiGLU
-activations ``phi`` in the forward dispatch layout, and FC2 weights ``W``.  It holds none of the
+activations ``phi`` in the forward dispatch layout, and FC2 weights ``W``; for the rest of the
+expert backward also the saved FC1 outputs (gate and up halves), the layer input ``x`` and the FC1
+weights ``W1``.  It holds none of the
 method's arithmetic (no counting, quotas, scores, selection, compaction or gradients); the router
 below is the forward gating step that precedes the method, reproduced only to obtain realistic
 routing skew.
@@ -31,7 +33,7 @@ _SO = os.path.join(_HERE, "libsynth.so")
 _LIB = None
 
 # Stream ids of the counter-based generator.
-S_X, S_WR, S_G, S_A, S_C, S_W, S_GSCALE, S_PHISCALE, S_TIES, S_KEYS = range(1, 11)
+S_X, S_WR, S_G, S_A, S_C, S_W, S_GSCALE, S_PHISCALE, S_TIES, S_KEYS, S_W1 = range(1, 12)
 
 _KIND = {"f64": 0, "f32": 1, "bf16": 2}
 
@@ -61,6 +63,8 @@ def _lib():
         lib.synth_uniforms_f32.argtypes = [u64, u64, i64, i64, vp]
         lib.synth_rows.argtypes = [u64, u64, vp, i64, i64, i64, dbl, dbl, u64, ctypes.c_int, vp]
         lib.synth_swiglu_rows.argtypes = [u64, u64, u64, vp, i64, i64, dbl, u64, ctypes.c_int, vp]
+        lib.synth_swiglu_context.argtypes = [u64, u64, u64, vp, i64, i64, dbl, u64, ctypes.c_int,
+                                             vp]
         _LIB = lib
     return _LIB
 
@@ -103,6 +107,17 @@ def swiglu_rows(seed, src_pair, ncols, *, row_sigma=0.0, kind="bf16") -> np.ndar
     out = np.empty((src.shape[0], ncols), dt)
     _lib().synth_swiglu_rows(seed, S_A, S_C, _ptr(src), src.shape[0], ncols, row_sigma,
                              S_PHISCALE, _KIND[kind], _ptr(out))
+    return out
+
+
+def swiglu_context_rows(seed, src_pair, ncols, *, row_sigma=0.0, kind="bf16") -> np.ndarray:
+    """[rows, 2*ncols]: the gate pre-activation a, then the (row-scaled) up projection c, of the
+    draws that swiglu_rows combines into phi."""
+    dt = {"f64": np.float64, "f32": np.float32, "bf16": np.uint16}[kind]
+    src = np.ascontiguousarray(src_pair, np.int64)
+    out = np.empty((src.shape[0], 2 * ncols), dt)
+    _lib().synth_swiglu_context(seed, S_A, S_C, _ptr(src), src.shape[0], ncols, row_sigma,
+                                S_PHISCALE, _KIND[kind], _ptr(out))
     return out
 
 
@@ -314,6 +329,29 @@ def make(cfg, **overrides) -> Workload:
              scale=1.0 / np.sqrt(sp.d), kind=sp.dtype).reshape(sp.E_loc, sp.h, sp.d)
     return Workload(sp, idx.astype(np.int32).copy(), alpha.reshape(-1).copy(), g, phi, W,
                     layout_pairs, bias, src_tok)
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    """Inputs of the rest of the expert backward (FC1 and the activation) of a workload."""
+    ac: np.ndarray   # [L, 2d] saved FC1 outputs per forward row: gate pre-activation a | up c
+    x: np.ndarray    # [T, h] the layer input of every token (FC1's input)
+    W1: np.ndarray   # [E_loc, 2d, h] FC1 weights of the local experts: gate rows, then up rows
+
+
+def layer_inputs(w: Workload) -> LayerInputs:
+    """Saved FC1 outputs, token inputs and FC1 weights for workload ``w``.
+
+    a and c are the draws behind phi (phi = SiLU(a) * c, row scale folded into c), x is the router
+    input of every token rounded to the storage type, W1 ~ N(0, 1/h).  Duplicated tokens copy their
+    source's x and context like every other per-token value."""
+    sp = w.spec
+    src_pair = w.dup_src[w.layout_pairs // sp.k] * sp.k + w.layout_pairs % sp.k
+    ac = swiglu_context_rows(sp.seed, src_pair, sp.d, row_sigma=sp.phi_row_sigma, kind=sp.dtype)
+    x = rows(sp.seed, S_X, sp.T, sp.h, src_row=w.dup_src, kind=sp.dtype)
+    W1 = rows(sp.seed, S_W1, sp.E_loc * 2 * sp.d, sp.h, row0=sp.e_lo * 2 * sp.d,
+              scale=1.0 / np.sqrt(sp.h), kind=sp.dtype).reshape(sp.E_loc, 2 * sp.d, sp.h)
+    return LayerInputs(ac, x, W1)
 
 
 def policy(sp: Spec, *, full: bool = False, rho=None, kind: str = "cap", cap=None) -> dict:

@@ -120,3 +120,26 @@ void synth_swiglu_rows(uint64_t seed, uint64_t sa, uint64_t sc, const int64_t* s
     }
   }
 }
+
+/*
+ * Saved FC1 outputs of the same pairs: row r holds the gate pre-activation a in columns [0, cols)
+ * and the up projection f*c in columns [cols, 2*cols), where a, c and the row scale f are the very
+ * draws synth_swiglu_rows turns into SiLU(a)*c*f.
+ */
+void synth_swiglu_context(uint64_t seed, uint64_t sa, uint64_t sc, const int64_t* src,
+                          int64_t rows, int64_t cols, double row_sigma, uint64_t row_stream,
+                          int kind, void* out) {
+  const uint64_t ka = synth_stream_key(seed, sa), kc = synth_stream_key(seed, sc);
+  const uint64_t rkey = synth_stream_key(seed, row_stream);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t s = src[r];
+    double f = 1.0;
+    if (row_sigma != 0.0) f = exp(row_sigma * normal_at(rkey, (uint64_t)s));
+    for (int64_t j = 0; j < cols; ++j) {
+      const uint64_t id = (uint64_t)(s * cols + j);
+      store(out, r * 2 * cols + j, kind, normal_at(ka, id));
+      store(out, r * 2 * cols + cols + j, kind, f * normal_at(kc, id));
+    }
+  }
+}
