@@ -7,6 +7,8 @@ kernels.  This package only marshals arguments (lrm.py) and sequences the six ca
 """
 from . import lrm, path  # noqa: F401
 from .lrm import (LRM_BF16, LRM_F32, LrmError, Problem, QuotaPolicy, load_library,  # noqa: F401
-                  lrm_compact, lrm_grouped_dw, lrm_grouped_dw_dx, lrm_grouped_dx, lrm_plan_quotas,
+                  lrm_compact, lrm_gather_tokens, lrm_grouped_dw, lrm_grouped_dw_dx,
+                  lrm_grouped_dx, lrm_grouped_fc1_dw, lrm_grouped_fc1_dw_dx, lrm_grouped_fc1_dx,
+                  lrm_plan_quotas, lrm_scatter_tokens, lrm_swiglu_backward,
                   lrm_read_device_error, lrm_score, lrm_score_criterion, lrm_select,
                   lrm_workspace_bytes, make_policy, make_problem)

@@ -34,6 +34,17 @@ lrm_status check_ws(const lrm_problem* p, const void* ws, size_t ws_bytes, WsLay
 
 lrm_status from_hip(hipError_t e) { return e == hipSuccess ? LRM_OK : LRM_ERR_HIP; }
 
+// FC1's gradients are the grouped products of the FC2 calls with the widths exchanged: rows of
+// width 2d (the activation's cotangent dH) against rows of width h (the token inputs x), and FC1
+// weights [E_loc][2d][h].  The workspace layout of this problem differs from the original's only
+// in the size of its last region (the split experts' partial slots).
+lrm_problem fc1_problem(const lrm_problem& p) {
+  lrm_problem q = p;
+  q.h = 2 * p.d;
+  q.d = p.h;
+  return q;
+}
+
 }  // namespace
 
 #define LRM_TRY(expr)                  \
@@ -46,7 +57,8 @@ extern "C" {
 
 size_t lrm_workspace_bytes(const lrm_problem* problem) {
   if (check_problem(problem) != LRM_OK) return 0;
-  return lrm::ws_layout(*problem).total;
+  const size_t a = lrm::ws_layout(*problem).total, b = lrm::ws_layout(fc1_problem(*problem)).total;
+  return a > b ? a : b;
 }
 
 lrm_status lrm_plan_quotas(const lrm_problem* problem, const lrm_quota_policy* policy,
@@ -155,6 +167,79 @@ lrm_status lrm_grouped_dw_dx(const lrm_problem* problem, const void* Gc, const v
   LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
   return from_hip(lrm::launch_gemms(*problem, Gc, Phic, W, cmp_off, dW, dphi, (char*)ws, wl,
                                     stream));
+}
+
+lrm_status lrm_swiglu_backward(const lrm_problem* problem, const int32_t* sel_row,
+                                const int32_t* cmp_off, const float* dphi, const void* ac,
+                                void* dH, void* ws, size_t ws_bytes, hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!sel_row || !cmp_off || !dphi || !ac || !dH) return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(dphi) || !aligned16(ac) || !aligned16(dH)) return LRM_ERR_UNSUPPORTED;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_swiglu_bwd(*problem, sel_row, cmp_off, dphi, ac, dH, (char*)ws, wl,
+                                         stream));
+}
+
+lrm_status lrm_gather_tokens(const lrm_problem* problem, const int32_t* sel_pair,
+                             const int32_t* cmp_off, const void* x, void* Xc, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!sel_pair || !cmp_off || !x || !Xc) return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(Xc)) return LRM_ERR_UNSUPPORTED;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_gather_tokens(*problem, sel_pair, cmp_off, x, Xc, (char*)ws, wl,
+                                            stream));
+}
+
+lrm_status lrm_grouped_fc1_dw(const lrm_problem* problem, const void* dH, const void* Xc,
+                              const int32_t* cmp_off, float* dW1, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!dH || !Xc || !cmp_off || !dW1) return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(dH) || !aligned16(Xc) || !aligned16(dW1)) return LRM_ERR_UNSUPPORTED;
+  const lrm_problem q = fc1_problem(*problem);
+  WsLayout wl;
+  LRM_TRY(check_ws(&q, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_dw(q, dH, Xc, cmp_off, dW1, (char*)ws, wl, stream));
+}
+
+lrm_status lrm_grouped_fc1_dx(const lrm_problem* problem, const void* dH, const void* W1,
+                              const int32_t* cmp_off, float* dX, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!dH || !W1 || !cmp_off || !dX) return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(dH) || !aligned16(W1) || !aligned16(dX)) return LRM_ERR_UNSUPPORTED;
+  const lrm_problem q = fc1_problem(*problem);
+  WsLayout wl;
+  LRM_TRY(check_ws(&q, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_dx(q, dH, W1, cmp_off, dX, (char*)ws, wl, stream));
+}
+
+lrm_status lrm_grouped_fc1_dw_dx(const lrm_problem* problem, const void* dH, const void* Xc,
+                                 const void* W1, const int32_t* cmp_off, float* dW1, float* dX,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!dH || !Xc || !W1 || !cmp_off || !dW1 || !dX) return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(dH) || !aligned16(Xc) || !aligned16(W1) || !aligned16(dW1) || !aligned16(dX))
+    return LRM_ERR_UNSUPPORTED;
+  const lrm_problem q = fc1_problem(*problem);
+  WsLayout wl;
+  LRM_TRY(check_ws(&q, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_gemms(q, dH, Xc, W1, cmp_off, dW1, dX, (char*)ws, wl, stream));
+}
+
+lrm_status lrm_scatter_tokens(const lrm_problem* problem, const int32_t* sel_pair,
+                              const int32_t* cmp_off, const float* dX, float* dx, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!sel_pair || !cmp_off || !dX || !dx) return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(dX) || !aligned16(dx)) return LRM_ERR_UNSUPPORTED;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_scatter_tokens(*problem, sel_pair, cmp_off, dX, dx, (char*)ws, wl,
+                                             stream));
 }
 
 lrm_status lrm_read_device_error(void* ws, int32_t* code, int32_t clear, hipStream_t stream) {

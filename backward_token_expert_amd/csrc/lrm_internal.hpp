@@ -87,6 +87,15 @@ hipError_t launch_select(const lrm_problem& p, const float* score, const int32_t
 hipError_t launch_gemms(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
                         const int32_t* cmp_off, float* dW, float* dphi, char* ws,
                         const WsLayout& wl, hipStream_t s);
+hipError_t launch_swiglu_bwd(const lrm_problem& p, const int32_t* sel_row, const int32_t* cmp_off,
+                             const float* dphi, const void* ac, void* dH, char* ws,
+                             const WsLayout& wl, hipStream_t s);
+hipError_t launch_gather_tokens(const lrm_problem& p, const int32_t* sel_pair,
+                                const int32_t* cmp_off, const void* x, void* Xc, char* ws,
+                                const WsLayout& wl, hipStream_t s);
+hipError_t launch_scatter_tokens(const lrm_problem& p, const int32_t* sel_pair,
+                                 const int32_t* cmp_off, const float* dX, float* dx, char* ws,
+                                 const WsLayout& wl, hipStream_t s);
 hipError_t launch_compact(const lrm_problem& p, const int32_t* sel_row, const int32_t* row_pair,
                           const int32_t* cmp_off, const float* topk_w, const void* g,
                           const void* phi, void* Gc, void* Phic, int32_t* sel_pair, char* ws,

@@ -20,7 +20,9 @@ DEVERR = {1: "EXPERT_ID", 2: "L_CAP", 4: "K_CAP", 8: "QUOTA", 16: "NONFINITE", 3
 
 EXPORTS = ("lrm_workspace_bytes", "lrm_plan_quotas", "lrm_score", "lrm_score_criterion",
            "lrm_select", "lrm_compact", "lrm_grouped_dw", "lrm_grouped_dx", "lrm_grouped_dw_dx",
-           "lrm_read_device_error", "lrm_status_string")
+           "lrm_swiglu_backward", "lrm_gather_tokens", "lrm_grouped_fc1_dw", "lrm_grouped_fc1_dx",
+           "lrm_grouped_fc1_dw_dx", "lrm_scatter_tokens", "lrm_read_device_error",
+           "lrm_status_string")
 
 QUOTA_KINDS = {"cap": 0, "proportional": 1, "waterfill": 2}
 CRITERIA = {"lrm": 0, "grad_sq": 1, "grad_abs": 2, "random": 3}
@@ -64,10 +66,16 @@ def load_library(path: Optional[str] = None):
     lib.lrm_grouped_dw.argtypes = [PP] + [vp] * 5 + [sz, vp]
     lib.lrm_grouped_dx.argtypes = [PP] + [vp] * 5 + [sz, vp]
     lib.lrm_grouped_dw_dx.argtypes = [PP] + [vp] * 7 + [sz, vp]
+    lib.lrm_swiglu_backward.argtypes = [PP] + [vp] * 6 + [sz, vp]
+    lib.lrm_gather_tokens.argtypes = [PP] + [vp] * 5 + [sz, vp]
+    lib.lrm_grouped_fc1_dw.argtypes = [PP] + [vp] * 5 + [sz, vp]
+    lib.lrm_grouped_fc1_dx.argtypes = [PP] + [vp] * 5 + [sz, vp]
+    lib.lrm_grouped_fc1_dw_dx.argtypes = [PP] + [vp] * 7 + [sz, vp]
+    lib.lrm_scatter_tokens.argtypes = [PP] + [vp] * 5 + [sz, vp]
     lib.lrm_read_device_error.argtypes = [vp, ctypes.POINTER(i32), i32, vp]
-    for f in ("lrm_plan_quotas", "lrm_score", "lrm_score_criterion", "lrm_select", "lrm_compact", "lrm_grouped_dw",
-              "lrm_grouped_dx", "lrm_grouped_dw_dx", "lrm_read_device_error"):
-        getattr(lib, f).restype = ctypes.c_int
+    for f in EXPORTS:
+        if f not in ("lrm_workspace_bytes", "lrm_status_string"):
+            getattr(lib, f).restype = ctypes.c_int
     lib.lrm_status_string.argtypes = [ctypes.c_int]
     lib.lrm_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -172,6 +180,50 @@ def lrm_grouped_dw_dx(problem, Gc, Phic, W, cmp_off, dW, dphi, ws, stream=None):
                                       _ptr(cmp_off), _ptr(dW), _ptr(dphi), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream)),
            "lrm_grouped_dw_dx")
+
+
+def _ws(ws):
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def lrm_swiglu_backward(problem, sel_row, cmp_off, dphi, ac, dH, ws, stream=None):
+    lib = load_library()
+    _check(lib, lib.lrm_swiglu_backward(ctypes.byref(problem), _ptr(sel_row), _ptr(cmp_off),
+                                        _ptr(dphi), _ptr(ac), _ptr(dH), *_ws(ws),
+                                        _stream(stream)), "lrm_swiglu_backward")
+
+
+def lrm_gather_tokens(problem, sel_pair, cmp_off, x, Xc, ws, stream=None):
+    lib = load_library()
+    _check(lib, lib.lrm_gather_tokens(ctypes.byref(problem), _ptr(sel_pair), _ptr(cmp_off),
+                                      _ptr(x), _ptr(Xc), *_ws(ws), _stream(stream)),
+           "lrm_gather_tokens")
+
+
+def lrm_grouped_fc1_dw(problem, dH, Xc, cmp_off, dW1, ws, stream=None):
+    lib = load_library()
+    _check(lib, lib.lrm_grouped_fc1_dw(ctypes.byref(problem), _ptr(dH), _ptr(Xc), _ptr(cmp_off),
+                                       _ptr(dW1), *_ws(ws), _stream(stream)), "lrm_grouped_fc1_dw")
+
+
+def lrm_grouped_fc1_dx(problem, dH, W1, cmp_off, dX, ws, stream=None):
+    lib = load_library()
+    _check(lib, lib.lrm_grouped_fc1_dx(ctypes.byref(problem), _ptr(dH), _ptr(W1), _ptr(cmp_off),
+                                       _ptr(dX), *_ws(ws), _stream(stream)), "lrm_grouped_fc1_dx")
+
+
+def lrm_grouped_fc1_dw_dx(problem, dH, Xc, W1, cmp_off, dW1, dX, ws, stream=None):
+    lib = load_library()
+    _check(lib, lib.lrm_grouped_fc1_dw_dx(ctypes.byref(problem), _ptr(dH), _ptr(Xc), _ptr(W1),
+                                          _ptr(cmp_off), _ptr(dW1), _ptr(dX), *_ws(ws),
+                                          _stream(stream)), "lrm_grouped_fc1_dw_dx")
+
+
+def lrm_scatter_tokens(problem, sel_pair, cmp_off, dX, dx, ws, stream=None):
+    lib = load_library()
+    _check(lib, lib.lrm_scatter_tokens(ctypes.byref(problem), _ptr(sel_pair), _ptr(cmp_off),
+                                       _ptr(dX), _ptr(dx), *_ws(ws), _stream(stream)),
+           "lrm_scatter_tokens")
 
 
 def lrm_read_device_error(ws, clear: bool = False, stream=None) -> int:

@@ -1,9 +1,11 @@
-"""Device buffers and the six-call sequence of the hot path (marshalling only).
+"""Device buffers and the call sequences of the hot path (marshalling only).
 
 ``DeviceBuffers`` allocates, with PyTorch, every output and the workspace of one problem; ``run``
 enqueues lrm_plan_quotas -> lrm_score (or lrm_score_criterion) -> lrm_select -> lrm_compact ->
-lrm_grouped_dw_dx (or lrm_grouped_dw -> lrm_grouped_dx) on one stream.  No step of the path is
-computed here.
+lrm_grouped_dw_dx (or lrm_grouped_dw -> lrm_grouped_dx) on one stream.  ``LayerBuffers`` and
+``run_layer`` do the same for the rest of the expert backward over the retained rows:
+lrm_swiglu_backward -> lrm_gather_tokens -> lrm_grouped_fc1_dw_dx (or the two FC1 calls) ->
+lrm_scatter_tokens.  No step of the path is computed here.
 """
 from __future__ import annotations
 
@@ -77,3 +79,33 @@ def run(problem, policy, topk_idx, topk_w, g, phi, W, bufs: DeviceBuffers, strea
     else:
         lrm.lrm_grouped_dw(problem, b.Gc, b.Phic, b.cmp_off, b.dW, b.ws, stream)
         lrm.lrm_grouped_dx(problem, b.Gc, W, b.cmp_off, b.dphi, b.ws, stream)
+
+
+class LayerBuffers:
+    """Outputs of the rest of the expert backward, sized to the problem's capacities."""
+
+    def __init__(self, problem: lrm.Problem, device="cuda"):
+        p = problem
+        st = storage_dtype("bf16" if p.dtype == lrm.LRM_BF16 else "f32")
+        f32 = dict(dtype=torch.float32, device=device)
+        self.dH = torch.zeros((p.K_cap, 2 * p.d), dtype=st, device=device)
+        self.Xc = torch.zeros((p.K_cap, p.h), dtype=st, device=device)
+        self.dW1 = torch.zeros((p.E_loc, 2 * p.d, p.h), **f32)
+        self.dX = torch.zeros((p.K_cap, p.h), **f32)
+        self.dx = torch.zeros((p.T, p.h), **f32)
+
+
+def run_layer(problem, ac, x, W1, bufs: DeviceBuffers, lay: LayerBuffers, stream=None,
+              fused: bool = True):
+    """Enqueue the rest of the expert backward after ``run`` on the same buffers: the activation's
+    backward from dphi, FC1's input rows, the FC1 gradients and the return to the tokens."""
+    b = bufs
+    lrm.lrm_swiglu_backward(problem, b.sel_row, b.cmp_off, b.dphi, ac, lay.dH, b.ws, stream)
+    lrm.lrm_gather_tokens(problem, b.sel_pair, b.cmp_off, x, lay.Xc, b.ws, stream)
+    if fused:
+        lrm.lrm_grouped_fc1_dw_dx(problem, lay.dH, lay.Xc, W1, b.cmp_off, lay.dW1, lay.dX, b.ws,
+                                  stream)
+    else:
+        lrm.lrm_grouped_fc1_dw(problem, lay.dH, lay.Xc, b.cmp_off, lay.dW1, b.ws, stream)
+        lrm.lrm_grouped_fc1_dx(problem, lay.dH, W1, b.cmp_off, lay.dX, b.ws, stream)
+    lrm.lrm_scatter_tokens(problem, b.sel_pair, b.cmp_off, lay.dX, lay.dx, b.ws, stream)

@@ -2,7 +2,10 @@
 """Throughput of the LRMoE backward hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input already resident in HBM:
-lrm_plan_quotas -> lrm_score -> lrm_select -> lrm_compact -> lrm_grouped_dw -> lrm_grouped_dx.
+lrm_plan_quotas -> lrm_score -> lrm_select -> lrm_compact -> lrm_grouped_dw_dx (both FC2
+gradients; --separate-gemms: lrm_grouped_dw -> lrm_grouped_dx).  The rest of the expert backward
+over the same retained rows (activation, FC1 gradients, return to the tokens) is timed after it
+as its own leg ("layer_backward"), outside the step.
 
 Default workload: the Qwen3-30B-A3B-shaped share of one GPU (128 experts, 16 local, top-8,
 32768 tokens, h=2048, d_ffn=768, bf16, retention rho = 0.5).  Prints ONE JSON line.
@@ -46,6 +49,9 @@ def parse():
                     help="repeat the oracle sample until at least this much CPU time has passed")
     ap.add_argument("--rho1-steps", type=int, default=None,
                     help="timed steps of the full-retention pass (default steps/2; 0 skips it)")
+    ap.add_argument("--layer-steps", type=int, default=None,
+                    help="timed steps of the rest of the expert backward (activation, FC1, return "
+                         "to the tokens) on the retained rows (default steps/2; 0 skips it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=512,
                     help="after timing, copy a buffer of this size once (a plain copy kernel of "
                          "known traffic, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE); 0 skips it")
@@ -157,6 +163,92 @@ def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True):
     info = {"L": int(fo[-1]), "K": int(co[-1]), "Ke": np.diff(co),
             "T_ret": int(np.unique(sel_pair // sp.k).size)}
     return ms_total / steps, wall / steps * 1e3, stage_ms, info
+
+
+LAYER_STAGES = ("swiglu", "gather", "fc1_gemm", "scatter")
+
+
+def layer_algorithmic(w, info):
+    """Algorithmic bytes / flops of the rest of the expert backward over K retained rows."""
+    sp = w.spec
+    b = 2 if sp.dtype == "bf16" else 4
+    K, T_ret, Ke = info["K"], info["T_ret"], info["Ke"]
+    h, d = sp.h, sp.d
+    return {
+        "swiglu": 4 * K + 4 * K * d + 2 * K * d * b + 2 * K * d * b,   # sel_row, dphi, [a|c], dH
+        "gather": 8 * K + T_ret * h * b + K * h * b,                    # ids, x once per token, Xc
+        "fc1_dw": K * (2 * d + h) * b + 4 * sp.E_loc * 2 * d * h,
+        "fc1_dx": K * 2 * d * b + int((Ke > 0).sum()) * 2 * d * h * b + 4 * K * h,
+        "scatter": 8 * K + 4 * K * h + 4 * sp.T * h,                    # ids, dX rows, dx rows
+        "flops_fc1": 8 * K * h * d,                                     # 2 products, 2*K*(2d)*h
+    }
+
+
+def layer_bench(w, pol_dict, steps, warmup, criterion="lrm"):
+    """Time the rest of the expert backward after one pass of the path: lrm_swiglu_backward,
+    lrm_gather_tokens, lrm_grouped_fc1_dw_dx, lrm_scatter_tokens, stage by stage."""
+    import torch
+    import synth
+    from backward_token_expert_amd import lrm, path
+    from backward_token_expert_amd.path import to_device, to_host
+    sp = w.spec
+    L_cap = sp.T * min(sp.k, sp.E_loc)
+    P = lrm.make_problem(sp.T, sp.k, sp.E, sp.e_lo, sp.E_loc, sp.h, sp.d, sp.dtype, L_cap, L_cap)
+    pol = lrm.make_policy(pol_dict["full"], pol_dict["rho_num"], pol_dict["rho_den"],
+                          pol_dict["cap_abs"], pol_dict.get("kind", "cap"))
+    li = synth.layer_inputs(w)
+    pad = lambda a: a if a.shape[0] >= L_cap else np.concatenate(  # noqa: E731
+        [a, np.zeros((L_cap - a.shape[0], a.shape[1]), a.dtype)])
+    idx, tw, g, ph, W = (to_device(a) for a in (w.topk_idx, w.topk_w, w.g, pad(w.phi), w.W))
+    ac, x, W1 = to_device(pad(li.ac)), to_device(li.x), to_device(li.W1)
+    keys = to_device(synth_keys(sp)) if criterion == "random" else None
+    b = path.DeviceBuffers(P)
+    lay = path.LayerBuffers(P)
+    s = torch.cuda.current_stream()
+    path.run(P, pol, idx, tw, g, ph, W, b, s, criterion=criterion, keys=keys)
+
+    def step(ev=None):
+        calls = (lambda: lrm.lrm_swiglu_backward(P, b.sel_row, b.cmp_off, b.dphi, ac, lay.dH, b.ws, s),
+                 lambda: lrm.lrm_gather_tokens(P, b.sel_pair, b.cmp_off, x, lay.Xc, b.ws, s),
+                 lambda: lrm.lrm_grouped_fc1_dw_dx(P, lay.dH, lay.Xc, W1, b.cmp_off, lay.dW1,
+                                                   lay.dX, b.ws, s),
+                 lambda: lrm.lrm_scatter_tokens(P, b.sel_pair, b.cmp_off, lay.dX, lay.dx, b.ws, s))
+        for j, c in enumerate(calls):
+            if ev is not None:
+                ev[j].record(s)
+            c()
+        if ev is not None:
+            ev[len(calls)].record(s)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    err = lrm.lrm_read_device_error(b.ws)
+    if err:
+        raise RuntimeError(f"device error word {err}: {lrm.deverr_names(err)}")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(LAYER_STAGES) + 1)]
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    stage_ms = {st: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+                for j, st in enumerate(LAYER_STAGES)}
+    co = to_host(b.cmp_off)
+    sel_pair = to_host(b.sel_pair)[:int(co[-1])]
+    info = {"K": int(co[-1]), "Ke": np.diff(co), "T_ret": int(np.unique(sel_pair // sp.k).size)}
+    a = layer_algorithmic(w, info)
+    t_mem = (stage_ms["swiglu"] + stage_ms["gather"] + stage_ms["scatter"]) * 1e-3
+    by = a["swiglu"] + a["gather"] + a["scatter"]
+    t_g = stage_ms["fc1_gemm"] * 1e-3
+    return {"calls": ["lrm_swiglu_backward", "lrm_gather_tokens", "lrm_grouped_fc1_dw_dx",
+                      "lrm_scatter_tokens"],
+            "steps": steps, "ms_per_step": float(sum(stage_ms.values())),
+            "K_retained": info["K"], "stages_ms": stage_ms,
+            "swiglu_gather_scatter_GBps": by / t_mem / 1e9,
+            "swiglu_gather_scatter_hbm_frac": by / t_mem / 1e9 / HBM_PEAK_GBS,
+            "fc1_TFLOPs": a["flops_fc1"] / t_g / 1e12,
+            "fc1_mfma_frac": a["flops_fc1"] / t_g / 1e12 / MFMA_PEAK_TFLOPS[sp.dtype]}
 
 
 def synth_keys(sp):
@@ -297,6 +389,9 @@ def main():
         out["rho1"] = {"value": info1["L"] / (ms1 * 1e-3), "ms_per_step": ms1,
                        "K_retained": info1["K"], "stages_ms": stages1,
                        "fractions": fractions(stages1, alg1, sp.dtype)}
+    nl = max(3, args.steps // 2) if args.layer_steps is None else args.layer_steps
+    if nl > 0:
+        out["layer_backward"] = layer_bench(w, pol, nl, 2, crit)
     if args.copy_calibration_mib > 0:
         import torch
         n = args.copy_calibration_mib << 20

@@ -21,6 +21,16 @@
  *                    of the input-gradient product)
  *   lrm_grouped_dw_dx  both of the above in one launch
  *
+ * and the rest of the expert backward over the same retained rows (Sec. 3.1: FC2, the activation
+ * function, FC1 and the backward dispatch use the same retained identities; Sec. 3.4: repacking
+ * shrinks all four expert-backward GEMMs; Algorithm 1 step 19, ScatterWithZeros):
+ *   lrm_swiglu_backward   cotangent of the saved FC1 output [a | c] through phi = SiLU(a) * c
+ *   lrm_gather_tokens     FC1's input row x_t of every retained pair
+ *   lrm_grouped_fc1_dw    grouped FC1 weight gradient dW1_e = sum_u dH_u x_u^T
+ *   lrm_grouped_fc1_dx    grouped FC1 input gradient dX_u = W1_e^T dH_u
+ *   lrm_grouped_fc1_dw_dx both in one launch
+ *   lrm_scatter_tokens    input-gradient rows returned to their tokens, zeros elsewhere
+ *
  * Conventions shared by every call
  * --------------------------------
  *  - Pairs.  Token t routes to k experts; pair p = t*k + j, slot j in descending-logit order.
@@ -42,6 +52,11 @@
  *  - Every call enqueues work on `stream` and returns without waiting: no host synchronisation,
  *    no allocation, so a sequence of calls can be captured in a HIP graph.  Results are bitwise
  *    deterministic for identical inputs.
+ *  - Rest of the expert backward: ac is the saved FC1 output per forward row, [L_cap][2d], gate
+ *    pre-activation a in columns [0, d) and up projection c in [d, 2d) (phi = SiLU(a) * c); x is
+ *    the layer input [T][h]; W1 is [E_loc][2d][h] (W1_e maps x (h) to [a; c] (2d)); dH, Xc are
+ *    compacted [K_cap][2d] and [K_cap][h] in the element type; dW1 [E_loc][2d][h], dX [K_cap][h]
+ *    and dx [T][h] are float32.
  *  - ws is caller-provided device scratch of at least lrm_workspace_bytes(problem) bytes,
  *    16-byte aligned.  Its first word is a sticky device error word (LRM_DEVERR_* bits) that
  *    lrm_plan_quotas clears and every call may set; read it with lrm_read_device_error.
@@ -127,7 +142,8 @@ typedef struct {
   int32_t kind;   /* LRM_QUOTA_* */
 } lrm_quota_policy;
 
-/* Bytes of device scratch the calls need for this problem (0 if the problem is invalid). */
+/* Bytes of device scratch every call needs for this problem, the FC1 calls included (0 if the
+ * problem is invalid). */
 size_t lrm_workspace_bytes(const lrm_problem* problem);
 
 /*
@@ -263,6 +279,81 @@ lrm_status lrm_grouped_dx(const lrm_problem* problem, const void* Gc, const void
 lrm_status lrm_grouped_dw_dx(const lrm_problem* problem, const void* Gc, const void* Phic,
                              const void* W, const int32_t* cmp_off, float* dW, float* dphi,
                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward of the SwiGLU activation over the retained rows (LRMoE Sec. 3.1: the activation
+ * function uses the same retained identities as FC2).  For i < K, with r = sel_row[i], a =
+ * ac[r][0:d], c = ac[r][d:2d] and g = dphi[i] (float32, as lrm_grouped_dx writes it):
+ *   s = 1 / (1 + exp(-a)),  SiLU(a) = a s,  SiLU'(a) = s (1 + a (1 - s))
+ *   dH[i][0:d]  = RNE_dtype((g c) SiLU'(a))        (cotangent of the gate a)
+ *   dH[i][d:2d] = RNE_dtype(g SiLU(a))             (cotangent of the up projection c)
+ * evaluated elementwise in float64 in exactly this operation order (no fused multiply-add) and
+ * rounded once, to nearest even, to the element type.
+ *  in : sel_row int32 [K_cap] (as lrm_select writes it); cmp_off (only cmp_off[E_loc] = K read);
+ *       dphi float32 [K_cap][d]; ac [L_cap][2d]
+ *  out: dH [K_cap][2d] (first K rows written)
+ * A selected row outside [0, L_cap) sets LRM_DEVERR_INDEX and gets zeros.  dphi, ac and dH must
+ * be 16-byte aligned.
+ */
+lrm_status lrm_swiglu_backward(const lrm_problem* problem, const int32_t* sel_row,
+                               const int32_t* cmp_off, const float* dphi, const void* ac,
+                               void* dH, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * FC1's input rows of the retained pairs (LRMoE Sec. 3.1: retained rows and their matching saved
+ * states are gathered in one pair order):  Xc[i] = x[sel_pair[i] / k] (bit copy) for i < K.
+ *  in : sel_pair int32 [K_cap] (as lrm_compact writes it); cmp_off (cmp_off[E_loc] = K read);
+ *       x [T][h]
+ *  out: Xc [K_cap][h] (first K rows written)
+ * Each x[t] is read once however many of its pairs are kept.  The workspace's pair -> row map is
+ * rebuilt from sel_pair by this call.  A pair id outside [0, T*k), or two rows naming one pair,
+ * sets LRM_DEVERR_INDEX; the rows concerned are left unwritten.
+ */
+lrm_status lrm_gather_tokens(const lrm_problem* problem, const int32_t* sel_pair,
+                             const int32_t* cmp_off, const void* x, void* Xc, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Grouped FC1 weight gradient over the retained rows only (LRMoE Sec. 3.4: the FC1
+ * weight-gradient GEMM runs over the retained rows):  for every local expert i,
+ *   dW1[i] = sum_{c in [cmp_off[i], cmp_off[i+1])} dH[c]^T (outer) Xc[c]     ([2d][h], float32)
+ * Same kernels and guarantees as lrm_grouped_dw (zeros for an expert with no retained row,
+ * bitwise reproducible) with the widths exchanged.  All pointers 16-byte aligned.
+ */
+lrm_status lrm_grouped_fc1_dw(const lrm_problem* problem, const void* dH, const void* Xc,
+                              const int32_t* cmp_off, float* dW1, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/*
+ * Grouped FC1 input gradient over the retained rows only (LRMoE Sec. 3.4):
+ *   dX[c][j] = sum_o dH[c][o] * W1[i][o][j]   for c in [cmp_off[i], cmp_off[i+1])
+ * i.e. dX[c] = W1_i^T dH[c] ([K_cap][h] float32, first K rows written).  Same kernels as
+ * lrm_grouped_dx with the widths exchanged.  All pointers 16-byte aligned.
+ */
+lrm_status lrm_grouped_fc1_dx(const lrm_problem* problem, const void* dH, const void* W1,
+                              const int32_t* cmp_off, float* dX, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* Both FC1 gradients in one call: results bit for bit those of the two calls above (one
+ * persistent launch for bf16, as lrm_grouped_dw_dx). */
+lrm_status lrm_grouped_fc1_dw_dx(const lrm_problem* problem, const void* dH, const void* Xc,
+                                 const void* W1, const int32_t* cmp_off, float* dW1, float* dX,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Input gradient of every token (LRMoE Sec. 3.1: returned input-gradient contributions are added
+ * at their original token and routing-slot positions in zero-initialised dense buffers;
+ * Algorithm 1 step 19, ScatterWithZeros):
+ *   dx[t] = fl32( sum over slots j = 0..k-1 in order, pair p = t*k + j retained at row i, of
+ *                 dX[i] ),  the sum taken in float64 from zero; dx[t] = 0 if no pair of t is kept
+ *  in : sel_pair int32 [K_cap]; cmp_off (cmp_off[E_loc] = K read); dX float32 [K_cap][h]
+ *  out: dx float32 [T][h] (every row written)
+ * The workspace's pair -> row map is rebuilt from sel_pair by this call.  A pair id outside
+ * [0, T*k), or two rows naming one pair, sets LRM_DEVERR_INDEX.  dX and dx 16-byte aligned.
+ */
+lrm_status lrm_scatter_tokens(const lrm_problem* problem, const int32_t* sel_pair,
+                              const int32_t* cmp_off, const float* dX, float* dx, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
 
 /*
  * Copies the device error word to *code (host).  Synchronises `stream` (tests and diagnostics

@@ -55,8 +55,9 @@ def test_workspace_bytes_and_validation_on_host():
     assert lib.lrm_score(P, fake, fake, fake, fake, fake, None, fake, n, None) == 1
     # misaligned g -> UNSUPPORTED (2)
     assert lib.lrm_score(P, fake, fake + 2, fake, fake, fake, fake, fake, n, None) == 2
-    # short workspace -> WORKSPACE_TOO_SMALL (3)
-    assert lib.lrm_select(P, fake, fake, fake, fake, fake, fake, n - 256, None) == 3
+    # short workspace -> WORKSPACE_TOO_SMALL (3); far below any call's need, so no call can pass
+    # the check and launch with these placeholder pointers
+    assert lib.lrm_select(P, fake, fake, fake, fake, fake, fake, 1024, None) == 3
     # bad retention fraction
     pol0 = bte.make_policy(0, 1, 0, -1)
     assert lib.lrm_plan_quotas(P, ctypes.byref(pol0), fake, fake, fake, fake, fake, fake, fake, n,
@@ -78,3 +79,24 @@ def test_workspace_bytes_and_validation_on_host():
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(lrm.LrmError):
         lrm.load_library(str(tmp_path / "missing.so"))
+
+
+def test_layer_calls_validate_on_host():
+    lib = bte.load_library()
+    p = bte.make_problem(32768, 8, 128, 0, 16, 2048, 768, "bf16", 262144, 262144)
+    n = bte.lrm_workspace_bytes(p)
+    P = ctypes.byref(p)
+    fake = 0x100000  # never dereferenced: each call below is rejected before any launch
+    assert lib.lrm_swiglu_backward(P, fake, fake, fake, fake, None, fake, n, None) == 1
+    assert lib.lrm_swiglu_backward(P, fake, fake, fake + 4, fake, fake, fake, n, None) == 2
+    assert lib.lrm_gather_tokens(P, None, fake, fake, fake, fake, n, None) == 1
+    assert lib.lrm_gather_tokens(P, fake, fake, fake + 8, fake, fake, n, None) == 2
+    assert lib.lrm_scatter_tokens(P, fake, fake, fake, fake, fake, 1024, None) == 3
+    assert lib.lrm_grouped_fc1_dw(P, fake, fake, fake, None, fake, n, None) == 1
+    assert lib.lrm_grouped_fc1_dx(P, fake, fake, fake, fake + 4, fake, n, None) == 2
+    # FC1's split-expert slots are 2d x h: the workspace is sized for them, and a workspace large
+    # enough for FC2's products alone is refused by the FC1 calls
+    fc2_only = n - 16 * 2048 * 768 * 4
+    assert lib.lrm_grouped_fc1_dw_dx(P, fake, fake, fake, fake, fake, fake, fake, fc2_only,
+                                     None) == 3
+    assert lib.lrm_grouped_fc1_dw_dx(P, fake, fake, fake, None, fake, fake, fake, n, None) == 1
