@@ -32,24 +32,24 @@ __device__ __forceinline__ int clamp_k(const int32_t* cmp_off, int E_loc, int K_
 // float64 -> bf16 bits, round to nearest even.  A bf16 value keeps 8 significant bits over
 // float32's exponent range.  Inside the normal range (2^-126 <= |v| < 2^128) the 45 low mantissa
 // bits of the float64 pattern are rounded away (a carry may step the exponent, up to 2^128, which
-// converts to infinity); elsewhere v is rounded at the spacing 2^(e-8) of its binade, never below
-// the smallest bf16 subnormal 2^-133.
-__device__ __forceinline__ uint32_t f64_to_bf16(double v) {
+// converts to infinity); *ok reports whether v was inside that range.
+__device__ __forceinline__ uint32_t f64_to_bf16_normal(double v, bool* ok) {
   uint64_t u = (uint64_t)__double_as_longlong(v);
   const int ex = (int)((u >> 52) & 0x7FF);
-  float f;
-  if (ex >= 1023 - 126 && ex <= 1023 + 127) {
-    const uint64_t low = (1ull << 45) - 1;
-    u += (low >> 1) + ((u >> 45) & 1);
-    u &= ~low;
-    f = (float)__longlong_as_double((long long)u);
-  } else {
-    int e;
-    (void)frexp(v, &e);
-    const int q = e - 8 > -133 ? e - 8 : -133;
-    f = (float)ldexp(rint(ldexp(v, -q)), q);
-  }
-  return __float_as_uint(f) >> 16;
+  *ok = ex >= 1023 - 126 && ex <= 1023 + 127;
+  const uint64_t low = (1ull << 45) - 1;
+  u += (low >> 1) + ((u >> 45) & 1);
+  u &= ~low;
+  return __float_as_uint((float)__longlong_as_double((long long)u)) >> 16;
+}
+
+// The same rounding for any float64: v is rounded at the spacing 2^(e-8) of its binade
+// (v = m 2^e, 1/2 <= |m| < 1), never below the smallest bf16 subnormal 2^-133.
+__device__ __forceinline__ uint32_t f64_to_bf16_any(double v) {
+  int e;
+  (void)frexp(v, &e);
+  const int q = e - 8 > -133 ? e - 8 : -133;
+  return __float_as_uint((float)ldexp(rint(ldexp(v, -q)), q)) >> 16;
 }
 
 // dA, dC of phi = SiLU(a) * c for the upstream dphi, in float64, in this operation order:
@@ -77,12 +77,21 @@ __global__ __launch_bounds__(kBlock) void swiglu_bwd(const int32_t* __restrict__
   constexpr int CW = kBF16 ? 8 : 4;  // columns per chunk
   const int K = clamp_k(cmp_off, E_loc, K_cap);
   const int nch = d / CW;
-  const int64_t total = (int64_t)K * nch;
+  // chunk f = i * nch + jc; the grid-stride step advances (i, jc) by (stride / nch, stride % nch)
+  const int64_t f0 = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * kBlock;
+  const int64_t di = stride / nch;
+  const int dj = (int)(stride - di * nch);
+  int64_t i = f0 / nch;
+  int jc = (int)(f0 - i * nch);
   int bad = 0;
-  for (int64_t f = (int64_t)blockIdx.x * kBlock + threadIdx.x; f < total; f += stride) {
-    const int64_t i = f / nch;
-    const int j = (int)(f - i * nch) * CW;
+  for (; i < K; i += di, jc += dj) {
+    if (jc >= nch) {
+      jc -= nch;
+      ++i;
+      if (i >= K) break;
+    }
+    const int j = jc * CW;
     const int r = sel_row[i];
     const bool ok = r >= 0 && r < L_cap;
     if (!ok) bad = LRM_DEVERR_INDEX;
@@ -99,14 +108,29 @@ __global__ __launch_bounds__(kBlock) void swiglu_bwd(const int32_t* __restrict__
       const uint4 av = ok ? *(const uint4*)(row + j) : make_uint4(0, 0, 0, 0);
       const uint4 cv = ok ? *(const uint4*)(row + d + j) : make_uint4(0, 0, 0, 0);
       const uint32_t aw[4] = {av.x, av.y, av.z, av.w}, cw[4] = {cv.x, cv.y, cv.z, cv.w};
-      uint32_t oa[4], oc[4];
+      double dA[8], dC[8];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        double dA0, dC0, dA1, dC1;
-        swiglu_grad(gv[2 * q], bf16_lo(aw[q]), bf16_lo(cw[q]), dA0, dC0);
-        swiglu_grad(gv[2 * q + 1], bf16_hi(aw[q]), bf16_hi(cw[q]), dA1, dC1);
-        oa[q] = f64_to_bf16(dA0) | (f64_to_bf16(dA1) << 16);
-        oc[q] = f64_to_bf16(dC0) | (f64_to_bf16(dC1) << 16);
+        swiglu_grad(gv[2 * q], bf16_lo(aw[q]), bf16_lo(cw[q]), dA[2 * q], dC[2 * q]);
+        swiglu_grad(gv[2 * q + 1], bf16_hi(aw[q]), bf16_hi(cw[q]), dA[2 * q + 1], dC[2 * q + 1]);
+      }
+      // round in the normal range; only a chunk holding a value outside it (zero, tiny, huge)
+      // takes the general rounding, so the common case skips it
+      uint32_t oa[4], oc[4];
+      bool all_ok = true;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bool k0, k1, k2, k3;
+        oa[q] = f64_to_bf16_normal(dA[2 * q], &k0) | (f64_to_bf16_normal(dA[2 * q + 1], &k1) << 16);
+        oc[q] = f64_to_bf16_normal(dC[2 * q], &k2) | (f64_to_bf16_normal(dC[2 * q + 1], &k3) << 16);
+        all_ok = all_ok && k0 && k1 && k2 && k3;
+      }
+      if (!all_ok) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          oa[q] = f64_to_bf16_any(dA[2 * q]) | (f64_to_bf16_any(dA[2 * q + 1]) << 16);
+          oc[q] = f64_to_bf16_any(dC[2 * q]) | (f64_to_bf16_any(dC[2 * q + 1]) << 16);
+        }
       }
       uint16_t* out = (uint16_t*)dH + i * 2 * d;
       if (!ok) {
