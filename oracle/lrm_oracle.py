@@ -231,6 +231,42 @@ def plan_quotas(n_loc: np.ndarray, policy: dict):
     return np.asarray(q, np.int64), np.asarray(off, np.int64)
 
 
+def admission_feasible(K: int, budget: dict, K_cap=None) -> bool:
+    """Whether a retained total K fits one GPU's resources: its row capacity K_cap, the HBM budget
+    (mem_base bytes needed whatever the retention -- the complete forward workload and its saved
+    state -- plus mem_per_row bytes per retained row) and the bytes the backward dispatch may move
+    inside the overlap window (comm_budget = B_eff * T_ovlp, comm_per_row bytes per retained row;
+    comm_budget < 0: no limit)."""
+    if K_cap is not None and K > K_cap:
+        return False
+    if budget["mem_base"] + K * budget["mem_per_row"] > budget["mem_budget"]:
+        return False
+    if budget["comm_budget"] >= 0 and K * budget["comm_per_row"] > budget["comm_budget"]:
+        return False
+    return True
+
+
+def admit_quotas(n_loc: np.ndarray, candidates, budget: dict, K_cap=None):
+    """Forward-time admission on one GPU: the candidate retention rates are tested in the given
+    order (decreasing, starting with full retention), each candidate's quotas come from
+    plan_quotas, and the first candidate whose retained total K = sum of its quotas is feasible
+    fixes the quotas; if none is, admission fails ([LRMoE] Algorithm 1, steps 2-11; Sec. 3.3:
+    candidates are tested in decreasing order starting with full retention, the first feasible one
+    fixes the quotas, and admission fails when none is feasible).
+
+    Returns (index of the admitted candidate or -1, quotas, offsets); a failed admission keeps no
+    row (all quotas zero).  The replica placement the pages plan jointly needs several GPUs and is
+    not part of one GPU's admission.
+    """
+    n_loc = np.asarray(n_loc)
+    for c, pol in enumerate(candidates):
+        q, off = plan_quotas(n_loc, pol)
+        if admission_feasible(int(off[-1]), budget, K_cap):
+            return c, q, off
+    E_loc = n_loc.size
+    return -1, np.zeros(E_loc, np.int64), np.zeros(E_loc + 1, np.int64)
+
+
 # ------------------------------------------------------------------------------------------------
 # a3: Load Recalibration Metric
 # ------------------------------------------------------------------------------------------------

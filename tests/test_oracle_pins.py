@@ -553,3 +553,59 @@ def test_run_end_to_end_small():
     retained = out["cmp_off"][1:] - out["cmp_off"][:-1]
     n_loc = out["fwd_off"][1:] - out["fwd_off"][:-1]
     assert np.array_equal(retained, np.minimum(out["quota"], n_loc))
+
+
+# ------------------------------------------------------------------------------------------------
+# forward-time admission (candidate descent against one GPU's budgets)
+# ------------------------------------------------------------------------------------------------
+
+def _budget(mem_budget, mem_base=0, mem_per_row=1, comm_budget=-1, comm_per_row=0):
+    return dict(mem_budget=mem_budget, mem_base=mem_base, mem_per_row=mem_per_row,
+                comm_budget=comm_budget, comm_per_row=comm_per_row)
+
+
+def test_admission_worked_example():
+    # The page-2 worked example: full retention carries all 131072 routed rows, the capacity rule
+    # with CF = 5/4 carries 118032.  A budget between the two admits the capacity candidate.
+    gx = _gold("expert_parallel_math_worked_example.json")
+    n = np.asarray(gx["n"])
+    full = {"full": 1, "rho_num": 1, "rho_den": 1, "cap_abs": -1}
+    cf = {"full": 0, "rho_num": gx["capacity_factor_num"], "rho_den": gx["capacity_factor_den"],
+          "cap_abs": -1}
+    row = 2 * 4096                                   # bytes per retained row
+    for mem, want in ((int(n.sum()) * row, 0), (gx["real_carried"] * row, 1),
+                      (gx["real_carried"] * row - 1, -1)):
+        c, q, off = O.admit_quotas(n, [full, cf], _budget(mem, mem_per_row=row))
+        assert c == want
+        if c == 1:
+            assert int(off[-1]) == gx["real_carried"] and int(q.max()) == gx["C"]
+        if c == -1:
+            assert not q.any() and not off.any()
+
+
+def test_admission_is_first_feasible_and_largest_rate():
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        E_loc = int(rng.integers(1, 9))
+        n = rng.integers(0, 60, E_loc)
+        kind = ["cap", "proportional", "waterfill"][trial % 3]
+        cap = -1 if kind == "proportional" else int(rng.integers(-1, 40))
+        rates = [(1, 1), (7, 8), (3, 4), (1, 2), (1, 4), (1, 8), (0, 1)]
+        cands = [{"full": 1, "rho_num": 1, "rho_den": 1, "cap_abs": cap, "kind": kind}] + \
+                [{"full": 0, "rho_num": a, "rho_den": b, "cap_abs": cap, "kind": kind}
+                 for a, b in rates]
+        Ks = [int(O.plan_quotas(n, p)[1][-1]) for p in cands]
+        # the retained total never grows as the rate decreases (so the first feasible candidate
+        # in decreasing order is the largest feasible rate)
+        assert all(Ks[i] >= Ks[i + 1] for i in range(len(Ks) - 1)), (kind, n, cap, Ks)
+        b = _budget(int(rng.integers(0, 400)), mem_base=int(rng.integers(0, 50)),
+                    mem_per_row=int(rng.integers(1, 4)), comm_budget=int(rng.integers(-1, 200)),
+                    comm_per_row=int(rng.integers(0, 3)))
+        K_cap = int(rng.integers(1, 400))
+        c, q, off = O.admit_quotas(n, cands, b, K_cap)
+        ok = [K <= K_cap and b["mem_base"] + K * b["mem_per_row"] <= b["mem_budget"] and
+              (b["comm_budget"] < 0 or K * b["comm_per_row"] <= b["comm_budget"]) for K in Ks]
+        want = ok.index(True) if any(ok) else -1
+        assert c == want
+        if c >= 0:
+            assert int(off[-1]) == Ks[c] and np.all(q <= n)
