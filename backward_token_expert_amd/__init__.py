@@ -6,7 +6,8 @@ Load Re-Calibration for Efficient MoE Training on Memory-Constrained Nodes" as h
 kernels.  This package only marshals arguments (lrm.py) and sequences the six calls (path.py).
 """
 from . import lrm, path  # noqa: F401
-from .lrm import (LRM_BF16, LRM_F32, LrmError, Problem, QuotaPolicy, load_library,  # noqa: F401
+from .lrm import (LRM_BF16, LRM_F32, Admission, LrmError, Problem, QuotaPolicy,  # noqa: F401
+                  load_library, lrm_admit_quotas, make_admission,
                   lrm_compact, lrm_gather_tokens, lrm_grouped_dw, lrm_grouped_dw_dx,
                   lrm_grouped_dx, lrm_grouped_fc1_dw, lrm_grouped_fc1_dw_dx, lrm_grouped_fc1_dx,
                   lrm_plan_quotas, lrm_scatter_tokens, lrm_swiglu_backward,

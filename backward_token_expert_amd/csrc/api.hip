@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/lrm.h: argument validation, workspace layout and
 // kernel launches.  No allocation, no synchronisation (except lrm_read_device_error).
+#include <stddef.h>
 #include <stdint.h>
 
 #include "lrm_internal.hpp"
@@ -9,6 +10,9 @@ using lrm::WsLayout;
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static_assert(sizeof(lrm_admission) == 248 && offsetof(lrm_admission, mem_budget) == 208,
+              "lrm_admission layout is part of the ABI");
 
 lrm_status check_problem(const lrm_problem* p) {
   if (!p) return LRM_ERR_INVALID_ARGUMENT;
@@ -76,6 +80,26 @@ lrm_status lrm_plan_quotas(const lrm_problem* problem, const lrm_quota_policy* p
   LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
   return from_hip(lrm::launch_plan(*problem, *policy, topk_idx, counts, fwd_off, row_pair, quota,
                                    cmp_off, (char*)ws, wl, stream));
+}
+
+lrm_status lrm_admit_quotas(const lrm_problem* problem, const lrm_admission* admission,
+                            const int32_t* fwd_off, int32_t* quota, int32_t* cmp_off,
+                            int32_t* admitted, void* ws, size_t ws_bytes, hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  const lrm_admission* a = admission;
+  if (!a || !fwd_off || !quota || !cmp_off || !admitted) return LRM_ERR_INVALID_ARGUMENT;
+  if (a->n_cand < 1 || a->n_cand > LRM_MAX_CANDIDATES) return LRM_ERR_INVALID_ARGUMENT;
+  if (a->kind < LRM_QUOTA_CAP || a->kind > LRM_QUOTA_WATERFILL) return LRM_ERR_INVALID_ARGUMENT;
+  if (a->kind == LRM_QUOTA_PROPORTIONAL && a->cap_abs >= 0) return LRM_ERR_INVALID_ARGUMENT;
+  for (int c = 0; c < a->n_cand; ++c)
+    if (!a->full[c] && (a->rho_den[c] <= 0 || a->rho_num[c] < 0)) return LRM_ERR_INVALID_ARGUMENT;
+  const int64_t lim = (int64_t)1 << 32;
+  if (a->mem_base < 0 || a->mem_per_row < 0 || a->mem_per_row > lim || a->comm_per_row < 0 ||
+      a->comm_per_row > lim || a->mem_base > ((int64_t)1 << 62))
+    return LRM_ERR_INVALID_ARGUMENT;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_admit(*problem, *a, fwd_off, quota, cmp_off, admitted, stream));
 }
 
 lrm_status lrm_score(const lrm_problem* problem, const float* topk_w, const void* g,

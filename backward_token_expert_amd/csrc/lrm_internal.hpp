@@ -87,6 +87,8 @@ hipError_t launch_select(const lrm_problem& p, const float* score, const int32_t
 hipError_t launch_gemms(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
                         const int32_t* cmp_off, float* dW, float* dphi, char* ws,
                         const WsLayout& wl, hipStream_t s);
+hipError_t launch_admit(const lrm_problem& p, const lrm_admission& adm, const int32_t* fwd_off,
+                        int32_t* quota, int32_t* cmp_off, int32_t* admitted, hipStream_t s);
 hipError_t launch_swiglu_bwd(const lrm_problem& p, const int32_t* sel_row, const int32_t* cmp_off,
                              const float* dphi, const void* ac, void* dH, char* ws,
                              const WsLayout& wl, hipStream_t s);

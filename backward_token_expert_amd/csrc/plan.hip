@@ -138,6 +138,26 @@ __device__ int waterfill_quota(int n, int cap, int B, int E_loc, int* mv, int* s
 
 constexpr int kScanBatch = 8;
 
+// Quota of thread tid's expert (tid < E_loc; 0 for the other threads) under `pol`, the expert
+// holding seg of the Lc local rows.  Every thread of the workgroup must call it (the proportional
+// and water-fill splits hold barriers); `pol` is the same for all of them.
+__device__ int policy_quota(const lrm_quota_policy& pol, int seg, int Lc, int E_loc, int* rem,
+                            int* sh) {
+  const int tid = threadIdx.x;
+  if (pol.full) return tid < E_loc ? seg : 0;
+  if (pol.kind == LRM_QUOTA_CAP) {
+    if (tid >= E_loc) return 0;
+    const int64_t c = ((int64_t)pol.rho_num * Lc) / ((int64_t)pol.rho_den * E_loc);
+    int64_t qq = seg < c ? seg : c;
+    if (pol.cap_abs >= 0 && qq > pol.cap_abs) qq = pol.cap_abs;
+    return (int)qq;
+  }
+  const int64_t bb = ((int64_t)pol.rho_num * Lc) / pol.rho_den;
+  const int B = (int)(bb < Lc ? bb : Lc);
+  return pol.kind == LRM_QUOTA_PROPORTIONAL ? proportional_quota(seg, Lc, B, E_loc, rem, sh)
+                                            : waterfill_quota(seg, pol.cap_abs, B, E_loc, rem, sh);
+}
+
 __global__ __launch_bounds__(1024) void plan_scan(int32_t* __restrict__ hist, int64_t nchunks,
                                                   int E, int e_lo, int E_loc, int L_cap, int K_cap,
                                                   lrm_quota_policy pol, int32_t* __restrict__ counts,
@@ -214,22 +234,7 @@ __global__ __launch_bounds__(1024) void plan_scan(int32_t* __restrict__ hist, in
   const int Lc = L < L_cap ? L : L_cap;
   if (tid < E_loc) fwd_off[tid] = f0;
   if (tid == 0) fwd_off[E_loc] = Lc;
-  int q = 0;
-  if (pol.full) {
-    q = tid < E_loc ? seg : 0;
-  } else if (pol.kind == LRM_QUOTA_CAP) {
-    if (tid < E_loc) {
-      const int64_t c = ((int64_t)pol.rho_num * Lc) / ((int64_t)pol.rho_den * E_loc);
-      int64_t qq = seg < c ? seg : c;
-      if (pol.cap_abs >= 0 && qq > pol.cap_abs) qq = pol.cap_abs;
-      q = (int)qq;
-    }
-  } else {
-    const int64_t bb = ((int64_t)pol.rho_num * Lc) / pol.rho_den;
-    const int B = (int)(bb < Lc ? bb : Lc);
-    q = pol.kind == LRM_QUOTA_PROPORTIONAL ? proportional_quota(seg, Lc, B, E_loc, rem, sh)
-                                           : waterfill_quota(seg, pol.cap_abs, B, E_loc, rem, sh);
-  }
+  const int q = policy_quota(pol, seg, Lc, E_loc, rem, sh);
   int K = 0;
   const int cpre = block_exclusive_scan_1024(q, sh, &K);
   const int o0 = cpre < K_cap ? cpre : K_cap;
@@ -296,7 +301,57 @@ __global__ __launch_bounds__(kPlanBlock) void plan_scatter(const int32_t* __rest
   }
 }
 
+// Forward-time admission (one workgroup): the candidates are tested in order; each one's quotas
+// come from policy_quota on the local counts fwd_off[i+1] - fwd_off[i], and the first whose total
+// K fits (K <= K_cap, mem_base + K * mem_per_row <= mem_budget, and K * comm_per_row <=
+// comm_budget unless that is negative) fixes quota, cmp_off and *admitted = its index.  If none
+// fits, every quota is zero and *admitted = -1.
+__global__ __launch_bounds__(1024) void admit_scan(const int32_t* __restrict__ fwd_off, int E_loc,
+                                                   int K_cap, lrm_admission adm,
+                                                   int32_t* __restrict__ quota,
+                                                   int32_t* __restrict__ cmp_off,
+                                                   int32_t* __restrict__ admitted) {
+  __shared__ int rem[1024];
+  __shared__ int sh[32];
+  const int tid = threadIdx.x;
+  int seg = 0;
+  if (tid < E_loc) {
+    seg = fwd_off[tid + 1] - fwd_off[tid];
+    seg = seg < 0 ? 0 : seg;
+  }
+  int Lc = 0;
+  (void)block_exclusive_scan_1024(seg, sh, &Lc);
+  int chosen = -1, q = 0;
+  for (int c = 0; c < adm.n_cand && chosen < 0; ++c) {
+    const lrm_quota_policy pol{adm.full[c], adm.rho_num[c], adm.rho_den[c], adm.cap_abs, adm.kind};
+    q = policy_quota(pol, seg, Lc, E_loc, rem, sh);
+    int K = 0;
+    (void)block_exclusive_scan_1024(q, sh, &K);
+    const bool fits = K <= K_cap && adm.mem_base + (int64_t)K * adm.mem_per_row <= adm.mem_budget &&
+                      (adm.comm_budget < 0 || (int64_t)K * adm.comm_per_row <= adm.comm_budget);
+    if (fits) chosen = c;            // K is the same in every thread, so is the decision
+  }
+  if (chosen < 0) q = 0;
+  int K = 0;
+  const int cpre = block_exclusive_scan_1024(q, sh, &K);
+  if (tid < E_loc) {
+    cmp_off[tid] = cpre;
+    quota[tid] = q;
+  }
+  if (tid == 0) {
+    cmp_off[E_loc] = K;
+    *admitted = chosen;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_admit(const lrm_problem& p, const lrm_admission& adm, const int32_t* fwd_off,
+                        int32_t* quota, int32_t* cmp_off, int32_t* admitted, hipStream_t s) {
+  hipLaunchKernelGGL(admit_scan, dim3(1), dim3(1024), 0, s, fwd_off, p.E_loc, p.K_cap, adm, quota,
+                     cmp_off, admitted);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan(const lrm_problem& p, const lrm_quota_policy& pol, const int32_t* topk_idx,
                        int32_t* counts, int32_t* fwd_off, int32_t* row_pair, int32_t* quota,

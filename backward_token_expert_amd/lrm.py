@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("LRM_LIBRARY") or os.path.join(_PKG, "liblrm.so")
 LRM_F32, LRM_BF16 = 0, 1
 DEVERR = {1: "EXPERT_ID", 2: "L_CAP", 4: "K_CAP", 8: "QUOTA", 16: "NONFINITE", 32: "INDEX"}
 
-EXPORTS = ("lrm_workspace_bytes", "lrm_plan_quotas", "lrm_score", "lrm_score_criterion",
+EXPORTS = ("lrm_workspace_bytes", "lrm_plan_quotas", "lrm_admit_quotas", "lrm_score", "lrm_score_criterion",
            "lrm_select", "lrm_compact", "lrm_grouped_dw", "lrm_grouped_dx", "lrm_grouped_dw_dx",
            "lrm_swiglu_backward", "lrm_gather_tokens", "lrm_grouped_fc1_dw", "lrm_grouped_fc1_dx",
            "lrm_grouped_fc1_dw_dx", "lrm_scatter_tokens", "lrm_read_device_error",
@@ -35,6 +35,33 @@ class Problem(ctypes.Structure):
 
 class QuotaPolicy(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("full", "rho_num", "rho_den", "cap_abs", "kind")]
+
+
+MAX_CANDIDATES = 16
+
+
+class Admission(ctypes.Structure):
+    _fields_ = [("n_cand", ctypes.c_int32), ("kind", ctypes.c_int32), ("cap_abs", ctypes.c_int32),
+                ("full", ctypes.c_int32 * MAX_CANDIDATES),
+                ("rho_num", ctypes.c_int32 * MAX_CANDIDATES),
+                ("rho_den", ctypes.c_int32 * MAX_CANDIDATES),
+                ("mem_budget", ctypes.c_int64), ("mem_base", ctypes.c_int64),
+                ("mem_per_row", ctypes.c_int64), ("comm_budget", ctypes.c_int64),
+                ("comm_per_row", ctypes.c_int64)]
+
+
+def make_admission(candidates, mem_budget, mem_base=0, mem_per_row=0, comm_budget=-1,
+                   comm_per_row=0, kind="cap", cap_abs=-1) -> Admission:
+    """candidates: list of (full, rho_num, rho_den), tested in that order."""
+    a = Admission()
+    a.n_cand = len(candidates)
+    a.kind = QUOTA_KINDS[kind] if isinstance(kind, str) else int(kind)
+    a.cap_abs = cap_abs
+    for i, (f, n, d) in enumerate(candidates):
+        a.full[i], a.rho_num[i], a.rho_den[i] = int(f), int(n), int(d)
+    a.mem_budget, a.mem_base, a.mem_per_row = mem_budget, mem_base, mem_per_row
+    a.comm_budget, a.comm_per_row = comm_budget, comm_per_row
+    return a
 
 
 class LrmError(RuntimeError):
@@ -59,6 +86,7 @@ def load_library(path: Optional[str] = None):
     lib.lrm_workspace_bytes.argtypes = [PP]
     lib.lrm_workspace_bytes.restype = sz
     lib.lrm_plan_quotas.argtypes = [PP, QP] + [vp] * 7 + [sz, vp]
+    lib.lrm_admit_quotas.argtypes = [PP, ctypes.POINTER(Admission)] + [vp] * 5 + [sz, vp]
     lib.lrm_score.argtypes = [PP] + [vp] * 7 + [sz, vp]
     lib.lrm_score_criterion.argtypes = [PP, i32] + [vp] * 8 + [sz, vp]
     lib.lrm_select.argtypes = [PP] + [vp] * 6 + [sz, vp]
@@ -180,6 +208,15 @@ def lrm_grouped_dw_dx(problem, Gc, Phic, W, cmp_off, dW, dphi, ws, stream=None):
                                       _ptr(cmp_off), _ptr(dW), _ptr(dphi), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream)),
            "lrm_grouped_dw_dx")
+
+
+def lrm_admit_quotas(problem, admission, fwd_off, quota, cmp_off, admitted, ws, stream=None):
+    lib = load_library()
+    _check(lib, lib.lrm_admit_quotas(ctypes.byref(problem), ctypes.byref(admission), _ptr(fwd_off),
+                                     _ptr(quota), _ptr(cmp_off), _ptr(admitted),
+                                     _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)),
+           "lrm_admit_quotas")
 
 
 def _ws(ws):

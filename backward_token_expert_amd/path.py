@@ -44,6 +44,7 @@ class DeviceBuffers:
         self.row_pair = torch.zeros(p.L_cap, **i32)
         self.quota = torch.zeros(p.E_loc, **i32)
         self.cmp_off = torch.zeros(p.E_loc + 1, **i32)
+        self.admitted = torch.full((1,), -2, **i32)
         self.score = torch.zeros(p.L_cap, dtype=torch.float32, device=device)
         self.sel_row = torch.zeros(p.K_cap, **i32)
         self.sel_pair = torch.zeros(p.K_cap, **i32)
@@ -58,14 +59,19 @@ class DeviceBuffers:
 
 
 def run(problem, policy, topk_idx, topk_w, g, phi, W, bufs: DeviceBuffers, stream=None,
-        criterion: str = "lrm", keys=None, fused: bool = True):
+        criterion: str = "lrm", keys=None, fused: bool = True, admission=None):
     """Enqueue the whole hot path on `stream` (default: torch's current stream).  `criterion`
     picks the selection score (lrm_score for "lrm", else lrm_score_criterion; "random" ranks by
     `keys`, one float32 per pair).  `fused` runs both GEMMs as lrm_grouped_dw_dx, else as
-    lrm_grouped_dw then lrm_grouped_dx."""
+    lrm_grouped_dw then lrm_grouped_dx.  With an `admission` (lrm.make_admission), the quotas are
+    those of the first feasible candidate (lrm_admit_quotas after lrm_plan_quotas) and
+    bufs.admitted receives its index (-1: none, every quota zero)."""
     b = bufs
     lrm.lrm_plan_quotas(problem, policy, topk_idx, b.counts, b.fwd_off, b.row_pair, b.quota,
                         b.cmp_off, b.ws, stream)
+    if admission is not None:
+        lrm.lrm_admit_quotas(problem, admission, b.fwd_off, b.quota, b.cmp_off, b.admitted, b.ws,
+                             stream)
     if criterion == "lrm":
         lrm.lrm_score(problem, topk_w, g, phi, b.row_pair, b.fwd_off, b.score, b.ws, stream)
     else:

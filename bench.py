@@ -251,6 +251,42 @@ def layer_bench(w, pol_dict, steps, warmup, criterion="lrm"):
             "fc1_mfma_frac": a["flops_fc1"] / t_g / 1e12 / MFMA_PEAK_TFLOPS[sp.dtype]}
 
 
+def admission_bench(w, steps):
+    """Time lrm_admit_quotas: six candidates (full retention, then rho = 1, 3/4, 1/2, 1/4, 1/8 of
+    the cap form) against an HBM budget sized, from the GPU's own quotas under the workload's
+    policy, to admit exactly the workload's rho."""
+    import torch
+    from backward_token_expert_amd import lrm, path
+    from backward_token_expert_amd.path import to_device, to_host
+    sp = w.spec
+    L_cap = sp.T * min(sp.k, sp.E_loc)
+    P = lrm.make_problem(sp.T, sp.k, sp.E, sp.e_lo, sp.E_loc, sp.h, sp.d, sp.dtype, L_cap, L_cap)
+    b = path.DeviceBuffers(P)
+    s = torch.cuda.current_stream()
+    idx = to_device(w.topk_idx)
+    own = lrm.make_policy(0, sp.rho_num, sp.rho_den, sp.cap_abs)
+    lrm.lrm_plan_quotas(P, own, idx, b.counts, b.fwd_off, b.row_pair, b.quota, b.cmp_off, b.ws, s)
+    torch.cuda.synchronize()
+    K_own = int(to_host(b.cmp_off)[-1])
+    rates = [(1, 1, 1), (0, 1, 1), (0, 3, 4), (0, 1, 2), (0, 1, 4), (0, 1, 8)]
+    el = 2 if sp.dtype == "bf16" else 4
+    row = (sp.h + sp.d) * el + 4 * sp.d + 8          # Gc, Phic, dphi, row ids per retained row
+    adm = lrm.make_admission(rates, mem_budget=(1 << 30) + K_own * row, mem_base=1 << 30,
+                             mem_per_row=row, cap_abs=sp.cap_abs)
+    for _ in range(3):
+        lrm.lrm_admit_quotas(P, adm, b.fwd_off, b.quota, b.cmp_off, b.admitted, b.ws, s)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(steps):
+        lrm.lrm_admit_quotas(P, adm, b.fwd_off, b.quota, b.cmp_off, b.admitted, b.ws, s)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return {"call": "lrm_admit_quotas", "candidates": len(rates),
+            "admitted": int(to_host(b.admitted)[0]), "K_retained": int(to_host(b.cmp_off)[-1]),
+            "K_budgeted": K_own, "us_per_call": e0.elapsed_time(e1) / steps * 1e3}
+
+
 def synth_keys(sp):
     import synth
     return synth.pair_keys(sp)
@@ -392,6 +428,7 @@ def main():
     nl = max(3, args.steps // 2) if args.layer_steps is None else args.layer_steps
     if nl > 0:
         out["layer_backward"] = layer_bench(w, pol, nl, 2, crit)
+    out["admission"] = admission_bench(w, 20)
     if args.copy_calibration_mib > 0:
         import torch
         n = args.copy_calibration_mib << 20

@@ -5,6 +5,8 @@
  * steps of "LRMoE: Demand-Side Load Re-Calibration for Efficient MoE Training on
  * Memory-Constrained Nodes" (Hu et al., arXiv 2610.37720):
  *   lrm_plan_quotas  routed counts n_e, forward layout, quotas q_e, compacted offsets
+ *   lrm_admit_quotas forward-time admission: the largest candidate retention rate whose retained
+ *                    total fits this GPU's budgets fixes the quotas (Algorithm 1 steps 2-11)
  *                    (Algorithm 1 step 1; Sec. 3.1 and 3.3 quotas 0 <= K_e <= N_e; the capacity
  *                    form of "Expert Parallel Math Deep", "Capacity and the exact drop-rate
  *                    formula")
@@ -142,6 +144,37 @@ typedef struct {
   int32_t kind;   /* LRM_QUOTA_* */
 } lrm_quota_policy;
 
+/*
+ * Forward-time admission on one GPU (LRMoE Algorithm 1 steps 2-11; Sec. 3.3: candidate retained
+ * counts are tested in decreasing order starting with full retention, against the memory budget
+ * and the communication window; the first feasible one fixes the quotas; if none is feasible,
+ * admission fails).  Candidate c is the quota policy {full[c], rho_num[c], rho_den[c], cap_abs,
+ * kind} of lrm_quota_policy; its retained total K_c = sum of its quotas is feasible when
+ *   K_c <= K_cap,   mem_base + K_c * mem_per_row <= mem_budget,
+ *   and (comm_budget < 0 or K_c * comm_per_row <= comm_budget)
+ * where mem_base counts the bytes needed whatever the retention (the complete forward workload
+ * and its saved state: feasibility covers those, not only the reduced backward), mem_per_row the
+ * bytes of one retained row's compacted buffers and gradients, comm_per_row the bytes one
+ * retained row sends in the backward dispatch, and comm_budget = B_eff * T_ovlp the bytes that fit
+ * the overlap window.  Replica placement, planned jointly on the pages, needs several GPUs and is
+ * not part of this call.
+ */
+#define LRM_MAX_CANDIDATES 16
+
+typedef struct {
+  int32_t n_cand;                          /* 1 .. LRM_MAX_CANDIDATES, tested in this order      */
+  int32_t kind;                            /* LRM_QUOTA_* of every candidate                      */
+  int32_t cap_abs;                         /* absolute per-expert cap (< 0: none)                 */
+  int32_t full[LRM_MAX_CANDIDATES];        /* candidate c keeps every routed row                  */
+  int32_t rho_num[LRM_MAX_CANDIDATES];     /* else its retention fraction rho_num / rho_den       */
+  int32_t rho_den[LRM_MAX_CANDIDATES];
+  int64_t mem_budget;                      /* bytes                                               */
+  int64_t mem_base;                        /* bytes, >= 0                                         */
+  int64_t mem_per_row;                     /* bytes, 0 .. 2^32                                    */
+  int64_t comm_budget;                     /* bytes; < 0: no communication limit                  */
+  int64_t comm_per_row;                    /* bytes, 0 .. 2^32                                    */
+} lrm_admission;
+
 /* Bytes of device scratch every call needs for this problem, the FC1 calls included (0 if the
  * problem is invalid). */
 size_t lrm_workspace_bytes(const lrm_problem* problem);
@@ -160,6 +193,23 @@ lrm_status lrm_plan_quotas(const lrm_problem* problem, const lrm_quota_policy* p
                            const int32_t* topk_idx, int32_t* counts, int32_t* fwd_off,
                            int32_t* row_pair, int32_t* quota, int32_t* cmp_off, void* ws,
                            size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Admission (see lrm_admission): from the local counts in fwd_off (as lrm_plan_quotas writes it),
+ * writes the quotas and compacted offsets of the first feasible candidate and its index to
+ * *admitted (device int32); if none is feasible, every quota is zero, cmp_off is all zeros and
+ * *admitted = -1 -- the later calls then keep no row.  Overwrites what lrm_plan_quotas wrote to
+ * quota and cmp_off; computed on the device in one launch, so the outcome needs no host
+ * round trip.
+ *  in : fwd_off int32 [E_loc+1]
+ *  out: quota int32 [E_loc]; cmp_off int32 [E_loc+1]; admitted int32 [1]
+ * Invalid candidates (rho_den <= 0 or rho_num < 0 without full, a cap with the proportional
+ * kind, n_cand outside [1, LRM_MAX_CANDIDATES], negative or oversized byte figures) return
+ * LRM_ERR_INVALID_ARGUMENT.
+ */
+lrm_status lrm_admit_quotas(const lrm_problem* problem, const lrm_admission* admission,
+                            const int32_t* fwd_off, int32_t* quota, int32_t* cmp_off,
+                            int32_t* admitted, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * LRM score of every local forward row (LRMoE Sec. 3.2, Prop. 3.1, Eq. (3)):

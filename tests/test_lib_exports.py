@@ -100,3 +100,27 @@ def test_layer_calls_validate_on_host():
     assert lib.lrm_grouped_fc1_dw_dx(P, fake, fake, fake, fake, fake, fake, fake, fc2_only,
                                      None) == 3
     assert lib.lrm_grouped_fc1_dw_dx(P, fake, fake, fake, None, fake, fake, fake, n, None) == 1
+
+
+def test_admission_struct_and_validation_on_host():
+    lib = bte.load_library()
+    assert ctypes.sizeof(lrm.Admission) == 248 and lrm.Admission.mem_budget.offset == 208
+    p = bte.make_problem(32768, 8, 128, 0, 16, 2048, 768, "bf16", 262144, 262144)
+    n = bte.lrm_workspace_bytes(p)
+    P = ctypes.byref(p)
+    fake = 0x100000  # never dereferenced: each call below is rejected before any launch
+
+    def call(a, ws_bytes=n):
+        return lib.lrm_admit_quotas(P, ctypes.byref(a), fake, fake, fake, fake, fake, ws_bytes,
+                                    None)
+    ok = [(1, 1, 1), (0, 1, 2)]
+    assert call(bte.make_admission([], 1 << 40)) == 1                                # no candidate
+    many = bte.make_admission([(0, 1, 1)] * 16, 1 << 40)
+    many.n_cand = 17                                                                  # too many
+    assert call(many) == 1
+    assert call(bte.make_admission([(0, 1, 0)], 1 << 40)) == 1                       # rho_den = 0
+    assert call(bte.make_admission(ok, 1 << 40, kind="proportional", cap_abs=5)) == 1
+    assert call(bte.make_admission(ok, 1 << 40, mem_per_row=-1)) == 1
+    assert call(bte.make_admission(ok, 1 << 40, comm_per_row=(1 << 32) + 1)) == 1
+    assert call(bte.make_admission(ok, 1 << 40), ws_bytes=1024) == 3
+    assert lib.lrm_admit_quotas(P, None, fake, fake, fake, fake, fake, n, None) == 1
