@@ -621,9 +621,9 @@ __global__ __launch_bounds__(CW::THREADS) void gemm_fused(
 // Every step is a closed form or a workgroup scan, so the schedule costs a few barriers.
 constexpr int kDwJobCost = 8;
 
-__global__ __launch_bounds__(1024) void dw_schedule(const int32_t* __restrict__ cmp_off, int E_loc,
-                                                    int K_cap, int groups, int gpx,
-                                                    int32_t* __restrict__ sched) {
+__device__ __forceinline__ void dw_schedule_body(const int32_t* __restrict__ cmp_off, int E_loc,
+                                                 int K_cap, int groups, int gpx,
+                                                 int32_t* __restrict__ sched) {
   constexpr int kG = kMaxXcd * kMaxGroupsPerXcd;
   __shared__ int rows[1024], by_rank[1024];
   __shared__ int load[kG], first[kG], count[kG];
@@ -906,10 +906,10 @@ __global__ __launch_bounds__(kF32Threads) void dx_f32(const float* __restrict__ 
 // dphi tile table: tiles[0] = number of row tiles, then (expert, first row) per tile, experts in
 // order, `tm` rows per tile (the last tile of a segment is partial; empty segments have none).
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void dx_schedule(const int32_t* __restrict__ cmp_off, int E_loc,
-                                                    int K_cap, int tm, int64_t max_tiles,
-                                                    int32_t* __restrict__ tiles,
-                                                    int32_t* __restrict__ queue) {
+__device__ __forceinline__ void dx_schedule_body(const int32_t* __restrict__ cmp_off, int E_loc,
+                                                 int K_cap, int tm, int64_t max_tiles,
+                                                 int32_t* __restrict__ tiles,
+                                                 int32_t* __restrict__ queue) {
   __shared__ int sh[32];
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
   if (queue && tid < kMaxXcd) queue[tid] = 0;  // unit counters of the fused launch
@@ -944,6 +944,34 @@ __global__ __launch_bounds__(1024) void dx_schedule(const int32_t* __restrict__ 
     __syncthreads();
   }
   if (tid == 0) tiles[0] = (int)(base_tiles < max_tiles ? base_tiles : max_tiles);
+}
+
+__global__ __launch_bounds__(1024) void dw_schedule(const int32_t* __restrict__ cmp_off, int E_loc,
+                                                    int K_cap, int groups, int gpx,
+                                                    int32_t* __restrict__ sched) {
+  dw_schedule_body(cmp_off, E_loc, K_cap, groups, gpx, sched);
+}
+
+__global__ __launch_bounds__(1024) void dx_schedule(const int32_t* __restrict__ cmp_off, int E_loc,
+                                                    int K_cap, int tm, int64_t max_tiles,
+                                                    int32_t* __restrict__ tiles,
+                                                    int32_t* __restrict__ queue) {
+  dx_schedule_body(cmp_off, E_loc, K_cap, tm, max_tiles, tiles, queue);
+}
+
+// Both schedules of the one-launch GEMMs in one launch of two workgroups: workgroup 0 builds the
+// dW job lists, workgroup 1 the dphi tile table (and resets the unit counters); they write
+// disjoint workspace regions.
+__global__ __launch_bounds__(1024) void gemm_schedules(const int32_t* __restrict__ cmp_off,
+                                                       int E_loc, int K_cap, int groups, int gpx,
+                                                       int32_t* __restrict__ sched, int tm,
+                                                       int64_t max_tiles,
+                                                       int32_t* __restrict__ tiles,
+                                                       int32_t* __restrict__ queue) {
+  if (blockIdx.x == 0)
+    dw_schedule_body(cmp_off, E_loc, K_cap, groups, gpx, sched);
+  else
+    dx_schedule_body(cmp_off, E_loc, K_cap, tm, max_tiles, tiles, queue);
 }
 
 
@@ -1019,10 +1047,9 @@ void launch_fused_t(const lrm_problem& p, const void* Gc, const void* Phic, cons
                     int64_t max_tiles, float* dW, float* slots, float* dphi, const Grid& g,
                     hipStream_t s) {
   const int gpx = groups_per_die<CW>(p, g);
-  hipLaunchKernelGGL(dw_schedule, dim3(1), dim3(kThreadsPerSchedule), 0, s, cmp_off, p.E_loc,
-                     p.K_cap, g.nxcd * gpx, gpx, sched);
-  hipLaunchKernelGGL(dx_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, CX::BM,
-                     max_tiles, tiles, queue);
+  static_assert(kThreadsPerSchedule == 1024, "one block shape for both schedules");
+  hipLaunchKernelGGL(gemm_schedules, dim3(2), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap,
+                     g.nxcd * gpx, gpx, sched, CX::BM, max_tiles, tiles, queue);
   hipLaunchKernelGGL((gemm_fused<CW, CX, stages_for<CW>()>), dim3(g.blocks), dim3(CW::THREADS), 0,
                      s, (const uint16_t*)Gc, (const uint16_t*)Phic, (const uint16_t*)W, cmp_off,
                      sched, tiles, queue, g.nxcd, p.E_loc, p.K_cap, p.h, p.d, dW, slots, dphi);

@@ -41,6 +41,8 @@ def parse():
                     help="selection score: the LRM, or one of the ablation criteria")
     ap.add_argument("--quota", default="cap", choices=["cap", "proportional", "waterfill"],
                     help="quota split of the retained total")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of replays of a captured HIP graph")
     ap.add_argument("--separate-gemms", action="store_true",
                     help="lrm_grouped_dw then lrm_grouped_dx instead of lrm_grouped_dw_dx")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -85,7 +87,7 @@ def algorithmic(w, oracle_like, criterion="lrm"):
     }
 
 
-def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True):
+def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True, graph=True):
     import torch
     from backward_token_expert_amd import lrm, path
     from backward_token_expert_amd.path import to_device, to_host
@@ -100,10 +102,10 @@ def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True):
     idx, tw, g, ph, W = (to_device(a) for a in (w.topk_idx, w.topk_w, w.g, phi, w.W))
     keys = to_device(synth_keys(sp)) if criterion == "random" else None
     b = path.DeviceBuffers(P)
-    s = torch.cuda.current_stream()
     stages = STAGES_FUSED if fused else STAGES_SPLIT
 
-    def step(ev=None):
+    def step(ev=None, s=None):
+        s = torch.cuda.current_stream() if s is None else s
         if ev is not None:
             ev[0].record(s)
         lrm.lrm_plan_quotas(P, pol, idx, b.counts, b.fwd_off, b.row_pair, b.quota, b.cmp_off, b.ws, s)
@@ -139,24 +141,49 @@ def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True):
     err = lrm.lrm_read_device_error(b.ws)
     if err:
         raise RuntimeError(f"device error word {err}: {lrm.deverr_names(err)}")
+    s = torch.cuda.current_stream()
 
-    # Timed region: exactly `steps` whole-path steps.  HIP events bracket every stage on the
-    # stream the kernels are launched on; they cost nothing measurable next to the stages.
+    # Stage times: eager steps with HIP events between the calls, on the stream the kernels are
+    # launched on (the events cost nothing measurable next to the stages).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
            for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    stage_ms = {st: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+                for j, st in enumerate(stages)}
+
+    # Whole-step time: the step captured once in a HIP graph and replayed (every call of the path
+    # is capturable: no allocation, no host synchronisation); --eager times eager launches.
+    run_step = step
+    if graph:
+        g_step = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(s)
+        with torch.cuda.stream(cs):
+            step(None, cs)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g_step, stream=cs):
+                step(None, cs)
+        torch.cuda.synchronize()
+        run_step = g_step.replay
+        for _ in range(warmup):
+            run_step()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     t_start.record(s)
     for i in range(steps):
-        step(evs[i])
+        run_step()
     t_end.record(s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = t_start.elapsed_time(t_end)
-    stage_ms = {st: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
-                for j, st in enumerate(stages)}
+    err = lrm.lrm_read_device_error(b.ws)
+    if err:
+        raise RuntimeError(f"device error word {err}: {lrm.deverr_names(err)}")
     fo = to_host(b.fwd_off)
     co = to_host(b.cmp_off)
     sel_pair = to_host(b.sel_pair)[:int(co[-1])]
@@ -368,14 +395,15 @@ def main():
     pol = synth.policy(sp, kind=args.quota, cap=-1 if args.quota == "proportional" else None)
     crit = args.criterion
     fused = not args.separate_gemms
-    ms, wall_ms, stages, info = gpu_bench(w, pol, args.steps, args.warmup, crit, fused)
+    ms, wall_ms, stages, info = gpu_bench(w, pol, args.steps, args.warmup, crit, fused,
+                                          not args.eager)
     alg = algorithmic(w, info, crit)
     L, K = info["L"], info["K"]
     # rho = 1 (full retention) on the same input
     n1 = max(3, args.steps // 2) if args.rho1_steps is None else args.rho1_steps
     if n1 > 0:
         pol_full = synth.policy(sp, full=True)
-        ms1, _, stages1, info1 = gpu_bench(w, pol_full, n1, 2, crit, fused)
+        ms1, _, stages1, info1 = gpu_bench(w, pol_full, n1, 2, crit, fused, not args.eager)
         alg1 = algorithmic(w, info1, crit)
 
     def fractions(st, a, dtype):
@@ -417,6 +445,7 @@ def main():
                      "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
                      "traffic": recorded_traffic(dom_call, sp.name)},
         "retained_rows_per_s": K / (ms * 1e-3),
+        "timing": "eager launches" if args.eager else "replays of one captured HIP graph",
         "wall_ms_per_step": wall_ms,
         "stages_ms": stages,
         "fractions": fractions(stages, alg, sp.dtype),
