@@ -190,7 +190,7 @@ lrm_status lrm_grouped_dw_dx(const lrm_problem* problem, const void* Gc, const v
   WsLayout wl;
   LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
   return from_hip(lrm::launch_gemms(*problem, Gc, Phic, W, cmp_off, dW, dphi, (char*)ws, wl,
-                                    stream));
+                                    stream, 2));
 }
 
 lrm_status lrm_swiglu_backward(const lrm_problem* problem, const int32_t* sel_row,
@@ -251,7 +251,7 @@ lrm_status lrm_grouped_fc1_dw_dx(const lrm_problem* problem, const void* dH, con
   const lrm_problem q = fc1_problem(*problem);
   WsLayout wl;
   LRM_TRY(check_ws(&q, ws, ws_bytes, &wl));
-  return from_hip(lrm::launch_gemms(q, dH, Xc, W1, cmp_off, dW1, dX, (char*)ws, wl, stream));
+  return from_hip(lrm::launch_gemms(q, dH, Xc, W1, cmp_off, dW1, dX, (char*)ws, wl, stream, 1));
 }
 
 lrm_status lrm_scatter_tokens(const lrm_problem* problem, const int32_t* sel_pair,

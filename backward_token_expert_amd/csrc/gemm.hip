@@ -567,7 +567,8 @@ __global__ __launch_bounds__(C::THREADS) void dx_bf16(const uint16_t* __restrict
 // workgroup that claims it, in the same order as in dx_bf16, so results do not depend on which
 // workgroup runs it.  A claim tries every die once, so every workgroup leaves when all ranges are
 // exhausted.
-template <class CW, class CX, int S>
+// kLayer (2: FC2, 1: FC1) only separates the two layers' launches in profiles.
+template <class CW, class CX, int S, int kLayer>
 __global__ __launch_bounds__(CW::THREADS) void gemm_fused(
     const uint16_t* __restrict__ Gc, const uint16_t* __restrict__ Phic,
     const uint16_t* __restrict__ W, const int32_t* __restrict__ cmp_off,
@@ -1041,7 +1042,7 @@ void launch_dw_t(const lrm_problem& p, const void* Gc, const void* Phic, const i
                      p.h, p.d, slots, dW);
 }
 
-template <class CW, class CX>
+template <class CW, class CX, int kLayer>
 void launch_fused_t(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
                     const int32_t* cmp_off, int32_t* sched, int32_t* tiles, int32_t* queue,
                     int64_t max_tiles, float* dW, float* slots, float* dphi, const Grid& g,
@@ -1050,7 +1051,7 @@ void launch_fused_t(const lrm_problem& p, const void* Gc, const void* Phic, cons
   static_assert(kThreadsPerSchedule == 1024, "one block shape for both schedules");
   hipLaunchKernelGGL(gemm_schedules, dim3(2), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap,
                      g.nxcd * gpx, gpx, sched, CX::BM, max_tiles, tiles, queue);
-  hipLaunchKernelGGL((gemm_fused<CW, CX, stages_for<CW>()>), dim3(g.blocks), dim3(CW::THREADS), 0,
+  hipLaunchKernelGGL((gemm_fused<CW, CX, stages_for<CW>(), kLayer>), dim3(g.blocks), dim3(CW::THREADS), 0,
                      s, (const uint16_t*)Gc, (const uint16_t*)Phic, (const uint16_t*)W, cmp_off,
                      sched, tiles, queue, g.nxcd, p.E_loc, p.K_cap, p.h, p.d, dW, slots, dphi);
   hipLaunchKernelGGL(dw_fixup, dim3(kMaxDwSlots * kFixupBlocks), dim3(256), 0, s, sched, p.E_loc,
@@ -1113,9 +1114,10 @@ hipError_t launch_dx(const lrm_problem& p, const void* Gc, const void* W, const 
   return hipGetLastError();
 }
 
-hipError_t launch_gemms(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
-                        const int32_t* cmp_off, float* dW, float* dphi, char* ws,
-                        const WsLayout& wl, hipStream_t s) {
+template <int kLayer>
+hipError_t launch_gemms_t(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
+                          const int32_t* cmp_off, float* dW, float* dphi, char* ws,
+                          const WsLayout& wl, hipStream_t s) {
   if (p.dtype != LRM_BF16) {
     const hipError_t e = launch_dw(p, Gc, Phic, cmp_off, dW, ws, wl, s);
     return e != hipSuccess ? e : launch_dx(p, Gc, W, cmp_off, dphi, ws, wl, s);
@@ -1128,12 +1130,19 @@ hipError_t launch_gemms(const lrm_problem& p, const void* Gc, const void* Phic, 
   static_assert(TileW_dX::BM == Tile128_dX::BM && TileW_dX::BM >= kDxTileM, "row tile");
   const int64_t max_tiles = ((int64_t)p.K_cap + TileW_dX::BM - 1) / TileW_dX::BM + p.E_loc;
   switch (pick_width(p.d)) {
-    case 0: launch_fused_t<TileW_dW, TileW_dX>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
-    case 1: launch_fused_t<Tile256_dW, Tile256_dX>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
-    case 2: launch_fused_t<Tile192_dW, Tile192_dX>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
-    default: launch_fused_t<Tile128_dW, Tile128_dX>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
+    case 0: launch_fused_t<TileW_dW, TileW_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
+    case 1: launch_fused_t<Tile256_dW, Tile256_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
+    case 2: launch_fused_t<Tile192_dW, Tile192_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
+    default: launch_fused_t<Tile128_dW, Tile128_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemms(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
+                        const int32_t* cmp_off, float* dW, float* dphi, char* ws,
+                        const WsLayout& wl, hipStream_t s, int layer) {
+  return layer == 1 ? launch_gemms_t<1>(p, Gc, Phic, W, cmp_off, dW, dphi, ws, wl, s)
+                    : launch_gemms_t<2>(p, Gc, Phic, W, cmp_off, dW, dphi, ws, wl, s);
 }
 
 }  // namespace lrm

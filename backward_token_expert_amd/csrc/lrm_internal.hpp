@@ -84,9 +84,10 @@ hipError_t launch_score_criterion(const lrm_problem& p, int criterion, const voi
 hipError_t launch_select(const lrm_problem& p, const float* score, const int32_t* fwd_off,
                          const int32_t* quota, const int32_t* cmp_off, int32_t* sel_row, char* ws,
                          const WsLayout& wl, hipStream_t s);
+// layer: 2 for FC2's gradients, 1 for FC1's (same kernels, told apart in profiles)
 hipError_t launch_gemms(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
                         const int32_t* cmp_off, float* dW, float* dphi, char* ws,
-                        const WsLayout& wl, hipStream_t s);
+                        const WsLayout& wl, hipStream_t s, int layer);
 hipError_t launch_admit(const lrm_problem& p, const lrm_admission& adm, const int32_t* fwd_off,
                         int32_t* quota, int32_t* cmp_off, int32_t* admitted, hipStream_t s);
 hipError_t launch_swiglu_bwd(const lrm_problem& p, const int32_t* sel_row, const int32_t* cmp_off,

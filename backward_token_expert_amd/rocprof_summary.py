@@ -26,10 +26,12 @@ import re
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 
-# C-ABI entry point -> (names of its GEMM kernels, translation unit)
-GEMM_KERNELS = {"lrm_grouped_dw": (("dw_bf16", "dw_f32"), "gemm.hip"),
-                "lrm_grouped_dx": (("dx_bf16", "dx_f32"), "gemm.hip"),
-                "lrm_grouped_dw_dx": (("gemm_fused",), "gemm.hip")}
+# C-ABI entry point -> (pattern of its GEMM kernels' short names, translation unit); the one-launch
+# kernel's last template argument tells FC2's launches (2) from FC1's (1)
+GEMM_KERNELS = {"lrm_grouped_dw": (r"(dw_bf16|dw_f32)\b", "gemm.hip"),
+                "lrm_grouped_dx": (r"(dx_bf16|dx_f32)\b", "gemm.hip"),
+                "lrm_grouped_dw_dx": (r"gemm_fused<.*, 2>$", "gemm.hip"),
+                "lrm_grouped_fc1_dw_dx": (r"gemm_fused<.*, 1>$", "gemm.hip")}
 _SHARED = ("lrm_device.hpp", "lrm_internal.hpp")
 
 
@@ -129,7 +131,7 @@ def counters_report(root: str, copy_bytes: int, workload: str):
                      f"{f(100 * hit / (hit + miss) if hit is not None and miss is not None else None)} | "
                      f"{f(conf, 0)} | {f(fe, 0)} | {f(wr, 0)} | {f(mb)} |")
         for call, (names, _) in GEMM_KERNELS.items():
-            if k.startswith(names) and mb is not None:
+            if re.match(names, k) and mb is not None:
                 rec["kernels"][call] = {"kernel": k, "traffic_bytes": mb * 1e6,
                                         "fetch_bytes": fe * 1024 * fs, "write_bytes": wr * 1024 * ws,
                                         "source_sha256": source_digest(call)}
