@@ -301,6 +301,23 @@ def test_segment_sizes_and_ragged_tiles(dtype):
         full_compare(w, pol)
 
 
+def test_select_segments_ending_at_the_row_capacity():
+    # every pair local, so the last segment ends exactly at L_cap = 4099 (not a multiple of 4, so
+    # the score, phi and row buffers end mid-16-byte chunk); segment starts 0, 1000, 1001, 3001
+    # take every offset modulo 4
+    sizes = [1000, 1, 2000, 1098]
+    rows = []
+    for e, n in enumerate(sizes):
+        rows += [[e]] * n
+    rows = np.asarray(rows)[np.random.default_rng(5).permutation(len(rows))]
+    w = custom(rows, E=4, e_lo=0, E_loc=4, h=64, d=64, dtype="bf16")
+    assert C.caps(w.spec)[0] == w.L == 4099
+    print("[case] segments ending at L_cap = 4099", flush=True)
+    for pol in ({"full": 0, "rho_num": 1, "rho_den": 2, "cap_abs": -1},
+                {"full": 0, "rho_num": 3, "rho_den": 1, "cap_abs": 777}):
+        full_compare(w, pol)
+
+
 @pytest.mark.parametrize("h,d", [(512, 384), (256, 512), (384, 1408), (2048, 200)])
 def test_gemm_tile_shapes(h, d):
     # column tiles of 192 (d % 192 == 0), 256 (d % 256 == 0) and 128 (otherwise, ragged edge)
