@@ -744,16 +744,18 @@ __device__ __forceinline__ void dw_schedule_body(const int32_t* __restrict__ cmp
 // ------------------------------------------------------------------------------------------------
 // fp32 path (v_mfma_f32_32x32x2f32); LDS tiles are [k][mn] with a padded pitch.
 // ------------------------------------------------------------------------------------------------
-constexpr int FBM = 128, FBN = 128;  // workgroup tile
-constexpr int BKF = 16;
-constexpr int PF = FBM + 4;  // floats per LDS k-row
+constexpr int FBM = 64, FBN = 64;    // workgroup tile: 4 wavefronts of 32 x 32
+constexpr int BKF = 64;              // K per step
+constexpr int PF = FBM + 4;          // floats per LDS k-row
+constexpr int JF = BKF * FBM / 4 / 128;  // 16-byte chunks each of 128 threads moves per step
+static_assert(FBM == FBN && FBM <= kDxTileM * 1 && kDxTileM == FBM, "dphi row tile of the table");
 
-// [k][mn] source: 16 rows x 128 columns = 512 chunks of 4 floats; thread t of 128 moves 4.
+// [k][mn] source: BKF rows x 64 columns = 16 BKF chunks of 4 floats; thread t of 128 moves JF.
 __device__ __forceinline__ void ld_kmn_f32(const float* __restrict__ X, int64_t ld, int k0,
-                                           int kend, int mn0, int mnend, int t, float4 v[4]) {
+                                           int kend, int mn0, int mnend, int t, float4 v[JF]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = t + 128 * j, row = c >> 5, col = mn0 + (c & 31) * 4;
+  for (int j = 0; j < JF; ++j) {
+    const int c = t + 128 * j, row = c >> 4, col = mn0 + (c & 15) * 4;
     if (k0 + row < kend && col < mnend)
       v[j] = *(const float4*)(X + (int64_t)(k0 + row) * ld + col);
     else
@@ -761,20 +763,20 @@ __device__ __forceinline__ void ld_kmn_f32(const float* __restrict__ X, int64_t 
   }
 }
 
-__device__ __forceinline__ void st_kmn_f32(float* __restrict__ s, int t, const float4 v[4]) {
+__device__ __forceinline__ void st_kmn_f32(float* __restrict__ s, int t, const float4 v[JF]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = t + 128 * j, row = c >> 5, col = (c & 31) * 4;
+  for (int j = 0; j < JF; ++j) {
+    const int c = t + 128 * j, row = c >> 4, col = (c & 15) * 4;
     *(float4*)(s + row * PF + col) = v[j];
   }
 }
 
-// [mn][k] source: 128 rows x 16 k = 512 chunks of 4 k; stored transposed into [k][mn].
+// [mn][k] source: 64 rows x BKF k = 16 BKF chunks of 4 k; stored transposed into [k][mn].
 __device__ __forceinline__ void ld_mnk_f32(const float* __restrict__ X, int64_t ld, int mn0,
-                                           int mnend, int k0, int kend, int t, float4 v[4]) {
+                                           int mnend, int k0, int kend, int t, float4 v[JF]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = t + 128 * j, row = c >> 2, kc = (c & 3) * 4;
+  for (int j = 0; j < JF; ++j) {
+    const int c = t + 128 * j, row = c / (BKF / 4), kc = (c % (BKF / 4)) * 4;
     if (mn0 + row < mnend && k0 + kc < kend)
       v[j] = *(const float4*)(X + (int64_t)(mn0 + row) * ld + k0 + kc);
     else
@@ -782,10 +784,10 @@ __device__ __forceinline__ void ld_mnk_f32(const float* __restrict__ X, int64_t 
   }
 }
 
-__device__ __forceinline__ void st_mnk_f32(float* __restrict__ s, int t, const float4 v[4]) {
+__device__ __forceinline__ void st_mnk_f32(float* __restrict__ s, int t, const float4 v[JF]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = t + 128 * j, row = c >> 2, kc = (c & 3) * 4;
+  for (int j = 0; j < JF; ++j) {
+    const int c = t + 128 * j, row = c / (BKF / 4), kc = (c % (BKF / 4)) * 4;
     s[(kc + 0) * PF + row] = v[j].x;
     s[(kc + 1) * PF + row] = v[j].y;
     s[(kc + 2) * PF + row] = v[j].z;
@@ -795,20 +797,13 @@ __device__ __forceinline__ void st_mnk_f32(float* __restrict__ s, int t, const f
 
 __device__ __forceinline__ void mma_step_f32(const float* __restrict__ sa,
                                              const float* __restrict__ sb, int wm, int wn,
-                                             int lane, f32x16 acc[2][2]) {
+                                             int lane, f32x16 acc[1][1]) {
   const int r = lane & 31, kh = lane >> 5;
 #pragma unroll
   for (int ks = 0; ks < BKF; ks += 2) {
-    float a[2], b[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) a[i] = sa[(ks + kh) * PF + wm * 64 + i * 32 + r];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = sb[(ks + kh) * PF + wn * 64 + j * 32 + r];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    const float a = sa[(ks + kh) * PF + wm * 32 + r];
+    const float b = sb[(ks + kh) * PF + wn * 32 + r];
+    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[0][0], 0, 0, 0);
   }
 }
 
@@ -823,20 +818,16 @@ __global__ __launch_bounds__(kF32Threads) void dw_f32(const float* __restrict__ 
   int s = cmp_off[e], t = cmp_off[e + 1];
   s = s < 0 ? 0 : (s > K_cap ? K_cap : s);
   t = t < s ? s : (t > K_cap ? K_cap : t);
-  f32x16 acc[2][2];
+  f32x16 acc[1][1];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  for (int r = 0; r < 16; ++r) acc[0][0][r] = 0.0f;
   const bool isA = tid < 128;
   const int blk = tid & 127;
   const float* X = isA ? Gc : Phic;
   const int64_t ld = isA ? h : d;
   const int mn0 = isA ? m0 : n0, mnend = isA ? h : d;
   const int nk = (t - s + BKF - 1) / BKF;
-  float4 v[4];
+  float4 v[JF];
   if (nk > 0) {
     ld_kmn_f32(X, ld, s, t, mn0, mnend, blk, v);
     st_kmn_f32(isA ? sa[0] : sb[0], blk, v);
@@ -849,7 +840,7 @@ __global__ __launch_bounds__(kF32Threads) void dw_f32(const float* __restrict__ 
     if (kt + 1 < nk) st_kmn_f32(isA ? sa[cur ^ 1] : sb[cur ^ 1], blk, v);
     __syncthreads();
   }
-  store_acc<2, 2>(dW + (int64_t)e * h * d, d, m0, h, n0, d, wm, wn, lane, acc);
+  store_acc<1, 1>(dW + (int64_t)e * h * d, d, m0, h, n0, d, wm, wn, lane, acc);
 }
 
 __global__ __launch_bounds__(kF32Threads) void dx_f32(const float* __restrict__ Gc,
@@ -866,18 +857,14 @@ __global__ __launch_bounds__(kF32Threads) void dx_f32(const float* __restrict__ 
   mend = mend > K_cap ? K_cap : mend;
   const int n0 = blockIdx.y * FBN;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave, wm = wv >> 1, wn = wv & 1;
-  f32x16 acc[2][2];
+  f32x16 acc[1][1];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  for (int r = 0; r < 16; ++r) acc[0][0][r] = 0.0f;
   const bool isA = tid < 128;
   const int blk = tid & 127;
   const float* We = W + (int64_t)e * h * d;
   const int nk = (h + BKF - 1) / BKF;
-  float4 v[4];
+  float4 v[JF];
   if (isA) {
     ld_mnk_f32(Gc, h, m0, mend, 0, h, blk, v);
     st_mnk_f32(sa[0], blk, v);
@@ -900,7 +887,7 @@ __global__ __launch_bounds__(kF32Threads) void dx_f32(const float* __restrict__ 
     }
     __syncthreads();
   }
-  store_acc<2, 2>(dphi, d, m0, mend, n0, d, wm, wn, lane, acc);
+  store_acc<1, 1>(dphi, d, m0, mend, n0, d, wm, wn, lane, acc);
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -12,7 +12,7 @@ namespace lrm {
 // Pairs handled by one wavefront in the counting passes of lrm_plan_quotas.
 constexpr int kPlanChunk = 1024;
 // Smallest row tile of the grouped input-gradient GEMMs (sizes the workspace tile table).
-constexpr int kDxTileM = 128;
+constexpr int kDxTileM = 64;
 // Upper bound on the accelerator dies (XCDs) the GEMM schedules spread work over.
 constexpr int kMaxXcd = 8;
 // dW schedule: at most kMaxGroupsPerXcd groups of workgroups per die share a job list; experts far
