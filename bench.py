@@ -386,7 +386,7 @@ def recorded_traffic(call, workload):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the path runs on one GPU; --gpus must be 1 (sharding across GPUs is not implemented)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import synth
