@@ -269,3 +269,60 @@ def test_layer_full_size(cfg):
         assert errx <= tol, f"dX expert {e}: rel fro {errx} on sampled rows"
     dx = O.scatter_with_zeros(g["dX"], g["sel_pair"], sp.T, sp.k).astype(np.float32)
     assert g["dx"].tobytes() == dx.tobytes()
+
+
+def test_layer_graph_replay_equals_eager():
+    """The path and the rest of the expert backward captured in one HIP graph: every replay gives
+    the eager result bit for bit (no call allocates, synchronises or records a memset)."""
+    torch = _torch()
+    from backward_token_expert_amd import path
+    w = C.workload(1, T=2048)
+    sp = w.spec
+    pol = synth.policy(sp)
+    P, bufs, lay, li, (ac, x, W1), err = run_layer_gpu(w, pol)
+    assert err == 0
+    want = host_layer(bufs, lay, sp)
+    inp = C.upload(w)
+    b = path.DeviceBuffers(P)
+    ly = path.LayerBuffers(P)
+    print("[case] layer backward graph replay", flush=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        path.run(P, C.policy_obj(pol), inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"],
+                 inp["W"], b, s)
+        path.run_layer(P, ac, x, W1, b, ly, s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            path.run(P, C.policy_obj(pol), inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"],
+                     inp["W"], b, s)
+            path.run_layer(P, ac, x, W1, b, ly, s)
+    for rep in range(3):
+        ly.dx.fill_(5.0)
+        ly.dW1.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host_layer(b, ly, sp)
+        for key in ("dH", "Xc", "dW1", "dX", "dx"):
+            assert got[key].tobytes() == want[key].tobytes(), (rep, key)
+
+
+def test_layer_more_than_64_slots_per_token():
+    """k = 70 experts per token, so the per-token passes (gradient compaction, FC1 input gather,
+    return to the tokens) walk a token's slots in two 64-lane blocks."""
+    from tests.test_gpu_parity import custom
+    rng = np.random.default_rng(4)
+    T, k, E = 96, 70, 80
+    rows = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    w = custom(rows, E=E, e_lo=3, E_loc=72, h=64, d=32, dtype="bf16")
+    sp = w.spec
+    pol = {"full": 0, "rho_num": 1, "rho_den": 2, "cap_abs": -1, "kind": "cap"}
+    print(f"[case] layer backward k={k}", flush=True)
+    P, bufs, lay, li, _, err = run_layer_gpu(w, pol)
+    assert err == 0
+    g = host_layer(bufs, lay, sp)
+    o_path = C.oracle_run(w, pol)
+    np.testing.assert_array_equal(g["sel_row"], o_path["sel_row"])
+    check_stages_full(w, g, li, sp.dtype)
