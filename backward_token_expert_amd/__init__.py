@@ -11,5 +11,6 @@ from .lrm import (LRM_BF16, LRM_F32, Admission, LrmError, Problem, QuotaPolicy, 
                   lrm_compact, lrm_gather_tokens, lrm_grouped_dw, lrm_grouped_dw_dx,
                   lrm_grouped_dx, lrm_grouped_fc1_dw, lrm_grouped_fc1_dw_dx, lrm_grouped_fc1_dx,
                   lrm_plan_quotas, lrm_scatter_tokens, lrm_swiglu_backward,
-                  lrm_read_device_error, lrm_score, lrm_score_criterion, lrm_select,
+                  lrm_read_device_error, lrm_score, lrm_score_combine, lrm_score_criterion,
+                  lrm_score_norms, lrm_select,
                   lrm_workspace_bytes, make_policy, make_problem)

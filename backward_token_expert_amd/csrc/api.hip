@@ -114,6 +114,27 @@ lrm_status lrm_score(const lrm_problem* problem, const float* topk_w, const void
                                     wl, stream));
 }
 
+lrm_status lrm_score_norms(const lrm_problem* problem, const void* g, const void* phi, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!g || !phi) return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(g) || !aligned16(phi)) return LRM_ERR_UNSUPPORTED;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_score_norms(*problem, g, phi, (char*)ws, wl, stream));
+}
+
+lrm_status lrm_score_combine(const lrm_problem* problem, const float* topk_w,
+                             const int32_t* row_pair, const int32_t* fwd_off, float* score,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!topk_w || !row_pair || !fwd_off || !score) return LRM_ERR_INVALID_ARGUMENT;
+  WsLayout wl;
+  LRM_TRY(check_ws(problem, ws, ws_bytes, &wl));
+  return from_hip(lrm::launch_score_combine(*problem, topk_w, row_pair, fwd_off, score, (char*)ws,
+                                            wl, stream));
+}
+
 lrm_status lrm_score_criterion(const lrm_problem* problem, int32_t criterion, const float* topk_w,
                                const void* g, const void* phi, const float* keys,
                                const int32_t* row_pair, const int32_t* fwd_off, float* score,

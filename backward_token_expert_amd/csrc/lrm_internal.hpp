@@ -34,6 +34,7 @@ struct WsLayout {
   size_t hist;    // int32 [nchunks][E+1] per-chunk expert histograms / local prefixes; column E
                   //                      counts expert ids outside [0, E)
   size_t gnorm;   // double [T]           ||g_t||^2
+  size_t pnorm;   // double [L_cap]       ||phi_r||^2 of the split score (lrm_score_norms)
   size_t tiles;   // int32 [1 + 2*max_tiles] dx tile table: count, then (expert, row0) pairs
   size_t order;   // int32 [kDwHeader + groups * jobs * 4] dW schedule: header, per-group job lists
   size_t dwslots; // float [kMaxDwSlots][h][d] partial dW of split experts
@@ -57,6 +58,8 @@ inline WsLayout ws_layout(const lrm_problem& p) {
   off = align_up(off + (size_t)w.nchunks * (p.E + 1) * 4, 256);
   w.gnorm = off;
   off = align_up(off + (size_t)p.T * 8, 256);
+  w.pnorm = off;
+  off = align_up(off + (size_t)p.L_cap * 8, 256);
   w.tiles = off;
   off = align_up(off + (size_t)(1 + 2 * w.max_tiles) * 4, 256);
   w.order = off;
@@ -77,6 +80,11 @@ hipError_t launch_plan(const lrm_problem& p, const lrm_quota_policy& pol, const 
 hipError_t launch_score(const lrm_problem& p, const float* topk_w, const void* g, const void* phi,
                         const int32_t* row_pair, const int32_t* fwd_off, float* score, char* ws,
                         const WsLayout& wl, hipStream_t s);
+hipError_t launch_score_norms(const lrm_problem& p, const void* g, const void* phi, char* ws,
+                              const WsLayout& wl, hipStream_t s);
+hipError_t launch_score_combine(const lrm_problem& p, const float* topk_w, const int32_t* row_pair,
+                                const int32_t* fwd_off, float* score, char* ws, const WsLayout& wl,
+                                hipStream_t s);
 hipError_t launch_score_criterion(const lrm_problem& p, int criterion, const void* g,
                                   const float* keys, const int32_t* row_pair,
                                   const int32_t* fwd_off, float* score, char* ws,

@@ -5,15 +5,21 @@
 // (counts and prefix offsets define the segments).  The quota cap follows the capacity rule
 // C = CF * mean load of "Expert Parallel Math Deep" ("Capacity and the exact drop-rate formula").
 //
-// Three launches, all sizes device-resident (no host round trip, as the TopoEP paper argues for
+// Two launches, all sizes device-resident (no host round trip, as the TopoEP paper argues for
 // planning in its host-plan latency model):
 //   plan_hist    one wavefront per chunk of kPlanChunk pairs: per-chunk expert histogram, plus a
 //                column counting expert ids outside [0, E)
-//   plan_scan    one workgroup: expert totals, per-chunk prefixes, fwd_off, quotas, cmp_off, and
-//                the device error word (overwritten, which clears what earlier calls left)
-//   plan_scatter one wavefront per chunk: stable counting-sort scatter of the local pairs
-// The scatter ranks equal experts inside a wavefront with ballots (a 64-lane "match"), so the
-// layout is stable (pair index ascending within each expert) without any sort.
+//   plan_place   1024-thread workgroups.  Each placing workgroup owns 16 consecutive chunks (one
+//                per wavefront): it sums the local experts' columns of the histogram table itself
+//                -- the totals, and the pairs in the chunks before its own -- so no workgroup
+//                waits for another, derives fwd_off, and scatters its chunks' local pairs (stable
+//                counting sort).  One more workgroup sums every column (counts, ids outside
+//                [0, E)) and writes fwd_off, the quotas, cmp_off and the device error word
+//                (overwritten, which clears what earlier calls left).
+// The planning is latency-bound (about 1 MB of indices): every pass keeps 16 loads per lane in
+// flight, so a pass costs one memory round trip.  The scatter ranks equal experts inside a
+// wavefront with ballots (a 64-lane "match"), so the layout is stable (pair index ascending
+// within each expert) without any sort.
 #include "lrm_device.hpp"
 #include "lrm_internal.hpp"
 
@@ -24,7 +30,8 @@ constexpr int kPlanBlock = 256;                 // 4 wavefronts, one chunk each
 constexpr int kChunksPerBlock = kPlanBlock / kWave;
 constexpr int kMaxE = 4096;
 
-constexpr int kHistBatch = 4;  // index loads a lane issues before its LDS atomics
+constexpr int kHistBatch = 16;  // index loads a lane issues before using them (a whole chunk)
+static_assert(kPlanChunk == kHistBatch * kWave, "one load batch per chunk");
 
 __global__ __launch_bounds__(kPlanBlock) void plan_hist(const int32_t* __restrict__ idx, int64_t P,
                                                         int E, int64_t nchunks,
@@ -59,7 +66,7 @@ __global__ __launch_bounds__(kPlanBlock) void plan_hist(const int32_t* __restric
 }
 
 // Largest value over the 1024 threads of a workgroup.
-__device__ int block_max_1024(int v, int* sh /* >= 17 ints */) {
+__device__ __forceinline__ int block_max_1024(int v, int* sh /* >= 17 ints */) {
   const int w = threadIdx.x / kWave;
 #pragma unroll
   for (int o = kWave / 2; o >= 1; o >>= 1) {
@@ -78,7 +85,8 @@ __device__ int block_max_1024(int v, int* sh /* >= 17 ints */) {
 // loads sum to L): floor(B * n / L) each, then one more row to the B - sum(floors) experts with
 // the largest remainders (B * n) mod L, the lower expert first on equal remainders.  Remainders
 // of different experts share the denominator L, so comparing them as integers is exact.
-__device__ int proportional_quota(int n, int L, int B, int E_loc, int* rem, int* sh) {
+__device__ __forceinline__ int proportional_quota(int n, int L, int B, int E_loc, int* rem,
+                                                  int* sh) {
   const int tid = threadIdx.x;
   int fl = 0, r = 0;
   if (tid < E_loc && L > 0) {
@@ -107,7 +115,7 @@ __device__ int proportional_quota(int n, int L, int B, int E_loc, int* rem, int*
 // total T(x) = sum_f min(m_f, x) is piecewise linear with breakpoints at the m_f, so the last
 // breakpoint v with T(v) <= B (v = 0 if none) and the slope c = #{f : m_f > v} give
 // level = v + (B - T(v)) / c, which stays below the next breakpoint because T there exceeds B.
-__device__ int waterfill_quota(int n, int cap, int B, int E_loc, int* mv, int* sh) {
+__device__ __forceinline__ int waterfill_quota(int n, int cap, int B, int E_loc, int* mv, int* sh) {
   const int tid = threadIdx.x;
   const int m = tid < E_loc ? (cap >= 0 && n > cap ? cap : n) : 0;
   int S = 0;
@@ -136,13 +144,12 @@ __device__ int waterfill_quota(int n, int cap, int B, int E_loc, int* mv, int* s
   return q;
 }
 
-constexpr int kScanBatch = 8;
 
 // Quota of thread tid's expert (tid < E_loc; 0 for the other threads) under `pol`, the expert
 // holding seg of the Lc local rows.  Every thread of the workgroup must call it (the proportional
 // and water-fill splits hold barriers); `pol` is the same for all of them.
-__device__ int policy_quota(const lrm_quota_policy& pol, int seg, int Lc, int E_loc, int* rem,
-                            int* sh) {
+__device__ __forceinline__ int policy_quota(const lrm_quota_policy& pol, int seg, int Lc,
+                                            int E_loc, int* rem, int* sh) {
   const int tid = threadIdx.x;
   if (pol.full) return tid < E_loc ? seg : 0;
   if (pol.kind == LRM_QUOTA_CAP) {
@@ -158,145 +165,169 @@ __device__ int policy_quota(const lrm_quota_policy& pol, int seg, int Lc, int E_
                                             : waterfill_quota(seg, pol.cap_abs, B, E_loc, rem, sh);
 }
 
-__global__ __launch_bounds__(1024) void plan_scan(int32_t* __restrict__ hist, int64_t nchunks,
-                                                  int E, int e_lo, int E_loc, int L_cap, int K_cap,
-                                                  lrm_quota_policy pol, int32_t* __restrict__ counts,
-                                                  int32_t* __restrict__ fwd_off,
-                                                  int32_t* __restrict__ quota,
-                                                  int32_t* __restrict__ cmp_off,
-                                                  int32_t* __restrict__ err) {
-  __shared__ int part[16][64];
-  __shared__ int nloc[1024];
-  __shared__ int rem[1024];
-  __shared__ int sh[32];
-  __shared__ int nbad;
-  const int tid = threadIdx.x, sub = tid & 63, grp = tid >> 6;
-  const int64_t cpg = (nchunks + 15) / 16;
-  const int64_t c0 = grp * cpg, c1 = (c0 + cpg < nchunks) ? c0 + cpg : nchunks;
+constexpr int kPlaceWaves = 16;  // chunks per placing workgroup, one per wavefront
+constexpr int kPlaceThreads = kPlaceWaves * kWave;
+constexpr int kMaxLoc = 1024;
+constexpr int kSumBatch = 16;    // table loads a thread keeps in flight
 
-  // Phase A: expert totals; per-chunk exclusive prefixes (in place) for the local experts.  Each
-  // thread walks its contiguous chunk range of one column with kScanBatch loads in flight.
+struct PlaceSmem {
+  union {
+    int base[kPlaceWaves][kMaxLoc];  // placing workgroups: next row of each local expert per wave
+    int cnt[kMaxE + 1];              // the quota workgroup: every column's total
+  };
+  int tot[kMaxLoc];  // local totals, then the clamped segment ends
+  int bef[kMaxLoc];  // local pairs in the chunks before this workgroup's first
+  int rem[1024];
+  int sh[32];
+};
+
+__global__ __launch_bounds__(kPlaceThreads) void plan_place(
+    const int32_t* __restrict__ idx, int64_t P, int E, int e_lo, int E_loc, int nbits,
+    int64_t nchunks, const int32_t* __restrict__ hist, int L_cap, int K_cap, lrm_quota_policy pol,
+    int32_t* __restrict__ counts, int32_t* __restrict__ fwd_off, int32_t* __restrict__ row_pair,
+    int32_t* __restrict__ quota, int32_t* __restrict__ cmp_off, int32_t* __restrict__ err) {
+  __shared__ PlaceSmem sm;
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
   const int cols = E + 1;
-  for (int e0 = 0; e0 < cols; e0 += 64) {
-    const int e = e0 + sub;
-    int s = 0;
-    if (e < cols)
-      for (int64_t c = c0; c < c1; c += kScanBatch) {
-        int v[kScanBatch];
+  const bool quota_wg = blockIdx.x == gridDim.x - 1;
+  const int64_t c_first = (int64_t)blockIdx.x * kPlaceWaves;
+  for (int i = tid; i < E_loc; i += kPlaceThreads) {
+    sm.tot[i] = 0;
+    sm.bef[i] = 0;
+  }
+  if (quota_wg)
+    for (int i = tid; i < cols; i += kPlaceThreads) sm.cnt[i] = 0;
+  __syncthreads();
+
+  int nbad = 0;
+  if (quota_wg) {
+    // Every column's total: thread (rg, cc) sums rows rg, rg + R, ... of columns cc, cc + C0, ...
+    // (consecutive threads read consecutive columns of a row).
+    const int C0 = cols < kPlaceThreads ? cols : kPlaceThreads, R = kPlaceThreads / C0;
+    const int rg = tid / C0, cc = tid % C0;
+    if (rg < R)
+      for (int c = cc; c < cols; c += C0) {
+        int sum = 0;
+        for (int64_t r0 = rg; r0 < nchunks; r0 += (int64_t)R * kSumBatch) {
+          int v[kSumBatch];
 #pragma unroll
-        for (int u = 0; u < kScanBatch; ++u) v[u] = c + u < c1 ? hist[(c + u) * cols + e] : 0;
-#pragma unroll
-        for (int u = 0; u < kScanBatch; ++u) s += v[u];
-      }
-    part[grp][sub] = s;
-    __syncthreads();
-    if (tid < 64) {
-      int run = 0;
-      for (int g2 = 0; g2 < 16; ++g2) {
-        const int v = part[g2][tid];
-        part[g2][tid] = run;
-        run += v;
-      }
-      if (e0 + tid < E) {
-        counts[e0 + tid] = run;
-        const int el = e0 + tid - e_lo;
-        if (el >= 0 && el < E_loc) nloc[el] = run;
-      } else if (e0 + tid == E) {
-        nbad = run;
-      }
-    }
-    __syncthreads();
-    if (e < E && e >= e_lo && e < e_lo + E_loc) {
-      int run = part[grp][sub];
-      for (int64_t c = c0; c < c1; c += kScanBatch) {
-        int v[kScanBatch];
-#pragma unroll
-        for (int u = 0; u < kScanBatch; ++u) v[u] = c + u < c1 ? hist[(c + u) * cols + e] : 0;
-#pragma unroll
-        for (int u = 0; u < kScanBatch; ++u) {
-          if (c + u < c1) {
-            hist[(c + u) * cols + e] = run;
-            run += v[u];
+          for (int u = 0; u < kSumBatch; ++u) {
+            const int64_t r = r0 + (int64_t)u * R;
+            v[u] = r < nchunks ? hist[r * cols + c] : 0;
           }
+#pragma unroll
+          for (int u = 0; u < kSumBatch; ++u) sum += v[u];
+        }
+        if (sum != 0) atomicAdd(&sm.cnt[c], sum);
+      }
+    __syncthreads();
+    for (int e = tid; e < E; e += kPlaceThreads) counts[e] = sm.cnt[e];
+    for (int i = tid; i < E_loc; i += kPlaceThreads) sm.tot[i] = sm.cnt[e_lo + i];
+    nbad = sm.cnt[E];
+  } else {
+    // The local columns: J threads per local expert walk the chunks j, j + J, ...; chunks before
+    // this workgroup's first add to bef, its own 16 are kept one by one for the wave offsets.
+    const int J = kPlaceThreads / E_loc;
+    const int el = tid % E_loc, j = tid / E_loc;
+    if (j < J) {
+      int t_sum = 0, b_sum = 0;
+      for (int64_t c0 = j; c0 < nchunks; c0 += (int64_t)J * kSumBatch) {
+        int v[kSumBatch];
+#pragma unroll
+        for (int u = 0; u < kSumBatch; ++u) {
+          const int64_t c = c0 + (int64_t)u * J;
+          v[u] = c < nchunks ? hist[c * cols + e_lo + el] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kSumBatch; ++u) {
+          const int64_t c = c0 + (int64_t)u * J;
+          if (c >= nchunks) continue;
+          t_sum += v[u];
+          if (c < c_first)
+            b_sum += v[u];
+          else if (c < c_first + kPlaceWaves)
+            sm.base[c - c_first][el] = v[u];
         }
       }
+      atomicAdd(&sm.tot[el], t_sum);
+      atomicAdd(&sm.bef[el], b_sum);
     }
-    __syncthreads();
   }
+  __syncthreads();
 
-  // Phase B: forward offsets (clamped to L_cap), quotas, compacted offsets (clamped to K_cap).
-  const int n = tid < E_loc ? nloc[tid] : 0;
+  // Forward offsets, clamped to L_cap (every workgroup derives the same values).
+  const int n = tid < E_loc ? sm.tot[tid] : 0;
   int L = 0;
-  const int pre = block_exclusive_scan_1024(n, sh, &L);
+  const int pre = block_exclusive_scan_1024(n, sm.sh, &L);
   const int f0 = pre < L_cap ? pre : L_cap;
   const int f1 = pre + n < L_cap ? pre + n : L_cap;
-  const int seg = f1 - f0;
   const int Lc = L < L_cap ? L : L_cap;
-  if (tid < E_loc) fwd_off[tid] = f0;
-  if (tid == 0) fwd_off[E_loc] = Lc;
-  const int q = policy_quota(pol, seg, Lc, E_loc, rem, sh);
-  int K = 0;
-  const int cpre = block_exclusive_scan_1024(q, sh, &K);
-  const int o0 = cpre < K_cap ? cpre : K_cap;
-  const int o1 = cpre + q < K_cap ? cpre + q : K_cap;
-  if (tid < E_loc) {
-    cmp_off[tid] = o0;
-    quota[tid] = o1 - o0;
-  }
-  if (tid == 0) {
-    cmp_off[E_loc] = K < K_cap ? K : K_cap;
-    // The first call of a sequence: its error word replaces whatever earlier calls left.
-    *err = (nbad ? LRM_DEVERR_EXPERT_ID : 0) | (L > L_cap ? LRM_DEVERR_L_CAP : 0) |
-           (K > K_cap ? LRM_DEVERR_K_CAP : 0);
-  }
-}
 
-__global__ __launch_bounds__(kPlanBlock) void plan_scatter(const int32_t* __restrict__ idx,
-                                                           int64_t P, int E, int e_lo, int E_loc,
-                                                           int nbits, int64_t nchunks,
-                                                           const int32_t* __restrict__ hist,
-                                                           const int32_t* __restrict__ fwd_off,
-                                                           int32_t* __restrict__ row_pair) {
-  __shared__ int base[kChunksPerBlock][1024];
-  const int w = threadIdx.x / kWave, lane = lane_id();
-  const int64_t c = (int64_t)blockIdx.x * kChunksPerBlock + w;
-  if (c >= nchunks) return;  // whole wavefront leaves; no block barrier follows
-  for (int i = lane; i < E_loc; i += kWave) base[w][i] = fwd_off[i] + hist[c * (E + 1) + e_lo + i];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (quota_wg) {
+    if (tid < E_loc) fwd_off[tid] = f0;
+    if (tid == 0) fwd_off[E_loc] = Lc;
+    const int q = policy_quota(pol, f1 - f0, Lc, E_loc, sm.rem, sm.sh);
+    int K = 0;
+    const int cpre = block_exclusive_scan_1024(q, sm.sh, &K);
+    const int o0 = cpre < K_cap ? cpre : K_cap;
+    const int o1 = cpre + q < K_cap ? cpre + q : K_cap;
+    if (tid < E_loc) {
+      cmp_off[tid] = o0;
+      quota[tid] = o1 - o0;
+    }
+    if (tid == 0) {
+      cmp_off[E_loc] = K < K_cap ? K : K_cap;
+      // The first call of a sequence: its error word replaces whatever earlier calls left.
+      *err = (nbad ? LRM_DEVERR_EXPERT_ID : 0) | (L > L_cap ? LRM_DEVERR_L_CAP : 0) |
+             (K > K_cap ? LRM_DEVERR_K_CAP : 0);
+    }
+    return;
+  }
+
+  // Each wave's first row per local expert: the segment start, the pairs of earlier chunks, then
+  // the counts of this workgroup's earlier chunks (waves past the last chunk get unused values).
+  if (tid < E_loc) {
+    int run = f0 + sm.bef[tid];
+    for (int x = 0; x < kPlaceWaves; ++x) {
+      const int v = sm.base[x][tid];
+      sm.base[x][tid] = run;
+      run += v;
+    }
+    sm.tot[tid] = f1;
+  }
+  __syncthreads();
+  const int64_t c = c_first + w;
+  if (c >= nchunks) return;  // no barrier follows
   const uint64_t lt = lanemask_lt();
   const int64_t p0 = c * kPlanChunk;
-  for (int r0 = 0; r0 < kPlanChunk; r0 += kHistBatch * kWave) {
-    int ev[kHistBatch];
+  int ev[kHistBatch];
 #pragma unroll
-    for (int u = 0; u < kHistBatch; ++u) {
-      const int64_t p = p0 + r0 + u * kWave + lane;
-      ev[u] = p < P ? idx[p] : -1;
+  for (int u = 0; u < kHistBatch; ++u) {
+    const int64_t p = p0 + u * kWave + lane;
+    ev[u] = p < P ? idx[p] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < kHistBatch; ++u) {
+    const int64_t p = p0 + u * kWave + lane;
+    const int e = ev[u];
+    const bool local = e >= e_lo && e < e_lo + E_loc;
+    const int el = local ? e - e_lo : 0;
+    uint64_t peers = ballot(local);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (el >> b) & 1;
+      const uint64_t m = ballot(bit);
+      peers &= bit ? m : ~m;
     }
-#pragma unroll
-    for (int u = 0; u < kHistBatch; ++u) {
-      const int64_t p = p0 + r0 + u * kWave + lane;
-      const int e = ev[u];
-      const bool local = e >= e_lo && e < e_lo + E_loc;
-      const int el = local ? e - e_lo : 0;
-      uint64_t peers = ballot(local);
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = (el >> b) & 1;
-        const uint64_t m = ballot(bit);
-        peers &= bit ? m : ~m;
-      }
-      const int leader = local ? __builtin_ctzll(peers) : lane;
-      int old = 0;
-      if (local && leader == lane) {
-        old = base[w][el];
-        base[w][el] = old + __builtin_popcountll(peers);
-      }
-      old = __shfl(old, leader, kWave);
-      if (local) {
-        const int row = old + __builtin_popcountll(peers & lt);
-        if (row < fwd_off[el + 1]) row_pair[row] = (int32_t)p;
-      }
+    const int leader = local ? __builtin_ctzll(peers) : lane;
+    int old = 0;
+    if (local && leader == lane) {
+      old = sm.base[w][el];
+      sm.base[w][el] = old + __builtin_popcountll(peers);
+    }
+    old = __shfl(old, leader, kWave);
+    if (local) {
+      const int row = old + __builtin_popcountll(peers & lt);
+      if (row < sm.tot[el]) row_pair[row] = (int32_t)p;
     }
   }
 }
@@ -362,12 +393,12 @@ hipError_t launch_plan(const lrm_problem& p, const lrm_quota_policy& pol, const 
   const unsigned nblk = (unsigned)((wl.nchunks + kChunksPerBlock - 1) / kChunksPerBlock);
   int nbits = 0;
   while ((1 << nbits) < p.E_loc) ++nbits;
+  const unsigned nplace = (unsigned)((wl.nchunks + kPlaceWaves - 1) / kPlaceWaves);
   hipLaunchKernelGGL(plan_hist, dim3(nblk), dim3(kPlanBlock), 0, s, topk_idx, P, p.E, wl.nchunks,
                      hist);
-  hipLaunchKernelGGL(plan_scan, dim3(1), dim3(1024), 0, s, hist, wl.nchunks, p.E, p.e_lo, p.E_loc,
-                     p.L_cap, p.K_cap, pol, counts, fwd_off, quota, cmp_off, err);
-  hipLaunchKernelGGL(plan_scatter, dim3(nblk), dim3(kPlanBlock), 0, s, topk_idx, P, p.E, p.e_lo,
-                     p.E_loc, nbits, wl.nchunks, hist, fwd_off, row_pair);
+  hipLaunchKernelGGL(plan_place, dim3(nplace + 1), dim3(kPlaceThreads), 0, s, topk_idx, P, p.E,
+                     p.e_lo, p.E_loc, nbits, wl.nchunks, hist, p.L_cap, p.K_cap, pol, counts,
+                     fwd_off, row_pair, quota, cmp_off, err);
   return hipGetLastError();
 }
 

@@ -9,6 +9,11 @@
 //   token_norm    ||g_t||^2 for all T tokens (one wavefront per row, 16-byte loads)
 //   row_score     ||phi_r||^2 per forward row (16 lanes per row, 4 rows per wavefront), then the
 //                 product with alpha^2 and ||g_t||^2
+// The split form (launch_score_norms, then launch_score_combine) takes the squared norms of g and
+// of every phi row up to L_cap before the layout exists -- neither norm depends on the routing --
+// so a caller can run it on a second stream while the counts and quotas are planned; the product
+// (row_combine) then only gathers alpha and the two norms per row.  Both forms evaluate the same
+// float64 expressions in the same order, so their scores are bitwise equal.
 // Squares of bf16/fp32 values are exact in float64, and the sums are accumulated in float64 with
 // a fixed lane assignment and a fixed butterfly, so two rows with equal contents give bitwise
 // equal scores wherever they sit; the final product is rounded once to float32.
@@ -78,17 +83,23 @@ __global__ __launch_bounds__(kBlock) void token_norm(const uint4* __restrict__ g
 constexpr int kLanesPerRow = 16;
 constexpr int kRowsPerWave = kWave / kLanesPerRow;
 
-template <bool kBF16>
+// kNorms: only ||phi_r||^2 (float64) to pnorm[r], for every row below L_cap, without reading the
+// layout (fwd_off, row_pair, score and err are unused).
+template <bool kBF16, bool kNorms>
 __global__ __launch_bounds__(kBlock) void row_score(const uint4* __restrict__ phi, int chunks,
                                                     const int32_t* __restrict__ fwd_off, int E_loc,
                                                     int L_cap, const int32_t* __restrict__ row_pair,
                                                     const float* __restrict__ topk_w, int k,
                                                     int64_t P, const double* __restrict__ gnorm,
                                                     float* __restrict__ score,
+                                                    double* __restrict__ pnorm,
                                                     int32_t* __restrict__ err) {
   const int lane = lane_id(), sub = lane % kLanesPerRow;
-  int L = fwd_off[E_loc];
-  L = L < 0 ? 0 : (L > L_cap ? L_cap : L);
+  int L = L_cap;
+  if (!kNorms) {
+    L = fwd_off[E_loc];
+    L = L < 0 ? 0 : (L > L_cap ? L_cap : L);
+  }
   const int64_t groups = ((int64_t)L + kRowsPerWave - 1) / kRowsPerWave;
   const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
   int bad = 0;
@@ -96,7 +107,7 @@ __global__ __launch_bounds__(kBlock) void row_score(const uint4* __restrict__ ph
        gi += nw) {
     const int64_t r = gi * kRowsPerWave + lane / kLanesPerRow;
     const bool live = r < L;
-    const int p = live ? row_pair[r] : 0;
+    const int p = live && !kNorms ? row_pair[r] : 0;
     const uint4* row = phi + (live ? r : 0) * chunks;
     double acc = 0.0;
     int c = sub;
@@ -112,7 +123,9 @@ __global__ __launch_bounds__(kBlock) void row_score(const uint4* __restrict__ ph
     for (; c < chunks; c += kLanesPerRow) acc = add_chunk<kBF16, false>(acc, load_nt(row + c));
 #pragma unroll
     for (int o = kLanesPerRow / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-    if (live && sub == 0) {
+    if (kNorms) {
+      if (live && sub == 0) pnorm[r] = acc;
+    } else if (live && sub == 0) {
       float out = 0.0f;
       if (p < 0 || p >= P) {
         bad |= LRM_DEVERR_INDEX;
@@ -124,6 +137,35 @@ __global__ __launch_bounds__(kBlock) void row_score(const uint4* __restrict__ ph
       }
       score[r] = out;
     }
+  }
+  if (bad) set_error(err, bad);
+}
+
+// Product of the split form: score[r] = fl32(alpha_p^2 * ||g_t||^2 * ||phi_r||^2) from the norms
+// in gnorm and pnorm, one row per thread, with the same checks and the same float64 expression as
+// row_score.
+__global__ __launch_bounds__(kBlock) void row_combine(const int32_t* __restrict__ fwd_off, int E_loc,
+                                                      int L_cap, const int32_t* __restrict__ row_pair,
+                                                      const float* __restrict__ topk_w, int k,
+                                                      int64_t P, const double* __restrict__ gnorm,
+                                                      const double* __restrict__ pnorm,
+                                                      float* __restrict__ score,
+                                                      int32_t* __restrict__ err) {
+  int L = fwd_off[E_loc];
+  L = L < 0 ? 0 : (L > L_cap ? L_cap : L);
+  int bad = 0;
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t r = (int64_t)blockIdx.x * kBlock + threadIdx.x; r < L; r += stride) {
+    const int p = row_pair[r];
+    float out = 0.0f;
+    if (p < 0 || p >= P) {
+      bad |= LRM_DEVERR_INDEX;
+    } else {
+      const double a = (double)topk_w[p];
+      out = (float)(((a * a) * gnorm[p / k]) * pnorm[r]);
+      if (!(out >= 0.0f && out <= 3.402823466e38f)) bad |= LRM_DEVERR_NONFINITE;
+    }
+    score[r] = out;
   }
   if (bad) set_error(err, bad);
 }
@@ -210,14 +252,55 @@ hipError_t launch_score(const lrm_problem& p, const float* topk_w, const void* g
   if (p.dtype == LRM_BF16) {
     hipLaunchKernelGGL((token_norm<true, false>), dim3(gblk), dim3(kBlock), 0, s, (const uint4*)g, p.T,
                        gch, gnorm);
-    hipLaunchKernelGGL(row_score<true>, dim3(lblk), dim3(kBlock), 0, s, (const uint4*)phi, pch,
-                       fwd_off, p.E_loc, p.L_cap, row_pair, topk_w, p.k, P, gnorm, score, err);
+    hipLaunchKernelGGL((row_score<true, false>), dim3(lblk), dim3(kBlock), 0, s, (const uint4*)phi,
+                       pch, fwd_off, p.E_loc, p.L_cap, row_pair, topk_w, p.k, P, gnorm, score,
+                       nullptr, err);
   } else {
     hipLaunchKernelGGL((token_norm<false, false>), dim3(gblk), dim3(kBlock), 0, s, (const uint4*)g, p.T,
                        gch, gnorm);
-    hipLaunchKernelGGL(row_score<false>, dim3(lblk), dim3(kBlock), 0, s, (const uint4*)phi, pch,
-                       fwd_off, p.E_loc, p.L_cap, row_pair, topk_w, p.k, P, gnorm, score, err);
+    hipLaunchKernelGGL((row_score<false, false>), dim3(lblk), dim3(kBlock), 0, s, (const uint4*)phi,
+                       pch, fwd_off, p.E_loc, p.L_cap, row_pair, topk_w, p.k, P, gnorm, score,
+                       nullptr, err);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_score_norms(const lrm_problem& p, const void* g, const void* phi, char* ws,
+                              const WsLayout& wl, hipStream_t s) {
+  double* gnorm = (double*)(ws + wl.gnorm);
+  double* pnorm = (double*)(ws + wl.pnorm);
+  const int esz = p.dtype == LRM_BF16 ? 2 : 4;
+  const int gch = p.h * esz / 16, pch = p.d * esz / 16;
+  const int64_t tb = ((int64_t)p.T + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t lb = ((int64_t)p.L_cap + 4 * kWavesPerBlock - 1) / (4 * kWavesPerBlock);
+  const unsigned gblk = (unsigned)(tb < 4096 ? tb : 4096);
+  const unsigned lblk = (unsigned)(lb < 4096 ? lb : 4096);
+  if (p.dtype == LRM_BF16) {
+    hipLaunchKernelGGL((token_norm<true, false>), dim3(gblk), dim3(kBlock), 0, s, (const uint4*)g, p.T,
+                       gch, gnorm);
+    hipLaunchKernelGGL((row_score<true, true>), dim3(lblk), dim3(kBlock), 0, s, (const uint4*)phi,
+                       pch, nullptr, p.E_loc, p.L_cap, nullptr, nullptr, p.k, (int64_t)0, nullptr,
+                       nullptr, pnorm, nullptr);
+  } else {
+    hipLaunchKernelGGL((token_norm<false, false>), dim3(gblk), dim3(kBlock), 0, s, (const uint4*)g, p.T,
+                       gch, gnorm);
+    hipLaunchKernelGGL((row_score<false, true>), dim3(lblk), dim3(kBlock), 0, s, (const uint4*)phi,
+                       pch, nullptr, p.E_loc, p.L_cap, nullptr, nullptr, p.k, (int64_t)0, nullptr,
+                       nullptr, pnorm, nullptr);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_score_combine(const lrm_problem& p, const float* topk_w, const int32_t* row_pair,
+                                const int32_t* fwd_off, float* score, char* ws, const WsLayout& wl,
+                                hipStream_t s) {
+  int32_t* err = (int32_t*)(ws + wl.err);
+  const double* gnorm = (const double*)(ws + wl.gnorm);
+  const double* pnorm = (const double*)(ws + wl.pnorm);
+  const int64_t lb = ((int64_t)p.L_cap + kBlock - 1) / kBlock;
+  const unsigned lblk = (unsigned)(lb < 2048 ? lb : 2048);
+  hipLaunchKernelGGL(row_combine, dim3(lblk), dim3(kBlock), 0, s, fwd_off, p.E_loc, p.L_cap,
+                     row_pair, topk_w, p.k, (int64_t)p.T * p.k, gnorm, pnorm, score, err);
   return hipGetLastError();
 }
 

@@ -18,7 +18,8 @@ LIB_PATH = os.environ.get("LRM_LIBRARY") or os.path.join(_PKG, "liblrm.so")
 LRM_F32, LRM_BF16 = 0, 1
 DEVERR = {1: "EXPERT_ID", 2: "L_CAP", 4: "K_CAP", 8: "QUOTA", 16: "NONFINITE", 32: "INDEX"}
 
-EXPORTS = ("lrm_workspace_bytes", "lrm_plan_quotas", "lrm_admit_quotas", "lrm_score", "lrm_score_criterion",
+EXPORTS = ("lrm_workspace_bytes", "lrm_plan_quotas", "lrm_admit_quotas", "lrm_score",
+           "lrm_score_norms", "lrm_score_combine", "lrm_score_criterion",
            "lrm_select", "lrm_compact", "lrm_grouped_dw", "lrm_grouped_dx", "lrm_grouped_dw_dx",
            "lrm_swiglu_backward", "lrm_gather_tokens", "lrm_grouped_fc1_dw", "lrm_grouped_fc1_dx",
            "lrm_grouped_fc1_dw_dx", "lrm_scatter_tokens", "lrm_read_device_error",
@@ -88,6 +89,8 @@ def load_library(path: Optional[str] = None):
     lib.lrm_plan_quotas.argtypes = [PP, QP] + [vp] * 7 + [sz, vp]
     lib.lrm_admit_quotas.argtypes = [PP, ctypes.POINTER(Admission)] + [vp] * 5 + [sz, vp]
     lib.lrm_score.argtypes = [PP] + [vp] * 7 + [sz, vp]
+    lib.lrm_score_norms.argtypes = [PP] + [vp] * 3 + [sz, vp]
+    lib.lrm_score_combine.argtypes = [PP] + [vp] * 5 + [sz, vp]
     lib.lrm_score_criterion.argtypes = [PP, i32] + [vp] * 8 + [sz, vp]
     lib.lrm_select.argtypes = [PP] + [vp] * 6 + [sz, vp]
     lib.lrm_compact.argtypes = [PP] + [vp] * 10 + [sz, vp]
@@ -160,6 +163,21 @@ def lrm_score(problem, topk_w, g, phi, row_pair, fwd_off, score, ws, stream=None
     _check(lib, lib.lrm_score(ctypes.byref(problem), _ptr(topk_w), _ptr(g), _ptr(phi),
                               _ptr(row_pair), _ptr(fwd_off), _ptr(score), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)), "lrm_score")
+
+
+def lrm_score_norms(problem, g, phi, ws, stream=None):
+    lib = load_library()
+    _check(lib, lib.lrm_score_norms(ctypes.byref(problem), _ptr(g), _ptr(phi), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)),
+           "lrm_score_norms")
+
+
+def lrm_score_combine(problem, topk_w, row_pair, fwd_off, score, ws, stream=None):
+    lib = load_library()
+    _check(lib, lib.lrm_score_combine(ctypes.byref(problem), _ptr(topk_w), _ptr(row_pair),
+                                      _ptr(fwd_off), _ptr(score), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)),
+           "lrm_score_combine")
 
 
 def lrm_score_criterion(problem, criterion, topk_w, g, phi, keys, row_pair, fwd_off, score, ws,

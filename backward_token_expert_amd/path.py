@@ -2,7 +2,8 @@
 
 ``DeviceBuffers`` allocates, with PyTorch, every output and the workspace of one problem; ``run``
 enqueues lrm_plan_quotas -> lrm_score (or lrm_score_criterion) -> lrm_select -> lrm_compact ->
-lrm_grouped_dw_dx (or lrm_grouped_dw -> lrm_grouped_dx) on one stream.  ``LayerBuffers`` and
+lrm_grouped_dw_dx (or lrm_grouped_dw -> lrm_grouped_dx) on one stream, or, given a second
+stream, runs lrm_score_norms there beside lrm_plan_quotas and lrm_score_combine after both.  ``LayerBuffers`` and
 ``run_layer`` do the same for the rest of the expert backward over the retained rows:
 lrm_swiglu_backward -> lrm_gather_tokens -> lrm_grouped_fc1_dw_dx (or the two FC1 calls) ->
 lrm_scatter_tokens.  No step of the path is computed here.
@@ -58,21 +59,43 @@ class DeviceBuffers:
         self.ws = torch.zeros(nws, dtype=torch.uint8, device=device)
 
 
+def _torch_stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
 def run(problem, policy, topk_idx, topk_w, g, phi, W, bufs: DeviceBuffers, stream=None,
-        criterion: str = "lrm", keys=None, fused: bool = True, admission=None):
+        criterion: str = "lrm", keys=None, fused: bool = True, admission=None, side_stream=None):
     """Enqueue the whole hot path on `stream` (default: torch's current stream).  `criterion`
     picks the selection score (lrm_score for "lrm", else lrm_score_criterion; "random" ranks by
     `keys`, one float32 per pair).  `fused` runs both GEMMs as lrm_grouped_dw_dx, else as
     lrm_grouped_dw then lrm_grouped_dx.  With an `admission` (lrm.make_admission), the quotas are
     those of the first feasible candidate (lrm_admit_quotas after lrm_plan_quotas) and
-    bufs.admitted receives its index (-1: none, every quota zero)."""
+    bufs.admitted receives its index (-1: none, every quota zero).  With a `side_stream` (LRM
+    criterion only) the score's norm pass (lrm_score_norms) runs on it, forked from and joined back
+    to `stream` with events, while lrm_plan_quotas runs on `stream`; the results are bitwise
+    those of the one-stream sequence."""
     b = bufs
+    split = criterion == "lrm" and side_stream is not None
+    if split:
+        main, side = _torch_stream(stream), _torch_stream(side_stream)
+        fork, join = torch.cuda.Event(), torch.cuda.Event()
+        fork.record(main)
+        side.wait_event(fork)
+        lrm.lrm_score_norms(problem, g, phi, b.ws, side)
+        join.record(side)
     lrm.lrm_plan_quotas(problem, policy, topk_idx, b.counts, b.fwd_off, b.row_pair, b.quota,
                         b.cmp_off, b.ws, stream)
     if admission is not None:
         lrm.lrm_admit_quotas(problem, admission, b.fwd_off, b.quota, b.cmp_off, b.admitted, b.ws,
                              stream)
-    if criterion == "lrm":
+    if split:
+        main.wait_event(join)
+        lrm.lrm_score_combine(problem, topk_w, b.row_pair, b.fwd_off, b.score, b.ws, stream)
+    elif criterion == "lrm":
         lrm.lrm_score(problem, topk_w, g, phi, b.row_pair, b.fwd_off, b.score, b.ws, stream)
     else:
         lrm.lrm_score_criterion(problem, criterion, topk_w, g, phi, keys, b.row_pair, b.fwd_off,

@@ -3,7 +3,9 @@
 
 One step = the whole path over one batch of synthetic input already resident in HBM:
 lrm_plan_quotas -> lrm_score -> lrm_select -> lrm_compact -> lrm_grouped_dw_dx (both FC2
-gradients; --separate-gemms: lrm_grouped_dw -> lrm_grouped_dx).  The rest of the expert backward
+gradients; --separate-gemms: lrm_grouped_dw -> lrm_grouped_dx).  --overlap runs the score in its
+two halves instead: lrm_score_norms on a second stream beside lrm_plan_quotas (it needs neither
+the routing nor the layout), then lrm_score_combine once both are done.  The rest of the expert backward
 over the same retained rows (activation, FC1 gradients, return to the tokens) is timed after it
 as its own leg ("layer_backward"), outside the step.
 
@@ -43,6 +45,9 @@ def parse():
                     help="quota split of the retained total")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of replays of a captured HIP graph")
+    ap.add_argument("--overlap", action="store_true",
+                    help="lrm_score_norms on a second stream beside lrm_plan_quotas, then "
+                         "lrm_score_combine, instead of lrm_score after the plan")
     ap.add_argument("--separate-gemms", action="store_true",
                     help="lrm_grouped_dw then lrm_grouped_dx instead of lrm_grouped_dw_dx")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -87,7 +92,7 @@ def algorithmic(w, oracle_like, criterion="lrm"):
     }
 
 
-def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True, graph=True):
+def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True, graph=True, overlap=False):
     import torch
     from backward_token_expert_amd import lrm, path
     from backward_token_expert_amd.path import to_device, to_host
@@ -103,15 +108,31 @@ def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True, graph=Tru
     keys = to_device(synth_keys(sp)) if criterion == "random" else None
     b = path.DeviceBuffers(P)
     stages = STAGES_FUSED if fused else STAGES_SPLIT
+    split = overlap and criterion == "lrm"
+    side = torch.cuda.Stream()
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
 
+    # With stage events (ev) the two score halves run one after the other on s, so that every
+    # stage has its own time; without, the norm half runs on the side stream beside the plan.
     def step(ev=None, s=None):
         s = torch.cuda.current_stream() if s is None else s
         if ev is not None:
             ev[0].record(s)
+        if split and ev is None:
+            fork.record(s)
+            side.wait_event(fork)
+            lrm.lrm_score_norms(P, g, ph, b.ws, side)
+            join.record(side)
         lrm.lrm_plan_quotas(P, pol, idx, b.counts, b.fwd_off, b.row_pair, b.quota, b.cmp_off, b.ws, s)
         if ev is not None:
             ev[1].record(s)
-        if criterion == "lrm":
+        if split:
+            if ev is None:
+                s.wait_event(join)
+            else:
+                lrm.lrm_score_norms(P, g, ph, b.ws, s)
+            lrm.lrm_score_combine(P, tw, b.row_pair, b.fwd_off, b.score, b.ws, s)
+        elif criterion == "lrm":
             lrm.lrm_score(P, tw, g, ph, b.row_pair, b.fwd_off, b.score, b.ws, s)
         else:
             lrm.lrm_score_criterion(P, criterion, tw, g, ph, keys, b.row_pair, b.fwd_off, b.score,
@@ -395,15 +416,17 @@ def main():
     pol = synth.policy(sp, kind=args.quota, cap=-1 if args.quota == "proportional" else None)
     crit = args.criterion
     fused = not args.separate_gemms
+    overlap = args.overlap
     ms, wall_ms, stages, info = gpu_bench(w, pol, args.steps, args.warmup, crit, fused,
-                                          not args.eager)
+                                          not args.eager, overlap)
     alg = algorithmic(w, info, crit)
     L, K = info["L"], info["K"]
     # rho = 1 (full retention) on the same input
     n1 = max(3, args.steps // 2) if args.rho1_steps is None else args.rho1_steps
     if n1 > 0:
         pol_full = synth.policy(sp, full=True)
-        ms1, _, stages1, info1 = gpu_bench(w, pol_full, n1, 2, crit, fused, not args.eager)
+        ms1, _, stages1, info1 = gpu_bench(w, pol_full, n1, 2, crit, fused, not args.eager,
+                                           overlap)
         alg1 = algorithmic(w, info1, crit)
 
     def fractions(st, a, dtype):
@@ -446,6 +469,9 @@ def main():
                      "traffic": recorded_traffic(dom_call, sp.name)},
         "retained_rows_per_s": K / (ms * 1e-3),
         "timing": "eager launches" if args.eager else "replays of one captured HIP graph",
+        "overlap": ("lrm_score_norms on a second stream beside lrm_plan_quotas; stage times from "
+                    "eager steps with the two halves in sequence") if overlap and crit == "lrm"
+                   else None,
         "wall_ms_per_step": wall_ms,
         "stages_ms": stages,
         "fractions": fractions(stages, alg, sp.dtype),

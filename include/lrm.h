@@ -12,6 +12,8 @@
  *                    formula")
  *   lrm_score        Load Recalibration Metric R_u = alpha_u^2 ||g_t||^2 ||phi_u||^2
  *                    (Sec. 3.2, Prop. 3.1, Eq. (3); Algorithm 1 step 13)
+ *   lrm_score_norms / lrm_score_combine  the same in two halves: the norms need neither the
+ *                    routing nor the layout, so they can run beside lrm_plan_quotas
  *   lrm_score_criterion  the same or one of the ablation criteria of Table 2
  *   lrm_select       per-expert TopK(q_e) (Algorithm 1 step 14; Sec. 3.3; Appendix 7.2 Prop. 7.1)
  *   lrm_compact      physical compaction into contiguous expert-major segments
@@ -225,6 +227,33 @@ lrm_status lrm_admit_quotas(const lrm_problem* problem, const lrm_admission* adm
 lrm_status lrm_score(const lrm_problem* problem, const float* topk_w, const void* g,
                      const void* phi, const int32_t* row_pair, const int32_t* fwd_off,
                      float* score, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * lrm_score in two halves (LRMoE Sec. 3.2, Eq. (3): R_u factors into alpha_u^2, a norm of the
+ * token's upstream gradient and a norm of the pair's saved activation; neither norm depends on
+ * the routing counts, the quotas or the layout).
+ *
+ * lrm_score_norms writes ||g_t||^2 of every token t < T and ||phi_r||^2 of every row r < L_cap
+ * (float64, the same fixed-order sums as lrm_score) into the workspace's norm region.  It reads
+ * only g and phi -- rows of phi at or past L may hold anything; their norms are never used -- and
+ * writes nothing but that region, which no other call writes, so it may run on another stream
+ * at the same time as lrm_plan_quotas (or lrm_admit_quotas) on the same workspace; the caller
+ * orders it (an event) before lrm_score_combine.  It sets no device error bits.
+ *  in : g [T][h]; phi [L_cap][d]
+ *
+ * lrm_score_combine then writes score[r] = fl32(alpha_p^2 * ||g_t||^2 * ||phi_r||^2) for every
+ * r < L (p = row_pair[r], t = p / k), from the norms the last lrm_score_norms on this workspace
+ * left.  Scores are bitwise equal to lrm_score's on the same inputs.
+ *  in : topk_w float32 [T*k]; row_pair int32 [L_cap]; fwd_off int32 [E_loc+1] (only fwd_off[E_loc])
+ *  out: score float32 [L_cap] (first L written)
+ * Row pairs outside [0, T*k) set LRM_DEVERR_INDEX (score 0); non-finite or negative results set
+ * LRM_DEVERR_NONFINITE.
+ */
+lrm_status lrm_score_norms(const lrm_problem* problem, const void* g, const void* phi, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+lrm_status lrm_score_combine(const lrm_problem* problem, const float* topk_w,
+                             const int32_t* row_pair, const int32_t* fwd_off, float* score,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Selection criteria (LRMoE Table 2 and Sec. 4.7 ablation).  The LRM criterion is lrm_score; the

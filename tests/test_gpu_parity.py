@@ -26,14 +26,17 @@ def _torch():
     return torch
 
 
-def run_gpu(w, pol, K_cap=None):
+def run_gpu(w, pol, K_cap=None, overlap=False):
+    """The path as bench.py runs it by default, on one stream (overlap=True: the score's norm half
+    on a second stream beside the plan, as bench.py --overlap)."""
     torch = _torch()
     from backward_token_expert_amd import lrm, path
     P = C.problem(w.spec, K_cap)
     bufs = path.DeviceBuffers(P)
     inp = C.upload(w)
+    side = torch.cuda.Stream() if overlap else None
     path.run(P, C.policy_obj(pol), inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"], inp["W"],
-             bufs)
+             bufs, side_stream=side)
     torch.cuda.synchronize()
     err = lrm.lrm_read_device_error(bufs.ws)
     return P, bufs, inp, err
@@ -341,6 +344,63 @@ def test_single_local_expert_and_no_local_pairs():
     assert g["fwd_off"][-1] == 0 and not g["dW"].any()
 
 
+def test_plan_with_wide_tables():
+    # 4096 experts (the per-chunk table is 4097 columns wide, more than a workgroup's threads),
+    # 1024 of them local (one summing thread per local expert), 21 chunks of pairs (a full and a
+    # partial placing workgroup)
+    rng = np.random.default_rng(21)
+    T, k = 10390, 2
+    rows = np.stack([rng.choice(4096, k, replace=False) for _ in range(T)])
+    w = custom(rows, E=4096, e_lo=2000, E_loc=1024, h=64, d=64, dtype="bf16")
+    print("[case] E=4096, E_loc=1024, 21 chunks", flush=True)
+    for pol in ({"full": 0, "rho_num": 1, "rho_den": 2, "cap_abs": -1},
+                {"full": 0, "rho_num": 1, "rho_den": 2, "cap_abs": -1, "kind": "waterfill"}):
+        full_compare(w, pol)
+
+
+def test_row_and_retained_capacities_truncate_and_flag():
+    # L > L_cap and K > K_cap: the forward segments end at L_cap, the quotas are those of the
+    # truncated segments, the compacted ones end at K_cap, and both capacity bits are set
+    torch = _torch()
+    from backward_token_expert_amd import lrm, path
+    w = C.workload(1, T=1024)
+    sp = w.spec
+    pol = synth.policy(sp)
+    L_cap, K_cap = 5000, 500          # truncated segments 1024, 1015, 971, 875, 791, 324, 0, ...
+    assert w.L > L_cap                # keep 156 each under rho = 1/2: K = 936 > K_cap
+    P = lrm.make_problem(sp.T, sp.k, sp.E, sp.e_lo, sp.E_loc, sp.h, sp.d, sp.dtype, L_cap, K_cap)
+    b = path.DeviceBuffers(P)
+    inp = C.upload(w)
+    print(f"[case] L={w.L} > L_cap={L_cap}, K_cap={K_cap}", flush=True)
+    path.run(P, C.policy_obj(pol), inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"], inp["W"],
+             b)
+    torch.cuda.synchronize()
+    err = lrm.lrm_read_device_error(b.ws)
+    assert err == lrm_bits("L_CAP", "K_CAP"), lrm.deverr_names(err)
+    from backward_token_expert_amd.path import to_host
+    counts = O.routed_counts(w.topk_idx, sp.E)
+    row_pair, fwd = O.forward_layout(w.topk_idx, sp.e_lo, sp.E_loc)
+    fwd_c = np.minimum(fwd, L_cap)
+    q = O.plan_quotas(np.diff(fwd_c), pol)[0]
+    pre = np.concatenate([[0], np.cumsum(q)])
+    o0 = np.minimum(pre[:-1], K_cap)
+    o1 = np.minimum(pre[1:], K_cap)
+    np.testing.assert_array_equal(to_host(b.counts), counts)
+    np.testing.assert_array_equal(to_host(b.fwd_off), fwd_c)
+    np.testing.assert_array_equal(to_host(b.row_pair)[:L_cap], row_pair[:L_cap])
+    np.testing.assert_array_equal(to_host(b.quota), o1 - o0)
+    np.testing.assert_array_equal(to_host(b.cmp_off), np.concatenate([o0, [min(pre[-1], K_cap)]]))
+    # the kept rows: each truncated segment's own top quota, from the GPU's float32 scores
+    score = to_host(b.score)[:L_cap]
+    want = O.select_top_quota(score, fwd_c, o1 - o0, row_pair[:L_cap])
+    np.testing.assert_array_equal(to_host(b.sel_row)[:K_cap], want)
+
+
+def lrm_bits(*names):
+    from backward_token_expert_amd import lrm
+    return sum(bit for bit, n in lrm.DEVERR.items() if n in names)
+
+
 def test_all_equal_scores_keep_first_rows():
     T = 500
     rows = np.zeros((T, 1), np.int32)
@@ -581,6 +641,65 @@ def test_bitwise_determinism_and_graph_replay():
         got = host(b, sp)
         for key in got:
             assert got[key].tobytes() == outs[0][key].tobytes(), (rep, key)
+
+
+def test_score_halves_on_a_side_stream():
+    """lrm_score_norms on a second stream beside lrm_plan_quotas, then lrm_score_combine, gives
+    every output of the one-stream sequence bit for bit; phi rows past L (NaN here) reach no score
+    and set no error; the forked sequence captures into one HIP graph whose replays (with eager
+    work between them) equal the eager result."""
+    torch = _torch()
+    from backward_token_expert_amd import lrm, path
+    w = C.workload(3, T=2048)          # extreme skew: empty experts, L well below L_cap
+    sp = w.spec
+    pol = C.policy_obj(synth.policy(sp))
+    P = C.problem(sp)
+    inp = dict(C.upload(w))
+    L = w.phi.shape[0]
+    assert L < P.L_cap
+    nan = 0x7FC0 if sp.dtype == "bf16" else float("nan")
+    inp["phi"][L:] = nan
+    args = (P, pol, inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"], inp["W"])
+    ref = path.DeviceBuffers(P)
+    path.run(*args, ref)
+    torch.cuda.synchronize()
+    assert lrm.lrm_read_device_error(ref.ws) == 0
+    want = host(ref, sp)
+    side = torch.cuda.Stream()
+    b = path.DeviceBuffers(P)
+    path.run(*args, b, side_stream=side)
+    torch.cuda.synchronize()
+    assert lrm.lrm_read_device_error(b.ws) == 0
+    got = host(b, sp)
+    for key in want:
+        assert got[key].tobytes() == want[key].tobytes(), key
+    # the two halves back to back on one stream
+    b.score.fill_(-1.0)
+    lrm.lrm_score_norms(P, inp["g"], inp["phi"], b.ws)
+    lrm.lrm_score_combine(P, inp["topk_w"], b.row_pair, b.fwd_off, b.score, b.ws)
+    torch.cuda.synchronize()
+    assert host(b, sp)["score"].tobytes() == want["score"].tobytes()
+    # the forked sequence in one graph
+    g = path.DeviceBuffers(P)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        path.run(*args, g, s, side_stream=side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            path.run(*args, g, s, side_stream=side)
+    for rep in range(3):
+        g.score.fill_(-1.0)
+        g.dW.fill_(7.0)
+        g.sel_row.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host(g, sp)
+        for key in got:
+            assert got[key].tobytes() == want[key].tobytes(), (rep, key)
+        assert lrm.lrm_read_device_error(g.ws) == 0
 
 
 # ------------------------------------------------------------------------------------------------

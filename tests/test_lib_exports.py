@@ -33,6 +33,14 @@ def test_library_exports_every_declared_symbol():
     assert set(_declared()) <= set(lrm.EXPORTS)
 
 
+def test_binding_types_every_argument():
+    # ctypes passes an untyped Python int as a 32-bit int: every call needs its argument types so
+    # that device pointers, sizes and stream handles keep their 64 bits
+    lib = bte.load_library()
+    for name in lrm.EXPORTS:
+        assert getattr(lib, name).argtypes is not None, name
+
+
 def test_workspace_bytes_and_validation_on_host():
     lib = bte.load_library()
     p = bte.make_problem(32768, 8, 128, 0, 16, 2048, 768, "bf16", 262144, 262144)
@@ -73,6 +81,12 @@ def test_workspace_bytes_and_validation_on_host():
     assert sc(P, 1, None, None, None, None, fake, fake, fake, fake, n, None) == 1   # no g
     assert sc(P, 2, None, fake + 2, None, None, fake, fake, fake, fake, n, None) == 2
     assert sc(P, 0, None, fake, fake, None, fake, fake, fake, fake, n, None) == 1   # LRM: no topk_w
+    # the score in two halves: a NULL input, a misaligned phi, a short workspace
+    assert lib.lrm_score_norms(P, None, fake, fake, n, None) == 1
+    assert lib.lrm_score_norms(P, fake, fake + 8, fake, n, None) == 2
+    assert lib.lrm_score_norms(P, fake, fake, fake, 1024, None) == 3
+    assert lib.lrm_score_combine(P, fake, None, fake, fake, fake, n, None) == 1
+    assert lib.lrm_score_combine(P, fake, fake, fake, fake, fake, 1024, None) == 3
     assert lib.lrm_status_string(3) == b"workspace too small"
 
 
