@@ -11,10 +11,13 @@
 //   2. MSB-first radix select over bits 30..0 in digits of 12, 10 and 9 bits finds the q-th
 //      largest key T and how many keys equal to T must be kept; after the first digit the keys
 //      still in play are gathered into a short list that the later digits scan;
-//   3. each wavefront owns a contiguous run of rows: it counts its keys > T and == T, one
-//      barrier publishes the counts, and each wavefront then writes its kept rows (key > T, or
-//      key == T among the first `need` tied rows) in row order with ballot prefix sums.
-// Segments longer than the LDS stage are read from global memory in every pass instead.
+//   3. each wavefront owns a contiguous run of rows: it compacts its rows with key >= T, in row
+//      order and marking the ties, into the front of its own run of the LDS stage; one barrier
+//      publishes the counts, and each wavefront then writes its kept rows (key > T, or key == T
+//      among the first `need` tied rows of the segment) from that short list with ballot prefix
+//      sums, so the stores cover consecutive lanes.
+// Segments longer than the LDS stage are read from global memory in every pass instead, and
+// their output pass counts first and then writes from the keys themselves.
 #include "lrm_device.hpp"
 #include "lrm_internal.hpp"
 
@@ -28,6 +31,7 @@ constexpr int kMaxBins = 4096;    // first radix digit: 12 bits
 constexpr int kCandBase = 1024;   // candidate list: histogram words past the later digits' bins
 constexpr int kMaxCand = kMaxBins - kCandBase;
 constexpr int kBatch = 8;         // keys a thread loads before using them (strided passes)
+constexpr int kStageBatch = 32;   // keys a thread loads before staging them (one pass for 32768)
 constexpr int kOutBatch = 4;      // 64-key groups a wavefront loads ahead in the output pass
 
 struct SelectSmem {
@@ -55,18 +59,18 @@ __device__ __forceinline__ void select_segment(SelectSmem& sm, const uint32_t* _
   if (tid == 0) sm.ncand = 0;
   __syncthreads();
 
-  // Stage the keys in LDS and count the first radix digit (bits 30..19) on the way, kBatch
+  // Stage the keys in LDS and count the first radix digit (bits 30..19) on the way, kStageBatch
   // independent loads in flight per thread.
   bool bad = false;
-  for (int base = 0; base < n; base += kBatch * kThreads) {
-    uint32_t v[kBatch];
+  for (int base = 0; base < n; base += kStageBatch * kThreads) {
+    uint32_t v[kStageBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
+    for (int j = 0; j < kStageBatch; ++j) {
       const int i = base + j * kThreads + tid;
       v[j] = i < n ? src[i] : 0u;
     }
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
+    for (int j = 0; j < kStageBatch; ++j) {
       const int i = base + j * kThreads + tid;
       if (i < n) {
         bad |= v[j] > 0x7F800000u;
@@ -178,30 +182,57 @@ __device__ __forceinline__ void select_segment(SelectSmem& sm, const uint32_t* _
   const uint32_t thr = prefix;
   const int need = rank;  // keys equal to thr that are kept, first in row order
 
-  // Ordered output: wavefront w owns the contiguous rows [w*chunk, (w+1)*chunk).  One pass counts
-  // each wave's keys above and equal to thr; after one barrier every wave knows how many rows the
-  // waves before it keep and how many tied keys they hold, and writes its kept rows in row order
-  // with ballot prefix sums (no further barriers).
+  // Ordered output: wavefront w owns the contiguous rows [w*chunk, (w+1)*chunk).  After one
+  // barrier every wave knows how many rows the waves before it keep and how many tied keys they
+  // hold, and writes its kept rows in row order with ballot prefix sums (no further barriers).
   const int chunk = ((n + kWaves - 1) / kWaves + kWave - 1) / kWave * kWave;
   const int c0 = w * chunk < n ? w * chunk : n;
   const int c1 = c0 + chunk < n ? c0 + chunk : n;
   int n_eq = 0, n_gt = 0;
-  for (int base = c0; base < c1; base += kOutBatch * kWave) {
-    uint32_t v[kOutBatch];
+  if constexpr (kStaged) {
+    // Compact the rows with key >= thr, in row order, into the front of this wave's own run of
+    // the stage: offset i, bit 31 set for a tie.  A slot rewritten lies at or before the group
+    // being read, whose keys are already in registers; later groups are untouched.
+    for (int base = c0; base < c1; base += kOutBatch * kWave) {
+      uint32_t v[kOutBatch];
 #pragma unroll
-    for (int u = 0; u < kOutBatch; ++u) {
-      const int i = base + u * kWave + lane;
-      v[u] = i < c1 ? key_at(i) : 0u;
-    }
+      for (int u = 0; u < kOutBatch; ++u) {
+        const int i = base + u * kWave + lane;
+        v[u] = i < c1 ? sm.keys[i] : 0u;
+      }
 #pragma unroll
-    for (int u = 0; u < kOutBatch; ++u) {
-      const bool valid = base + u * kWave + lane < c1;
-      n_eq += valid && v[u] == thr;
-      n_gt += valid && v[u] > thr;
+      for (int u = 0; u < kOutBatch; ++u) {
+        const int i = base + u * kWave + lane;
+        const bool valid = i < c1;
+        const bool is_eq = valid && v[u] == thr;
+        const bool cand = is_eq || (valid && v[u] > thr);
+        const uint64_t bc = ballot(cand);
+        if (cand)
+          sm.keys[c0 + n_gt + n_eq + __builtin_popcountll(bc & lt)] =
+              (uint32_t)i | (is_eq ? 0x80000000u : 0u);
+        const int ne = __builtin_popcountll(ballot(is_eq));
+        n_eq += ne;
+        n_gt += __builtin_popcountll(bc) - ne;
+      }
     }
+  } else {
+    for (int base = c0; base < c1; base += kOutBatch * kWave) {
+      uint32_t v[kOutBatch];
+#pragma unroll
+      for (int u = 0; u < kOutBatch; ++u) {
+        const int i = base + u * kWave + lane;
+        v[u] = i < c1 ? key_at(i) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kOutBatch; ++u) {
+        const bool valid = base + u * kWave + lane < c1;
+        n_eq += valid && v[u] == thr;
+        n_gt += valid && v[u] > thr;
+      }
+    }
+    n_eq = wave_sum_int(n_eq);
+    n_gt = wave_sum_int(n_gt);
   }
-  n_eq = wave_sum_int(n_eq);
-  n_gt = wave_sum_int(n_gt);
   if (lane == 0) {
     sm.weq[w] = n_eq;
     sm.wkeep[w] = n_gt;
@@ -215,26 +246,46 @@ __device__ __forceinline__ void select_segment(SelectSmem& sm, const uint32_t* _
     pos += sm.wkeep[x] + tied;
     eq_before += e_x;
   }
-  for (int base = c0; base < c1; base += kOutBatch * kWave) {
-    uint32_t v[kOutBatch];
-#pragma unroll
-    for (int u = 0; u < kOutBatch; ++u) {
-      const int i = base + u * kWave + lane;
-      v[u] = i < c1 ? key_at(i) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < kOutBatch; ++u) {
-      const int i = base + u * kWave + lane;
-      const bool valid = i < c1;
-      const bool is_eq = valid && v[u] == thr;
-      const uint64_t beq = ballot(is_eq);
-      const bool keep =
-          (valid && v[u] > thr) || (is_eq && eq_before + __builtin_popcountll(beq & lt) < need);
+  if constexpr (kStaged) {
+    // This wave keeps its first t_w ties; its list holds n_gt + n_eq entries in row order.
+    int t_w = need - eq_before;
+    t_w = t_w < 0 ? 0 : (t_w > n_eq ? n_eq : t_w);
+    const int m = n_gt + n_eq;
+    int ties = 0;
+    for (int j = 0; j < m; j += kWave) {
+      const bool valid = j + lane < m;
+      const uint32_t x = valid ? sm.keys[c0 + j + lane] : 0u;
+      const bool tie = valid && (x >> 31);
+      const uint64_t bt = ballot(tie);
+      const bool keep = valid && (!tie || ties + __builtin_popcountll(bt & lt) < t_w);
       const uint64_t bk = ballot(keep);
       const int at = pos + __builtin_popcountll(bk & lt);
-      if (keep && at < q) sel_row[o0 + at] = r0 + i;
+      if (keep && at < q) sel_row[o0 + at] = r0 + (int)(x & 0x7FFFFFFFu);
       pos += __builtin_popcountll(bk);
-      eq_before += __builtin_popcountll(beq);
+      ties += __builtin_popcountll(bt);
+    }
+  } else {
+    for (int base = c0; base < c1; base += kOutBatch * kWave) {
+      uint32_t v[kOutBatch];
+#pragma unroll
+      for (int u = 0; u < kOutBatch; ++u) {
+        const int i = base + u * kWave + lane;
+        v[u] = i < c1 ? key_at(i) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kOutBatch; ++u) {
+        const int i = base + u * kWave + lane;
+        const bool valid = i < c1;
+        const bool is_eq = valid && v[u] == thr;
+        const uint64_t beq = ballot(is_eq);
+        const bool keep =
+            (valid && v[u] > thr) || (is_eq && eq_before + __builtin_popcountll(beq & lt) < need);
+        const uint64_t bk = ballot(keep);
+        const int at = pos + __builtin_popcountll(bk & lt);
+        if (keep && at < q) sel_row[o0 + at] = r0 + i;
+        pos += __builtin_popcountll(bk);
+        eq_before += __builtin_popcountll(beq);
+      }
     }
   }
 }
