@@ -199,6 +199,17 @@ __global__ __launch_bounds__(kPlaceThreads) void plan_place(
     for (int i = tid; i < cols; i += kPlaceThreads) sm.cnt[i] = 0;
   __syncthreads();
 
+  // A placing wave's own chunk of expert ids, loaded first so the memory round trip overlaps the
+  // table sums below.
+  const int64_t c = c_first + w;
+  const int64_t p0 = c * kPlanChunk;
+  int ev[kHistBatch];
+#pragma unroll
+  for (int u = 0; u < kHistBatch; ++u) {
+    const int64_t p = p0 + u * kWave + lane;
+    ev[u] = !quota_wg && c < nchunks && p < P ? idx[p] : -1;
+  }
+
   int nbad = 0;
   if (quota_wg) {
     // Every column's total: thread (rg, cc) sums rows rg, rg + R, ... of columns cc, cc + C0, ...
@@ -296,16 +307,8 @@ __global__ __launch_bounds__(kPlaceThreads) void plan_place(
     sm.tot[tid] = f1;
   }
   __syncthreads();
-  const int64_t c = c_first + w;
   if (c >= nchunks) return;  // no barrier follows
   const uint64_t lt = lanemask_lt();
-  const int64_t p0 = c * kPlanChunk;
-  int ev[kHistBatch];
-#pragma unroll
-  for (int u = 0; u < kHistBatch; ++u) {
-    const int64_t p = p0 + u * kWave + lane;
-    ev[u] = p < P ? idx[p] : -1;
-  }
 #pragma unroll
   for (int u = 0; u < kHistBatch; ++u) {
     const int64_t p = p0 + u * kWave + lane;

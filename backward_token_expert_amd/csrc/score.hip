@@ -108,6 +108,10 @@ __global__ __launch_bounds__(kBlock) void row_score(const uint4* __restrict__ ph
     const int64_t r = gi * kRowsPerWave + lane / kLanesPerRow;
     const bool live = r < L;
     const int p = live && !kNorms ? row_pair[r] : 0;
+    // The row's routing weight and token norm are fetched while its phi chunks stream in.
+    const bool pair_ok = live && !kNorms && p >= 0 && p < P;
+    const float alpha = pair_ok ? topk_w[p] : 0.0f;
+    const double gn = pair_ok ? gnorm[p / k] : 0.0;
     const uint4* row = phi + (live ? r : 0) * chunks;
     double acc = 0.0;
     int c = sub;
@@ -127,11 +131,11 @@ __global__ __launch_bounds__(kBlock) void row_score(const uint4* __restrict__ ph
       if (live && sub == 0) pnorm[r] = acc;
     } else if (live && sub == 0) {
       float out = 0.0f;
-      if (p < 0 || p >= P) {
+      if (!pair_ok) {
         bad |= LRM_DEVERR_INDEX;
       } else {
-        const double a = (double)topk_w[p];
-        out = (float)(((a * a) * gnorm[p / k]) * acc);
+        const double a = (double)alpha;
+        out = (float)(((a * a) * gn) * acc);
         // Scores are products of squares: anything but a finite value >= +0 is an input error.
         if (!(out >= 0.0f && out <= 3.402823466e38f)) bad |= LRM_DEVERR_NONFINITE;
       }
