@@ -31,8 +31,9 @@ constexpr int kQueueWord = 8;
 // Layout of the caller-provided workspace (byte offsets, all 256-byte aligned).
 struct WsLayout {
   size_t err;     // int32 error word; words kQueueWord.. hold the fused GEMM's unit counters
-  size_t hist;    // int32 [nchunks][E+1] per-chunk expert histograms / local prefixes; column E
-                  //                      counts expert ids outside [0, E)
+  size_t hist;     // int32 [nchunks][E_loc] per-chunk counts of the local experts
+  size_t hist_all; // int32 [ceil(nchunks/4)][E+1] per 4 chunks, counts of every expert; column E
+                   //                      counts expert ids outside [0, E)
   size_t gnorm;   // double [T]           ||g_t||^2
   size_t pnorm;   // double [L_cap]       ||phi_r||^2 of the split score (lrm_score_norms)
   size_t tiles;   // int32 [1 + 2*max_tiles] dx tile table: count, then (expert, row0) pairs
@@ -55,7 +56,9 @@ inline WsLayout ws_layout(const lrm_problem& p) {
   w.err = off;
   off += 256;
   w.hist = off;
-  off = align_up(off + (size_t)w.nchunks * (p.E + 1) * 4, 256);
+  off = align_up(off + (size_t)w.nchunks * p.E_loc * 4, 256);
+  w.hist_all = off;
+  off = align_up(off + (size_t)((w.nchunks + 3) / 4) * (p.E + 1) * 4, 256);
   w.gnorm = off;
   off = align_up(off + (size_t)p.T * 8, 256);
   w.pnorm = off;

@@ -7,8 +7,9 @@
 //
 // Two launches, all sizes device-resident (no host round trip, as the TopoEP paper argues for
 // planning in its host-plan latency model):
-//   plan_hist    one wavefront per chunk of kPlanChunk pairs: per-chunk expert histogram, plus a
-//                column counting expert ids outside [0, E)
+//   plan_hist    one wavefront per chunk of kPlanChunk pairs: the chunk's counts of the local
+//                experts, and per workgroup of 4 chunks the counts of every expert plus a column
+//                counting expert ids outside [0, E)
 //   plan_place   1024-thread workgroups.  Each placing workgroup owns 16 consecutive chunks (one
 //                per wavefront): it sums the local experts' columns of the histogram table itself
 //                -- the totals, and the pairs in the chunks before its own -- so no workgroup
@@ -28,14 +29,18 @@ namespace {
 
 constexpr int kPlanBlock = 256;                 // 4 wavefronts, one chunk each
 constexpr int kChunksPerBlock = kPlanBlock / kWave;
+static_assert(kChunksPerBlock == 4, "ws_layout sizes hist_all for 4 chunks per row");
 constexpr int kMaxE = 4096;
 
 constexpr int kHistBatch = 16;  // index loads a lane issues before using them (a whole chunk)
 static_assert(kPlanChunk == kHistBatch * kWave, "one load batch per chunk");
 
+// hist_loc [nchunks][E_loc]: per chunk, its pairs of each local expert.
+// hist_all [nblocks][E+1]: per workgroup of kChunksPerBlock chunks, its pairs of each expert.
 __global__ __launch_bounds__(kPlanBlock) void plan_hist(const int32_t* __restrict__ idx, int64_t P,
-                                                        int E, int64_t nchunks,
-                                                        int32_t* __restrict__ hist) {
+                                                        int E, int e_lo, int E_loc, int64_t nchunks,
+                                                        int32_t* __restrict__ hist_loc,
+                                                        int32_t* __restrict__ hist_all) {
   __shared__ int32_t h[kChunksPerBlock][kMaxE + 1];
   const int w = threadIdx.x / kWave, lane = lane_id();
   const int cols = E + 1;  // column E counts expert ids outside [0, E)
@@ -59,9 +64,15 @@ __global__ __launch_bounds__(kPlanBlock) void plan_hist(const int32_t* __restric
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < kChunksPerBlock * cols; i += kPlanBlock) {
-    const int64_t cc = (int64_t)blockIdx.x * kChunksPerBlock + i / cols;
-    if (cc < nchunks) hist[cc * cols + i % cols] = h[i / cols][i % cols];
+  for (int i = threadIdx.x; i < kChunksPerBlock * E_loc; i += kPlanBlock) {
+    const int64_t cc = (int64_t)blockIdx.x * kChunksPerBlock + i / E_loc;
+    if (cc < nchunks) hist_loc[cc * E_loc + i % E_loc] = h[i / E_loc][e_lo + i % E_loc];
+  }
+  for (int i = threadIdx.x; i < cols; i += kPlanBlock) {
+    int t = 0;
+#pragma unroll
+    for (int x = 0; x < kChunksPerBlock; ++x) t += h[x][i];  // rows of absent chunks stay zero
+    hist_all[(int64_t)blockIdx.x * cols + i] = t;
   }
 }
 
@@ -183,7 +194,8 @@ struct PlaceSmem {
 
 __global__ __launch_bounds__(kPlaceThreads) void plan_place(
     const int32_t* __restrict__ idx, int64_t P, int E, int e_lo, int E_loc, int nbits,
-    int64_t nchunks, const int32_t* __restrict__ hist, int L_cap, int K_cap, lrm_quota_policy pol,
+    int64_t nchunks, const int32_t* __restrict__ hist_loc, const int32_t* __restrict__ hist_all,
+    int L_cap, int K_cap, lrm_quota_policy pol,
     int32_t* __restrict__ counts, int32_t* __restrict__ fwd_off, int32_t* __restrict__ row_pair,
     int32_t* __restrict__ quota, int32_t* __restrict__ cmp_off, int32_t* __restrict__ err) {
   __shared__ PlaceSmem sm;
@@ -212,19 +224,20 @@ __global__ __launch_bounds__(kPlaceThreads) void plan_place(
 
   int nbad = 0;
   if (quota_wg) {
-    // Every column's total: thread (rg, cc) sums rows rg, rg + R, ... of columns cc, cc + C0, ...
-    // (consecutive threads read consecutive columns of a row).
+    // Every column's total over the per-workgroup rows: thread (rg, cc) sums rows rg, rg + R, ...
+    // of columns cc, cc + C0, ... (consecutive threads read consecutive columns of a row).
+    const int64_t nrows = (nchunks + kChunksPerBlock - 1) / kChunksPerBlock;
     const int C0 = cols < kPlaceThreads ? cols : kPlaceThreads, R = kPlaceThreads / C0;
     const int rg = tid / C0, cc = tid % C0;
     if (rg < R)
       for (int c = cc; c < cols; c += C0) {
         int sum = 0;
-        for (int64_t r0 = rg; r0 < nchunks; r0 += (int64_t)R * kSumBatch) {
+        for (int64_t r0 = rg; r0 < nrows; r0 += (int64_t)R * kSumBatch) {
           int v[kSumBatch];
 #pragma unroll
           for (int u = 0; u < kSumBatch; ++u) {
             const int64_t r = r0 + (int64_t)u * R;
-            v[u] = r < nchunks ? hist[r * cols + c] : 0;
+            v[u] = r < nrows ? hist_all[r * cols + c] : 0;
           }
 #pragma unroll
           for (int u = 0; u < kSumBatch; ++u) sum += v[u];
@@ -247,7 +260,7 @@ __global__ __launch_bounds__(kPlaceThreads) void plan_place(
 #pragma unroll
         for (int u = 0; u < kSumBatch; ++u) {
           const int64_t c = c0 + (int64_t)u * J;
-          v[u] = c < nchunks ? hist[c * cols + e_lo + el] : 0;
+          v[u] = c < nchunks ? hist_loc[c * E_loc + el] : 0;
         }
 #pragma unroll
         for (int u = 0; u < kSumBatch; ++u) {
@@ -391,16 +404,18 @@ hipError_t launch_plan(const lrm_problem& p, const lrm_quota_policy& pol, const 
                        int32_t* counts, int32_t* fwd_off, int32_t* row_pair, int32_t* quota,
                        int32_t* cmp_off, char* ws, const WsLayout& wl, hipStream_t s) {
   int32_t* err = (int32_t*)(ws + wl.err);
-  int32_t* hist = (int32_t*)(ws + wl.hist);
+  int32_t* hist_loc = (int32_t*)(ws + wl.hist);
+  int32_t* hist_all = (int32_t*)(ws + wl.hist_all);
   const int64_t P = (int64_t)p.T * p.k;
   const unsigned nblk = (unsigned)((wl.nchunks + kChunksPerBlock - 1) / kChunksPerBlock);
   int nbits = 0;
   while ((1 << nbits) < p.E_loc) ++nbits;
   const unsigned nplace = (unsigned)((wl.nchunks + kPlaceWaves - 1) / kPlaceWaves);
-  hipLaunchKernelGGL(plan_hist, dim3(nblk), dim3(kPlanBlock), 0, s, topk_idx, P, p.E, wl.nchunks,
-                     hist);
+  hipLaunchKernelGGL(plan_hist, dim3(nblk), dim3(kPlanBlock), 0, s, topk_idx, P, p.E, p.e_lo,
+                     p.E_loc, wl.nchunks, hist_loc, hist_all);
   hipLaunchKernelGGL(plan_place, dim3(nplace + 1), dim3(kPlaceThreads), 0, s, topk_idx, P, p.E,
-                     p.e_lo, p.E_loc, nbits, wl.nchunks, hist, p.L_cap, p.K_cap, pol, counts,
+                     p.e_lo, p.E_loc, nbits, wl.nchunks, hist_loc, hist_all, p.L_cap, p.K_cap, pol,
+                     counts,
                      fwd_off, row_pair, quota, cmp_off, err);
   return hipGetLastError();
 }
