@@ -230,19 +230,19 @@ __global__ __launch_bounds__(kPlaceThreads) void plan_place(
     const int C0 = cols < kPlaceThreads ? cols : kPlaceThreads, R = kPlaceThreads / C0;
     const int rg = tid / C0, cc = tid % C0;
     if (rg < R)
-      for (int c = cc; c < cols; c += C0) {
+      for (int col = cc; col < cols; col += C0) {
         int sum = 0;
         for (int64_t r0 = rg; r0 < nrows; r0 += (int64_t)R * kSumBatch) {
           int v[kSumBatch];
 #pragma unroll
           for (int u = 0; u < kSumBatch; ++u) {
             const int64_t r = r0 + (int64_t)u * R;
-            v[u] = r < nrows ? hist_all[r * cols + c] : 0;
+            v[u] = r < nrows ? hist_all[r * cols + col] : 0;
           }
 #pragma unroll
           for (int u = 0; u < kSumBatch; ++u) sum += v[u];
         }
-        if (sum != 0) atomicAdd(&sm.cnt[c], sum);
+        if (sum != 0) atomicAdd(&sm.cnt[col], sum);
       }
     __syncthreads();
     for (int e = tid; e < E; e += kPlaceThreads) counts[e] = sm.cnt[e];
@@ -259,18 +259,18 @@ __global__ __launch_bounds__(kPlaceThreads) void plan_place(
         int v[kSumBatch];
 #pragma unroll
         for (int u = 0; u < kSumBatch; ++u) {
-          const int64_t c = c0 + (int64_t)u * J;
-          v[u] = c < nchunks ? hist_loc[c * E_loc + el] : 0;
+          const int64_t ch = c0 + (int64_t)u * J;
+          v[u] = ch < nchunks ? hist_loc[ch * E_loc + el] : 0;
         }
 #pragma unroll
         for (int u = 0; u < kSumBatch; ++u) {
-          const int64_t c = c0 + (int64_t)u * J;
-          if (c >= nchunks) continue;
+          const int64_t ch = c0 + (int64_t)u * J;
+          if (ch >= nchunks) continue;
           t_sum += v[u];
-          if (c < c_first)
+          if (ch < c_first)
             b_sum += v[u];
-          else if (c < c_first + kPlaceWaves)
-            sm.base[c - c_first][el] = v[u];
+          else if (ch < c_first + kPlaceWaves)
+            sm.base[ch - c_first][el] = v[u];
         }
       }
       atomicAdd(&sm.tot[el], t_sum);
