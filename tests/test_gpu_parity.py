@@ -702,6 +702,21 @@ def test_score_halves_on_a_side_stream():
         assert lrm.lrm_read_device_error(g.ws) == 0
 
 
+def test_full_size_score_halves_on_a_side_stream_match_one_stream():
+    # the Qwen3 share at full size: the forked sequence (bench.py --overlap) against the one-stream
+    # sequence bench.py times by default, every output bit for bit
+    w = C.workload(1)
+    sp = w.spec
+    pol = synth.policy(sp)
+    print("[case] full-size cfg1, score halves on a side stream", flush=True)
+    _, b1, _, e1 = run_gpu(w, pol)
+    _, b2, _, e2 = run_gpu(w, pol, overlap=True)
+    assert e1 == 0 and e2 == 0
+    h1, h2 = host(b1, sp), host(b2, sp)
+    for key in h1:
+        assert h1[key].tobytes() == h2[key].tobytes(), key
+
+
 # ------------------------------------------------------------------------------------------------
 # full-size workloads (the launch configuration bench.py times): exact where cheap, sampled GEMMs
 # ------------------------------------------------------------------------------------------------
