@@ -235,7 +235,8 @@ lrm_status lrm_score(const lrm_problem* problem, const float* topk_w, const void
  *
  * lrm_score_norms writes ||g_t||^2 of every token t < T and ||phi_r||^2 of every row r < L_cap
  * (float64, the same fixed-order sums as lrm_score) into the workspace's norm region.  It reads
- * only g and phi -- rows of phi at or past L may hold anything; their norms are never used -- and
+ * only g and all L_cap rows of phi (so phi must hold L_cap rows) -- rows at or past L may hold
+ * anything; their norms are never used -- and
  * writes nothing but that region, which no other call writes, so it may run on another stream
  * at the same time as lrm_plan_quotas (or lrm_admit_quotas) on the same workspace; the caller
  * orders it (an event) before lrm_score_combine.  It sets no device error bits.
