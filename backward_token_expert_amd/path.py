@@ -3,8 +3,9 @@
 ``DeviceBuffers`` allocates, with PyTorch, every output and the workspace of one problem; ``run``
 enqueues lrm_plan_quotas -> lrm_score (or lrm_score_criterion) -> lrm_select -> lrm_compact ->
 lrm_grouped_dw_dx (or lrm_grouped_dw -> lrm_grouped_dx) on one stream, or, given a second
-stream, runs lrm_score_norms there beside lrm_plan_quotas and lrm_score_combine after both.  ``LayerBuffers`` and
-``run_layer`` do the same for the rest of the expert backward over the retained rows:
+stream, runs lrm_score_norms there beside lrm_plan_quotas and lrm_score_combine after both.
+``LayerBuffers`` and ``run_layer`` do the same for the rest of the expert backward over the
+retained rows:
 lrm_swiglu_backward -> lrm_gather_tokens -> lrm_grouped_fc1_dw_dx (or the two FC1 calls) ->
 lrm_scatter_tokens.  No step of the path is computed here.
 """
