@@ -396,6 +396,54 @@ def test_row_and_retained_capacities_truncate_and_flag():
     np.testing.assert_array_equal(to_host(b.sel_row)[:K_cap], want)
 
 
+def test_nonfinite_scores_are_flagged_and_ranked_as_zero():
+    # A NaN phi row gives a NaN score and a +inf in g infinite scores: lrm_score sets NONFINITE,
+    # lrm_select ranks NaN (and any pattern with the sign bit) as +0 and +inf above every finite
+    # score, and flags the NaN.  The same holds for caller keys of the random criterion, with a
+    # negative and a NaN key.
+    torch = _torch()
+    from backward_token_expert_amd import lrm, path
+    from backward_token_expert_amd.path import to_host, to_device
+    w = C.workload(1, T=512)
+    sp = w.spec
+    pol = synth.policy(sp)
+    P = C.problem(sp)
+    inp = dict(C.upload(w))
+    r_nan = 5
+    t_inf = int(w.layout_pairs[r_nan]) // sp.k + 1   # a token that does not own row r_nan
+    inp["phi"][r_nan] = 0x7FC0                   # bf16 NaN
+    inp["g"][t_inf, 3] = 0x7F80                  # bf16 +inf
+    print("[case] NaN phi row, +inf in g", flush=True)
+    b = path.DeviceBuffers(P)
+    path.run(P, C.policy_obj(pol), inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"],
+             inp["W"], b)
+    torch.cuda.synchronize()
+    assert lrm.lrm_read_device_error(b.ws) & lrm_bits("NONFINITE")
+    fo, rp = to_host(b.fwd_off), to_host(b.row_pair)[:w.L]
+    score = to_host(b.score)[:w.L]
+    assert np.isnan(score[r_nan])
+    inf_rows = np.flatnonzero(rp // sp.k == t_inf)
+    assert inf_rows.size and np.all(np.isposinf(score[inf_rows]))
+    ranked = np.where(np.isnan(score), np.float32(0), score)
+    want = O.select_top_quota(ranked, fo, to_host(b.quota), rp)
+    np.testing.assert_array_equal(to_host(b.sel_row)[:want.size], want)
+    assert np.isin(inf_rows, want).all()          # +inf ranks first: always kept
+
+    keys = synth.pair_keys(sp).copy()
+    p_neg, p_nan = int(rp[fo[1]]), int(rp[fo[2] + 1])   # a pair of experts 1 and 2
+    keys[p_neg], keys[p_nan] = -1.0, np.nan
+    print("[case] random criterion with a negative and a NaN key", flush=True)
+    b = path.DeviceBuffers(P)
+    path.run(P, C.policy_obj(pol), inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"],
+             inp["W"], b, criterion="random", keys=to_device(keys))
+    torch.cuda.synchronize()
+    assert lrm.lrm_read_device_error(b.ws) & lrm_bits("NONFINITE")
+    kr = keys[rp].astype(np.float32)
+    kr = np.where(np.isnan(kr) | (kr < 0), np.float32(0), kr)
+    want = O.select_top_quota(kr, fo, to_host(b.quota), rp)
+    np.testing.assert_array_equal(to_host(b.sel_row)[:want.size], want)
+
+
 def lrm_bits(*names):
     from backward_token_expert_amd import lrm
     return sum(bit for bit, n in lrm.DEVERR.items() if n in names)
