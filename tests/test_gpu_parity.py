@@ -444,6 +444,57 @@ def test_nonfinite_scores_are_flagged_and_ranked_as_zero():
     np.testing.assert_array_equal(to_host(b.sel_row)[:want.size], want)
 
 
+def test_select_clamps_quotas_outside_the_segment_and_flags():
+    # quota above n (clamped to n: every row kept) and below 0 (clamped to 0: none kept) set
+    # QUOTA; an offset that would run past K_cap truncates that segment at K_cap and sets K_CAP
+    torch = _torch()
+    from backward_token_expert_amd import lrm, path
+    from backward_token_expert_amd.path import to_host, to_device
+    w = C.workload(1, T=512)
+    sp = w.spec
+    pol = synth.policy(sp)
+    P = C.problem(sp)
+    inp = C.upload(w)
+    b = path.DeviceBuffers(P)
+    path.run(P, C.policy_obj(pol), inp["topk_idx"], inp["topk_w"], inp["g"], inp["phi"],
+             inp["W"], b)
+    torch.cuda.synchronize()
+    assert lrm.lrm_read_device_error(b.ws) == 0
+    fo, rp = to_host(b.fwd_off), to_host(b.row_pair)
+    n = np.diff(fo)
+    score = to_host(b.score)[:fo[-1]]
+    q = to_host(b.quota).astype(np.int64)
+    q_bad = q.copy()
+    q_bad[0], q_bad[1] = n[0] + 5, -3
+    q_eff = np.clip(q_bad, 0, n)
+    off = np.concatenate([[0], np.cumsum(q_eff)])
+    print("[case] quotas n+5 and -3", flush=True)
+    b.sel_row.fill_(-7)
+    lrm.lrm_select(P, b.score, b.fwd_off, to_device(q_bad.astype(np.int32)),
+                   to_device(off.astype(np.int32)), b.sel_row, b.ws)
+    torch.cuda.synchronize()
+    assert lrm.lrm_read_device_error(b.ws, clear=True) & lrm_bits("QUOTA")
+    want = O.select_top_quota(score, fo, q_eff, rp)
+    np.testing.assert_array_equal(to_host(b.sel_row)[:off[-1]], want)
+    assert want[:n[0]].tolist() == list(range(fo[0], fo[1]))      # expert 0 keeps every row
+
+    # K_cap below the end of the last segment: the segment that crosses it keeps only its top
+    # K_cap - offset rows, the ones after it none
+    K = int(off[-1])
+    K_cap = K - 10
+    Ps = C.problem(sp, K_cap=K_cap)
+    b.sel_row.fill_(-7)
+    print(f"[case] K_cap = {K_cap} < K = {K}", flush=True)
+    lrm.lrm_select(Ps, b.score, b.fwd_off, to_device(q_eff.astype(np.int32)),
+                   to_device(off.astype(np.int32)), b.sel_row, b.ws)
+    torch.cuda.synchronize()
+    assert lrm.lrm_read_device_error(b.ws, clear=True) & lrm_bits("K_CAP")
+    q_cut = np.clip(np.minimum(q_eff, K_cap - off[:-1]), 0, None)
+    got = to_host(b.sel_row)
+    np.testing.assert_array_equal(got[:K_cap], O.select_top_quota(score, fo, q_cut, rp))
+    assert np.all(got[K_cap:K] == -7)
+
+
 def lrm_bits(*names):
     from backward_token_expert_amd import lrm
     return sum(bit for bit, n in lrm.DEVERR.items() if n in names)
