@@ -495,6 +495,39 @@ def test_select_clamps_quotas_outside_the_segment_and_flags():
     assert np.all(got[K_cap:K] == -7)
 
 
+def test_score_flags_row_pairs_out_of_range():
+    # a row whose pair id lies outside [0, T*k) scores 0 and sets INDEX, in lrm_score and in the
+    # split form alike; every other row keeps its score
+    torch = _torch()
+    from backward_token_expert_amd import lrm, path
+    from backward_token_expert_amd.path import to_host
+    w = C.workload(1, T=512)
+    sp = w.spec
+    P = C.problem(sp)
+    inp = C.upload(w)
+    b = path.DeviceBuffers(P)
+    path.run(P, C.policy_obj(synth.policy(sp)), inp["topk_idx"], inp["topk_w"], inp["g"],
+             inp["phi"], inp["W"], b)
+    torch.cuda.synchronize()
+    want = to_host(b.score)[:w.L].copy()
+    b.row_pair[3] = sp.T * sp.k + 5
+    b.row_pair[4] = -2
+    want[3] = want[4] = 0.0
+    print("[case] row_pair entries out of range", flush=True)
+    for split in (False, True):
+        b.score.fill_(-1.0)
+        lrm.lrm_read_device_error(b.ws, clear=True)
+        if split:
+            lrm.lrm_score_norms(P, inp["g"], inp["phi"], b.ws)
+            lrm.lrm_score_combine(P, inp["topk_w"], b.row_pair, b.fwd_off, b.score, b.ws)
+        else:
+            lrm.lrm_score(P, inp["topk_w"], inp["g"], inp["phi"], b.row_pair, b.fwd_off, b.score,
+                          b.ws)
+        torch.cuda.synchronize()
+        assert lrm.lrm_read_device_error(b.ws) == lrm_bits("INDEX"), split
+        assert to_host(b.score)[:w.L].tobytes() == want.tobytes(), split
+
+
 def lrm_bits(*names):
     from backward_token_expert_amd import lrm
     return sum(bit for bit, n in lrm.DEVERR.items() if n in names)
