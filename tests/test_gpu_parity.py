@@ -623,8 +623,8 @@ def _compact_with(P, bufs, inp, sel_host, rp_host, K):
 
 GEMM_SHAPES = [
     # (retained rows per expert, h, d): tile widths 192 / 256 / 384 (with a partial column tile),
-    # one or several row tiles, an empty expert, and a run of full rounds followed by a leftover
-    # round whose units are split along K (130 row tiles x 2 column tiles on 256 workgroups)
+    # one or several row tiles, an empty expert, and a full round of dphi units followed by a
+    # partial one (130 row tiles x 2 column tiles = 260 units on 256 workgroups)
     ([32], 256, 192),
     ([300], 512, 768),
     ([100], 256, 1408),
