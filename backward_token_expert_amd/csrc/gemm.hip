@@ -16,16 +16,20 @@
 // bf16 section).  The kernels are persistent: one workgroup per CU, and the work is laid out per
 // XCD (the MI355X has 8 dies of 32 CUs, each with its own L2; workgroup ids are dealt to dies
 // round-robin):
-//   dW   whole experts are dealt to dies (largest first, in a snake order), and the 32 workgroups
-//        of a die walk the tiles of their experts together, so every row of Gc/Phic is fetched
-//        from HBM once per die and the other tiles of that expert hit in L2;
+//   dW   the workgroups of a die form 1, 2 or 4 groups; experts are dealt to the groups (whole,
+//        largest first, in a snake order, or, when that leaves a group far above the fair share,
+//        cut along K into pieces whose later partial sums dw_fixup adds in piece order), and a
+//        group walks the tiles of one job together, so every row of Gc/Phic is fetched from HBM
+//        once per group and the other tiles of that job hit in L2;
 //   dphi each die takes a contiguous range of (row tile, column tile) units, columns fastest, so
-//        a row tile's Gc rows and the expert's W stay in that die's L2.
-// Global loads run three K steps ahead of the MFMAs through a ring of LDS stages.
-// fp32: v_mfma_f32_32x32x2f32 on 128 x 128 tiles, plain grids.
+//        a row tile's Gc rows and the expert's W stay in that die's L2; the one-launch kernel
+//        (gemm_fused) runs its dW share first and then claims dphi units from these ranges.
+// Global loads are issued S - 1 K steps ahead of their use through a ring of S LDS stages (S = 4
+// for the 384-wide tile, 5 for the narrower ones).
+// fp32: v_mfma_f32_32x32x2f32 on 64 x 64 tiles (four 32 x 32 wavefronts), plain grids.
 // Expert sizes stay on the device: schedules are built by one-workgroup kernels from cmp_off; a
-// zero-length segment writes zeros.  No atomics: every output element is owned by one workgroup,
-// so results are bitwise deterministic.
+// zero-length segment writes zeros.  No atomics on the outputs (only on gemm_fused's unit
+// counters): every output element is owned by one workgroup, so results are bitwise deterministic.
 #include "lrm_device.hpp"
 #include "lrm_internal.hpp"
 
