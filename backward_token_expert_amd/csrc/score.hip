@@ -84,9 +84,10 @@ constexpr int kLanesPerRow = 16;
 constexpr int kRowsPerWave = kWave / kLanesPerRow;
 
 // kNorms: only ||phi_r||^2 (float64) to pnorm[r], for every row below L_cap, without reading the
-// layout (fwd_off, row_pair, score and err are unused).
+// layout (fwd_off, row_pair, score and err are unused).  Eight waves per SIMD (at most 64 VGPRs,
+// no spills) keep more rows' loads in flight than the compiler's own choice of five.
 template <bool kBF16, bool kNorms>
-__global__ __launch_bounds__(kBlock) void row_score(const uint4* __restrict__ phi, int chunks,
+__global__ __launch_bounds__(kBlock, 8) void row_score(const uint4* __restrict__ phi, int chunks,
                                                     const int32_t* __restrict__ fwd_off, int E_loc,
                                                     int L_cap, const int32_t* __restrict__ row_pair,
                                                     const float* __restrict__ topk_w, int k,
