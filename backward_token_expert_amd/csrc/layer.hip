@@ -66,8 +66,10 @@ __device__ __forceinline__ void swiglu_grad(double g, double a, double c, double
 
 // One thread per chunk of 8 (bf16) or 4 (f32) columns of a retained row; chunks of a row are
 // consecutive threads.  A selected row outside [0, L_cap) sets LRM_DEVERR_INDEX and gets zeros.
+// Bounded to seven waves per SIMD (at most 72 VGPRs, no spills; the compiler alone takes 88 and
+// five waves).
 template <bool kBF16>
-__global__ __launch_bounds__(kBlock) void swiglu_bwd(const int32_t* __restrict__ sel_row,
+__global__ __launch_bounds__(kBlock, 7) void swiglu_bwd(const int32_t* __restrict__ sel_row,
                                                      const int32_t* __restrict__ cmp_off,
                                                      int E_loc, int K_cap, int L_cap, int d,
                                                      const float* __restrict__ dphi,
