@@ -429,6 +429,8 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[MT][NT]) {
 
 // C[m][n] for the wavefront's MT x NT tiles, rows < mend and columns < nend only.
 // 32x32 accumulator layout: lane l holds column l % 32, rows 8 (r / 4) + 4 (l / 32) + r % 4.
+// The stores are non-temporal: the float32 outputs are not read again by the launch, and keeping
+// them out of L2 leaves it to the operand panels the other workgroups still reuse.
 template <int MT, int NT>
 __device__ __forceinline__ void store_acc(float* __restrict__ out, int64_t ldo, int m0, int mend,
                                           int n0, int nend, int wm, int wn, int lane,
@@ -441,7 +443,8 @@ __device__ __forceinline__ void store_acc(float* __restrict__ out, int64_t ldo, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * 32 * MT + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < mend && n < nend) out[(int64_t)m * ldo + n] = acc[i][j][r];
+        if (m < mend && n < nend)
+          __builtin_nontemporal_store(acc[i][j][r], out + (int64_t)m * ldo + n);
       }
     }
 }

@@ -252,7 +252,8 @@ __global__ __launch_bounds__(kBlock) void gather_tokens(const int32_t* __restric
 
 // One wavefront per token: dx[t] = sum over its retained slots, in slot order, of the float32 rows
 // dX[i], accumulated in float64 from zero and rounded once; kCB float4 column chunks per lane per
-// pass.  Tokens without a retained row get zeros.
+// pass.  Tokens without a retained row get zeros.  The rows are written with non-temporal stores
+// (the launch reads none of them back).
 constexpr int kCB = 4;
 
 __global__ __launch_bounds__(kBlock) void scatter_tokens(const int32_t* __restrict__ inv,
@@ -298,8 +299,8 @@ __global__ __launch_bounds__(kBlock) void scatter_tokens(const int32_t* __restri
       for (int c = 0; c < kCB; ++c) {
         const int ch = c0 + lane + c * kWave;
         if (ch < hch)
-          dst[ch] = make_float4((float)acc[c][0], (float)acc[c][1], (float)acc[c][2],
-                                (float)acc[c][3]);
+          store_nt(dst + ch, make_float4((float)acc[c][0], (float)acc[c][1], (float)acc[c][2],
+                                         (float)acc[c][3]));
       }
     }
   }

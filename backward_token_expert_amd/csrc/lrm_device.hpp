@@ -75,6 +75,12 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16-byte streaming store of four floats (non-temporal hint: the data is not read again here).
+__device__ __forceinline__ void store_nt(float4* p, float4 v) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store((f32x4){v.x, v.y, v.z, v.w}, (f32x4*)p);
+}
+
 // bf16 bit pattern -> float (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
