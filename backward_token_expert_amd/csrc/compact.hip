@@ -101,7 +101,8 @@ __global__ __launch_bounds__(kBlock) void compact_rows_phi(
 }
 
 // Pass 2: one wavefront per token.  GC = 16-byte chunks of g_t each lane keeps in registers
-// (rows up to GC * 64 chunks); GC = 0 re-reads g_t for every kept pair (wider rows).
+// (rows up to GC * 64 chunks; loaded non-temporally, as nothing reads them again); GC = 0
+// re-reads g_t for every kept pair (wider rows).
 template <bool kBF16, int GC>
 __global__ __launch_bounds__(kBlock) void compact_tokens_g(
     const int32_t* __restrict__ inv, const int32_t* __restrict__ sel_pair,
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void compact_tokens_g(
 #pragma unroll
         for (int c = 0; c < (GC > 0 ? GC : 1); ++c) {
           const int ch = lane + c * kWave;
-          x[c] = ch < gch ? gs[ch] : make_uint4(0, 0, 0, 0);
+          x[c] = ch < gch ? load_nt(gs + ch) : make_uint4(0, 0, 0, 0);
         }
         loaded = true;
       }

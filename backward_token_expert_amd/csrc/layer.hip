@@ -252,8 +252,8 @@ __global__ __launch_bounds__(kBlock) void gather_tokens(const int32_t* __restric
 
 // One wavefront per token: dx[t] = sum over its retained slots, in slot order, of the float32 rows
 // dX[i], accumulated in float64 from zero and rounded once; kCB float4 column chunks per lane per
-// pass.  Tokens without a retained row get zeros.  The rows are written with non-temporal stores
-// (the launch reads none of them back).
+// pass.  Tokens without a retained row get zeros.  dX rows are read and dx rows written with
+// non-temporal hints (each is touched once).
 constexpr int kCB = 4;
 
 __global__ __launch_bounds__(kBlock) void scatter_tokens(const int32_t* __restrict__ inv,
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kBlock) void scatter_tokens(const int32_t* __restri
 #pragma unroll
           for (int c = 0; c < kCB; ++c) {
             const int ch = c0 + lane + c * kWave;
-            v[c] = ch < hch ? src[ch] : make_float4(0, 0, 0, 0);
+            v[c] = ch < hch ? load_nt(src + ch) : make_float4(0, 0, 0, 0);
           }
 #pragma unroll
           for (int c = 0; c < kCB; ++c) {

@@ -75,6 +75,13 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16-byte streaming load of four floats (non-temporal hint: the data is read once).
+__device__ __forceinline__ float4 load_nt(const float4* p) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const f32x4 v = __builtin_nontemporal_load((const f32x4*)p);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // 16-byte streaming store of four floats (non-temporal hint: the data is not read again here).
 __device__ __forceinline__ void store_nt(float4* p, float4 v) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
