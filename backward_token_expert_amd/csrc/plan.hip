@@ -1,6 +1,6 @@
 // lrm_plan_quotas: routed counts, stable forward layout, quotas and compacted offsets.
 //
-// LRMoE (arXiv 2610.37720) Algorithm 1 step 1 (N_e <- |P_e|), Sec. 3.1/3.3 (quotas fixed before
+// LRMoE (arXiv 2610.37720) Algorithm 1's count of each expert's pairs (N_e <- |P_e|), Sec. 3.1/3.3 (quotas fixed before
 // backward, 0 <= K_e <= N_e; rows kept in a consistent pair order grouped by expert), Fig. 4
 // (counts and prefix offsets define the segments).  The quota cap follows the capacity rule
 // C = CF * mean load of "Expert Parallel Math Deep" ("Capacity and the exact drop-rate formula").

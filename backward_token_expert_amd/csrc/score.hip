@@ -1,6 +1,6 @@
 // lrm_score: Load Recalibration Metric of every local forward row.
 //
-// LRMoE (arXiv 2610.37720) Sec. 3.2, Prop. 3.1, Eq. (3) and Algorithm 1 step 13:
+// LRMoE (arXiv 2610.37720) Sec. 3.2, Prop. 3.1, Eq. (3) and Algorithm 1's score:
 //   R_u = alpha_u^2 * ||g_t||_2^2 * ||phi_u||_2^2,
 // the squared Frobenius norm of the pair's FC2 weight-gradient contribution (alpha_u g_t) phi_u^T,
 // evaluated without materialising it (rank-one identity, Appendix 7.1 Eq. (11)-(12)).

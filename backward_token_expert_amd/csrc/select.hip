@@ -1,6 +1,6 @@
 // lrm_select: per-expert TopK(q_e) with a deterministic tie-break.
 //
-// LRMoE (arXiv 2610.37720) Algorithm 1 step 14 and Sec. 3.3: within each logical expert keep the
+// LRMoE (arXiv 2610.37720) Algorithm 1's per-expert TopK and Sec. 3.3: within each logical expert keep the
 // q_e highest-scoring pairs (per-expert, not layer-wide).  Appendix 7.2, Prop. 7.1: keeping the
 // largest scores is optimal and ties at the boundary leave several optimal sets; the kept set is
 // made unique by ranking on (score descending, pair index ascending).

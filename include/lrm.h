@@ -6,20 +6,20 @@
  * Memory-Constrained Nodes" (Hu et al., arXiv 2610.37720):
  *   lrm_plan_quotas  routed counts n_e, forward layout, quotas q_e, compacted offsets
  *   lrm_admit_quotas forward-time admission: the largest candidate retention rate whose retained
- *                    total fits this GPU's budgets fixes the quotas (Algorithm 1 steps 2-11)
- *                    (Algorithm 1 step 1; Sec. 3.1 and 3.3 quotas 0 <= K_e <= N_e; the capacity
+ *                    total fits this GPU's budgets fixes the quotas (Algorithm 1's admission loop)
+ *                    (Algorithm 1's count of each expert's pairs; Sec. 3.1 and 3.3 quotas 0 <= K_e <= N_e; the capacity
  *                    form of "Expert Parallel Math Deep", "Capacity and the exact drop-rate
  *                    formula")
  *   lrm_score        Load Recalibration Metric R_u = alpha_u^2 ||g_t||^2 ||phi_u||^2
- *                    (Sec. 3.2, Prop. 3.1, Eq. (3); Algorithm 1 step 13)
+ *                    (Sec. 3.2, Prop. 3.1, Eq. (3); Algorithm 1's score)
  *   lrm_score_norms / lrm_score_combine  the same in two halves: the norms need neither the
  *                    routing nor the layout, so they can run beside lrm_plan_quotas
  *   lrm_score_criterion  the same or one of the ablation criteria of Table 2
- *   lrm_select       per-expert TopK(q_e) (Algorithm 1 step 14; Sec. 3.3; Appendix 7.2 Prop. 7.1)
+ *   lrm_select       per-expert TopK(q_e) (Algorithm 1's per-expert TopK; Sec. 3.3; Appendix 7.2 Prop. 7.1)
  *   lrm_compact      physical compaction into contiguous expert-major segments
  *                    (Sec. 3.3, Sec. 3.4, Fig. 4; Appendix 7.1 Eq. (5))
  *   lrm_grouped_dw   variable-size grouped FC2 weight gradient dW_e = sum_u delta_u phi_u^T
- *                    (Sec. 3.2 Eq. (1); Appendix 7.1 Eq. (8)-(9); Algorithm 1 step 17)
+ *                    (Sec. 3.2 Eq. (1); Appendix 7.1 Eq. (8)-(9); Algorithm 1's grouped weight-gradient GEMM)
  *   lrm_grouped_dx   variable-size grouped FC2 input gradient dphi_u = W_e^T delta_u
  *                    (Appendix 7.1 Eq. (4)-(7); Sec. 3.3: the retained count is the row dimension
  *                    of the input-gradient product)
@@ -27,7 +27,7 @@
  *
  * and the rest of the expert backward over the same retained rows (Sec. 3.1: FC2, the activation
  * function, FC1 and the backward dispatch use the same retained identities; Sec. 3.4: repacking
- * shrinks all four expert-backward GEMMs; Algorithm 1 step 19, ScatterWithZeros):
+ * shrinks all four expert-backward GEMMs; Algorithm 1's ScatterWithZeros):
  *   lrm_swiglu_backward   cotangent of the saved FC1 output [a | c] through phi = SiLU(a) * c
  *   lrm_gather_tokens     FC1's input row x_t of every retained pair
  *   lrm_grouped_fc1_dw    grouped FC1 weight gradient dW1_e = sum_u dH_u x_u^T
@@ -147,7 +147,7 @@ typedef struct {
 } lrm_quota_policy;
 
 /*
- * Forward-time admission on one GPU (LRMoE Algorithm 1 steps 2-11; Sec. 3.3: candidate retained
+ * Forward-time admission on one GPU (LRMoE Algorithm 1's admission loop; Sec. 3.3: candidate retained
  * counts are tested in decreasing order starting with full retention, against the memory budget
  * and the communication window; the first feasible one fixes the quotas; if none is feasible,
  * admission fails).  Candidate c is the quota policy {full[c], rho_num[c], rho_den[c], cap_abs,
@@ -182,7 +182,7 @@ typedef struct {
 size_t lrm_workspace_bytes(const lrm_problem* problem);
 
 /*
- * Counts, forward layout, quotas and compacted offsets (LRMoE Algorithm 1 step 1; Sec. 3.3).
+ * Counts, forward layout, quotas and compacted offsets (LRMoE Algorithm 1's count of each expert's pairs; Sec. 3.3).
  *  in : topk_idx  int32 [T*k]
  *  out: counts    int32 [E]          routed pairs of every global expert (sum = T*k)
  *       fwd_off   int32 [E_loc + 1]  exclusive prefix of the local counts; fwd_off[E_loc] = L
@@ -290,7 +290,7 @@ lrm_status lrm_score_criterion(const lrm_problem* problem, int32_t criterion, co
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Per-expert top-q selection (LRMoE Algorithm 1 step 14; Appendix 7.2 Prop. 7.1).  In each
+ * Per-expert top-q selection (LRMoE Algorithm 1's per-expert TopK; Appendix 7.2 Prop. 7.1).  In each
  * forward segment i keep the quota[i] rows that come first in the order (score descending, pair
  * index ascending; within a segment pair order equals row order) and write their forward-row ids,
  * ascending, to sel_row[cmp_off[i] ...].  Scores are compared as float32 (equal bit patterns tie).
@@ -423,7 +423,7 @@ lrm_status lrm_grouped_fc1_dw_dx(const lrm_problem* problem, const void* dH, con
 /*
  * Input gradient of every token (LRMoE Sec. 3.1: returned input-gradient contributions are added
  * at their original token and routing-slot positions in zero-initialised dense buffers;
- * Algorithm 1 step 19, ScatterWithZeros):
+ * Algorithm 1's ScatterWithZeros):
  *   dx[t] = fl32( sum over slots j = 0..k-1 in order, pair p = t*k + j retained at row i, of
  *                 dX[i] ),  the sum taken in float64 from zero; dx[t] = 0 if no pair of t is kept
  *  in : sel_pair int32 [K_cap]; cmp_off (cmp_off[E_loc] = K read); dX float32 [K_cap][h]

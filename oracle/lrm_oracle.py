@@ -90,7 +90,7 @@ def f32_to_bf16_rne(x: np.ndarray) -> np.ndarray:
 def routed_counts(topk_idx: np.ndarray, E: int) -> np.ndarray:
     """n_e = |P_e|, the number of routed pairs of every expert e in [0, E).
 
-    [LRMoE] Algorithm 1, step 1 (N_{l,e} <- |P_{l,e}|); [EPMath] "Routing as an expectation over
+    [LRMoE] Algorithm 1, its count of each expert's pairs (N_{l,e} <- |P_{l,e}|); [EPMath] "Routing as an expectation over
     a batch": each token makes k dispatches, so the counts sum to T*k.
     """
     idx = np.asarray(topk_idx).reshape(-1).astype(np.int64)
@@ -250,7 +250,7 @@ def admit_quotas(n_loc: np.ndarray, candidates, budget: dict, K_cap=None):
     """Forward-time admission on one GPU: the candidate retention rates are tested in the given
     order (decreasing, starting with full retention), each candidate's quotas come from
     plan_quotas, and the first candidate whose retained total K = sum of its quotas is feasible
-    fixes the quotas; if none is, admission fails ([LRMoE] Algorithm 1, steps 2-11; Sec. 3.3:
+    fixes the quotas; if none is, admission fails ([LRMoE] Algorithm 1, its admission loop over candidate policies; Sec. 3.3:
     candidates are tested in decreasing order starting with full retention, the first feasible one
     fixes the quotas, and admission fails when none is feasible).
 
@@ -275,7 +275,7 @@ def admit_quotas(n_loc: np.ndarray, candidates, budget: dict, K_cap=None):
 def lrm_scores(topk_w, g, phi, row_pair, k: int, dtype: str, chunk: int = 65536) -> np.ndarray:
     """R_r = alpha_p^2 * ||g_t||_2^2 * ||phi_r||_2^2 for every local forward row r, in float64.
 
-    [LRMoE] Sec. 3.2, Prop. 3.1, Eq. (3) (and Algorithm 1, step 13): the squared Frobenius norm of
+    [LRMoE] Sec. 3.2, Prop. 3.1, Eq. (3) (and Algorithm 1's score): the squared Frobenius norm of
     the pair's FC2 weight-gradient contribution G_u = (alpha_u g_t) phi_u^T, factorised with the
     rank-one identity of Appendix 7.1, Eq. (11)-(12).  p = row_pair[r], t = p // k.
     """
@@ -347,7 +347,7 @@ def scores(criterion: str, topk_w, g, phi, row_pair, k: int, dtype: str, keys=No
 def select_top_quota(score32: np.ndarray, fwd_off, quota, row_pair) -> np.ndarray:
     """Forward rows kept by per-expert TopK(q_e), ascending within each expert, experts in order.
 
-    [LRMoE] Algorithm 1, step 14 and Sec. 3.3: within each logical expert keep the q_e
+    [LRMoE] Algorithm 1's per-expert TopK and Sec. 3.3: within each logical expert keep the q_e
     highest-scoring pairs; Appendix 7.2, Prop. 7.1: keeping the largest scores is optimal, and ties
     at the boundary admit several optimal sets.  The set is made unique by ranking on
     (score descending, pair index ascending).  Scores are the float32 values the decision is taken
@@ -552,7 +552,7 @@ def scatter_with_zeros(dXc, sel_pair, T: int, k: int) -> np.ndarray:
     """Input gradient of every token: the retained rows' contributions returned to their token
     and summed, tokens without a retained pair left at zero ([LRMoE] Sec. 3.1: returned
     input-gradient contributions are scatter-added at their original token and routing-slot
-    positions in zero-initialised dense buffers; Algorithm 1, step 19, ScatterWithZeros).
+    positions in zero-initialised dense buffers; Algorithm 1's ScatterWithZeros).
 
     Float64 sum per token over its slots j = 0..k-1 in order, starting from zero; shape [T, h].
     """
