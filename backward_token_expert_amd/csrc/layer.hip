@@ -2,10 +2,10 @@
 // gather of FC1's input rows, and the return of FC1's input-gradient rows to their tokens.
 //
 // LRMoE (arXiv 2610.37720) Sec. 3.1: FC2, the activation function, FC1 and the backward dispatch
-// use the same retained pair identities, and returned input-gradient contributions are added at
-// their original token and routing-slot positions in zero-initialised dense buffers (Algorithm 1,
-// step 19, ScatterWithZeros); Sec. 3.4: repacking shrinks the row dimension of all four
-// expert-backward GEMMs.  The FC1 GEMMs themselves are the grouped kernels of gemm.hip with the
+// work on one set of retained pair identities, and a kept row's input gradient goes back to the
+// token and slot it came from, in an output that starts as all zeros (Algorithm 1,
+// scatter-with-zeros); Sec. 3.4: repacking shrinks the row dimension of all four expert-backward
+// GEMMs.  The FC1 GEMMs themselves are the grouped kernels of gemm.hip with the
 // roles of the widths exchanged (their launchers are in api.hip).
 //
 //   swiglu_bwd      dH[i] = [dphi*c*SiLU'(a) | dphi*SiLU(a)] from the saved FC1 output [a | c] of

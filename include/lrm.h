@@ -421,9 +421,9 @@ lrm_status lrm_grouped_fc1_dw_dx(const lrm_problem* problem, const void* dH, con
                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Input gradient of every token (LRMoE Sec. 3.1: returned input-gradient contributions are added
- * at their original token and routing-slot positions in zero-initialised dense buffers;
- * Algorithm 1's ScatterWithZeros):
+ * Input gradient of every token (LRMoE Sec. 3.1: a kept row's input gradient goes back to the
+ * token and slot it came from, in an output that starts as all zeros; Algorithm 1,
+ * scatter-with-zeros):
  *   dx[t] = fl32( sum over slots j = 0..k-1 in order, pair p = t*k + j retained at row i, of
  *                 dX[i] ),  the sum taken in float64 from zero; dx[t] = 0 if no pair of t is kept
  *  in : sel_pair int32 [K_cap]; cmp_off (cmp_off[E_loc] = K read); dX float32 [K_cap][h]

@@ -194,7 +194,7 @@ def plan_quotas(n_loc: np.ndarray, policy: dict):
     """Retention quotas q_e and compacted-segment offsets.
 
     [LRMoE] Sec. 3.1/3.3: quotas satisfy 0 <= K_e <= N_e and are fixed for the invocation;
-    "starting with full retention" means K_e = N_e.  The cap form (policy kind "cap", the
+    the admission search begins at full retention, K_e = N_e.  The cap form (policy kind "cap", the
     default) follows [EPMath] "Capacity and the exact drop-rate formula": an expert keeps
     min(n_e, C) rows with C = CF * (mean load), here C = floor(num*L / (den*E_loc)) computed
     exactly in integers, optionally also capped at an absolute cap.  Kinds "proportional" and
@@ -550,9 +550,9 @@ def fc1_grouped_dx(dH, W1, cmp_off, dtype: str) -> np.ndarray:
 
 def scatter_with_zeros(dXc, sel_pair, T: int, k: int) -> np.ndarray:
     """Input gradient of every token: the retained rows' contributions returned to their token
-    and summed, tokens without a retained pair left at zero ([LRMoE] Sec. 3.1: returned
-    input-gradient contributions are scatter-added at their original token and routing-slot
-    positions in zero-initialised dense buffers; Algorithm 1's ScatterWithZeros).
+    and summed, tokens without a retained pair left at zero ([LRMoE] Sec. 3.1: a kept row's
+    input gradient goes back to the token and slot it came from, in an output that starts as all
+    zeros, so dropped slots contribute nothing; Algorithm 1, scatter-with-zeros).
 
     Float64 sum per token over its slots j = 0..k-1 in order, starting from zero; shape [T, h].
     """

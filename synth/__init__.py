@@ -11,9 +11,9 @@ routing skew.
 
 Workload shapes follow the LRMoE paper's evaluation models (Sec. 4.1: Qwen3-30B-A3B with 128
 experts, top-8, H=2048, F=768, 32768 tokens per GPU) and the GLM-4.5-Air shape listed in the
-TopoEP paper's model table (hidden 4096, expert intermediate 1408).  The router bias follows the
-TopoEP paper's synthetic-routing recipe ("random logits with a fixed expert-specific bias",
-Sec. 6 skew experiments) with Zipf-shaped per-expert biases.
+TopoEP paper's model table (hidden 4096, expert intermediate 1408).  The router follows the
+TopoEP paper's synthetic-routing recipe (Sec. 6, skew experiments: random router logits plus a
+constant offset per expert), here with Zipf-shaped per-expert offsets.
 
 Random values come from the counter-based SplitMix64 + Box-Muller generator in ``rng.c``; every
 value depends only on its identity (seed, stream, index), never on the array layout.

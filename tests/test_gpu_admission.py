@@ -7,6 +7,8 @@ import pytest
 import oracle as O
 import synth
 from tests import _common as C
+from tests.test_gpu_parity import (check_compact, check_gemms, check_scores,
+                                   check_selection_valid, gate_compact_gemms, host)
 
 pytestmark = pytest.mark.gpu
 
@@ -76,11 +78,16 @@ def test_admission_descent(cfg, kind, cap):
             continue
         # the rest of the path on the admitted quotas equals the path under that policy
         o = C.oracle_run(w, pols[want_c], gemms=False)
-        sel = to_host(b.sel_row)[:K]
-        if np.array_equal(sel, o["sel_row"]):
-            assert to_host(b.sel_pair)[:K].tobytes() == o["sel_pair"].astype(np.int32).tobytes()
-            bf = sp.dtype == "bf16"
-            assert to_host(b.Gc, bf)[:K].tobytes() == o["Gc"].tobytes()
-        else:                                   # only where the float32 scores differ in bits
-            s = to_host(b.score)[:int(o["fwd_off"][-1])]
-            assert not np.array_equal(s.view(np.uint32), o["score32"].view(np.uint32))
+        g = host(b, sp)
+        if np.array_equal(g["sel_row"], o["sel_row"]):
+            check_compact(g, o)
+            if bi == 0:                          # the products once per workload (host time)
+                check_gemms(g, o, w.W, sp.dtype)
+        else:
+            # the selections may differ only where the float32 scores differ in bits; then the
+            # admitted selection must still be the valid top-q under the GPU's own scores, and
+            # the GPU's compaction and GEMMs on the oracle's selection must match the oracle
+            assert not np.array_equal(g["score"].view(np.uint32), o["score32"].view(np.uint32))
+            check_scores(g, o)
+            check_selection_valid(g, o)
+            gate_compact_gemms(P, b, inp, o, w.W, sp.dtype)
