@@ -150,6 +150,24 @@ constexpr int stages_for() {
   return (160 * 1024) / ((C::SA + C::SB) * 2) < 5 ? (160 * 1024) / ((C::SA + C::SB) * 2) : 5;
 }
 
+// Columns are dealt to the wavefronts interleaved: column sub-tile j of wavefront column wn starts
+// at 32 wn + 32 WN j, so a tile whose last columns lie past the matrix edge leaves every
+// wavefront the same number of live sub-tiles (a prefix j < NTA), and the wavefronts skip the
+// MFMAs and fragment reads of the dead ones together instead of one SIMD idling the others.
+template <class C>
+__device__ __forceinline__ int col_of(int wn, int j) {
+  return 32 * wn + 32 * C::WN * j;
+}
+
+// Live column sub-tiles of wavefront column wn when `ncols` columns of the tile are inside the
+// matrix.
+template <class C>
+__device__ __forceinline__ int live_cols(int wn, int ncols) {
+  const int r = ncols - 32 * wn;
+  const int n = r <= 0 ? 0 : (r + 32 * C::WN - 1) / (32 * C::WN);
+  return n > C::NT ? C::NT : n;
+}
+
 // Lane-dependent byte offsets (within a stage) of this wavefront's fragment reads, fixed for the
 // whole kernel.  [k][mn] operands: offset of the first of the two transpose reads at k = 0; the
 // second read is 4 rows on and the k = 16 slice 16 rows on, both constants.  [mn][k] operand:
@@ -183,7 +201,7 @@ __device__ __forceinline__ FragOffsets<C> frag_offsets(int wm, int wn, int lane)
   }
 #pragma unroll
   for (int j = 0; j < C::NT; ++j)
-    f.b[j] = C::SA * 2 + kmn_offset<C::BN>(wn * 32 * C::NT + j * 32, lane);
+    f.b[j] = C::SA * 2 + kmn_offset<C::BN>(col_of<C>(wn, j), lane);
   return f;
 }
 
@@ -214,33 +232,36 @@ __device__ __forceinline__ bf16x8 read_b(uint32_t st, const FragOffsets<C>& f, i
 // use and the next slice's fragments (bn, a0n) along the way, so at most 2 NT + 2 fragments are
 // live.  Scheduling groups alternate one MFMA with LDS reads, so the reads hide behind the matrix
 // work.
-template <class C, int HC, int HN>
+template <class C, int HC, int HN, int NT>
 __device__ __forceinline__ void half_step(uint32_t sc, uint32_t sn, const FragOffsets<C>& fo,
                                           const bf16x8 (&bc)[C::NT], const bf16x8& a0c,
                                           bf16x8 (&bn)[C::NT], bf16x8& a0n,
                                           f32x16 (&acc)[C::MT][C::NT]) {
-  constexpr int MT = C::MT, NT = C::NT;
-  bf16x8 a = a0c;
+  // NT (<= C::NT): the live column sub-tiles; the dead ones are neither read nor multiplied
+  constexpr int MT = C::MT;
+  if constexpr (NT > 0) {
+    bf16x8 a = a0c;
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    bf16x8 an;
-    if (i + 1 < MT) an = read_a<C, HC>(sc, fo, i + 1);
+    for (int i = 0; i < MT; ++i) {
+      bf16x8 an;
+      if (i + 1 < MT) an = read_a<C, HC>(sc, fo, i + 1);
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-      if (j * MT / NT == i) bn[j] = read_b<C, HN>(sn, fo, j);
-    if (i == MT - 1) a0n = read_a<C, HN>(sn, fo, 0);
+      for (int j = 0; j < NT; ++j)
+        if (j * MT / NT == i) bn[j] = read_b<C, HN>(sn, fo, j);
+      if (i == MT - 1) a0n = read_a<C, HN>(sn, fo, 0);
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bc[j], acc[i][j], 0, 0, 0);
-    if (i + 1 < MT) a = an;
-  }
-  constexpr int kReads = (C::AKMN ? 2 : 1) * MT + 2 * NT;  // LDS read instructions per slice
-  constexpr int kMfma = MT * NT;
-  constexpr int per = (kReads + kMfma - 1) / kMfma;
+      for (int j = 0; j < NT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bc[j], acc[i][j], 0, 0, 0);
+      if (i + 1 < MT) a = an;
+    }
+    constexpr int kReads = (C::AKMN ? 2 : 1) * MT + 2 * NT;  // LDS read instructions per slice
+    constexpr int kMfma = MT * NT;
+    constexpr int per = (kReads + kMfma - 1) / kMfma;
 #pragma unroll
-  for (int q = 0; q < kMfma; ++q) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+    for (int q = 0; q < kMfma; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+    }
   }
 }
 
@@ -375,7 +396,7 @@ struct Loader {
 // the K range too (they fall outside their windows and write zeros), so the number of loads in
 // flight at each wait is the same constant.  Ends with every load drained and a barrier, so the
 // ring may be reused right away.
-template <class C, int S>
+template <class C, int S, int NTA>
 __device__ __forceinline__ void mainloop(const Operands& o, uint32_t ring, const FragOffsets<C>& fo,
                                          int w, int lane, f32x16 (&acc)[C::MT][C::NT]) {
   using R = Ring<C, S>;
@@ -394,12 +415,14 @@ __device__ __forceinline__ void mainloop(const Operands& o, uint32_t ring, const
   uint32_t rd = ring;                        // stage kt
   uint32_t wr = ring + (S - 1) * R::STG;     // stage kt - 1 (the DMA target)
   bf16x8 bA[C::NT], bB[C::NT], aA, aB;
-  aA = read_a<C, 0>(rd, fo, 0);
+  if constexpr (NTA > 0) {
+    aA = read_a<C, 0>(rd, fo, 0);
 #pragma unroll
-  for (int j = 0; j < C::NT; ++j) bA[j] = read_b<C, 0>(rd, fo, j);
+    for (int j = 0; j < NTA; ++j) bA[j] = read_b<C, 0>(rd, fo, j);
+  }
   for (int kt = 0; kt < nk; ++kt) {
     // first half: slice 0 of stage kt; reads slice 1 of the same stage
-    half_step<C, 0, 1>(rd, rd, fo, bA, aA, bB, aB, acc);
+    half_step<C, 0, 1, NTA>(rd, rd, fo, bA, aA, bB, aB, acc);
     __builtin_amdgcn_sched_barrier(0);
     // middle: stage kt+1 complete for every wave; stage kt-1 free
     wait_vm<(S - 3) * I>();
@@ -409,12 +432,29 @@ __device__ __forceinline__ void mainloop(const Operands& o, uint32_t ring, const
     wr = wr + R::STG == ring + R::BYTES ? ring : wr + R::STG;
     __builtin_amdgcn_sched_barrier(0);
     // second half: slice 1 of stage kt; reads slice 0 of stage kt+1 (unused after the last step)
-    half_step<C, 1, 0>(rd, rn, fo, bB, aB, bA, aA, acc);
+    half_step<C, 1, 0, NTA>(rd, rn, fo, bB, aB, bA, aA, acc);
     __builtin_amdgcn_sched_barrier(0);
     rd = rn;
   }
   wait_vm<0>();
   lds_barrier();
+}
+
+// The mainloop specialised for the wavefront's live column sub-tiles `nta` (wave-uniform).  Every
+// specialisation issues the same loads and barriers, so the wavefronts of one workgroup may take
+// different ones.
+template <class C, int S, int NTA = C::NT>
+__device__ __forceinline__ void mainloop_live(int nta, const Operands& o, uint32_t ring,
+                                              const FragOffsets<C>& fo, int w, int lane,
+                                              f32x16 (&acc)[C::MT][C::NT]) {
+  if constexpr (NTA == 0) {
+    mainloop<C, S, 0>(o, ring, fo, w, lane, acc);
+  } else {
+    if (nta >= NTA)
+      mainloop<C, S, NTA>(o, ring, fo, w, lane, acc);
+    else
+      mainloop_live<C, S, NTA - 1>(nta, o, ring, fo, w, lane, acc);
+  }
 }
 
 template <int MT, int NT>
@@ -427,11 +467,12 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[MT][NT]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 }
 
-// C[m][n] for the wavefront's MT x NT tiles, rows < mend and columns < nend only.
+// C[m][n] for the wavefront's MT x NT tiles (columns dealt as col_of), rows < mend and columns
+// < nend only.
 // 32x32 accumulator layout: lane l holds column l % 32, rows 8 (r / 4) + 4 (l / 32) + r % 4.
 // The stores are non-temporal: the float32 outputs are not read again by the launch, and keeping
 // them out of L2 leaves it to the operand panels the other workgroups still reuse.
-template <int MT, int NT>
+template <int MT, int NT, int WN>
 __device__ __forceinline__ void store_acc(float* __restrict__ out, int64_t ldo, int m0, int mend,
                                           int n0, int nend, int wm, int wn, int lane,
                                           const f32x16 (&acc)[MT][NT]) {
@@ -439,7 +480,7 @@ __device__ __forceinline__ void store_acc(float* __restrict__ out, int64_t ldo, 
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int n = n0 + wn * 32 * NT + j * 32 + (lane & 31);
+      const int n = n0 + 32 * wn + 32 * WN * j + (lane & 31);   // interleaved, as col_of
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * 32 * MT + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -479,9 +520,9 @@ __device__ __forceinline__ void dw_jobs(const uint16_t* __restrict__ Gc,
     const int m0 = (local / tn) * C::BM, n0 = (local % tn) * C::BN;
     const Operands o{Gc, h, m0, h, Phic, d, n0, d, kb, ke};
     zero_acc(acc);
-    mainloop<C, S>(o, ring_addr, fo, w, lane, acc);
+    mainloop_live<C, S>(live_cols<C>(wn, d - n0), o, ring_addr, fo, w, lane, acc);
     float* out = slot < 0 ? dW + (int64_t)e * h * d : slots + (int64_t)slot * h * d;
-    store_acc(out, d, m0, h, n0, d, wm, wn, lane, acc);
+    store_acc<C::MT, C::NT, C::WN>(out, d, m0, h, n0, d, wm, wn, lane, acc);
   }
 }
 
@@ -542,8 +583,8 @@ __device__ __forceinline__ void dx_unit(const uint16_t* __restrict__ Gc,
   mend = mend > K_cap ? K_cap : mend;
   const Operands o{Gc, h, m0, mend, W + (int64_t)e * h * d, d, n0, d, 0, h};
   zero_acc(acc);
-  mainloop<C, S>(o, ring_addr, fo, w, lane, acc);
-  store_acc(dphi, d, m0, mend, n0, d, wm, wn, lane, acc);
+  mainloop_live<C, S>(live_cols<C>(wn, d - n0), o, ring_addr, fo, w, lane, acc);
+  store_acc<C::MT, C::NT, C::WN>(dphi, d, m0, mend, n0, d, wm, wn, lane, acc);
 }
 
 // dphi: persistent, die x owns the contiguous unit range [x * per, (x + 1) * per).
@@ -847,7 +888,7 @@ __global__ __launch_bounds__(kF32Threads) void dw_f32(const float* __restrict__ 
     if (kt + 1 < nk) st_kmn_f32(isA ? sa[cur ^ 1] : sb[cur ^ 1], blk, v);
     __syncthreads();
   }
-  store_acc<1, 1>(dW + (int64_t)e * h * d, d, m0, h, n0, d, wm, wn, lane, acc);
+  store_acc<1, 1, 2>(dW + (int64_t)e * h * d, d, m0, h, n0, d, wm, wn, lane, acc);
 }
 
 __global__ __launch_bounds__(kF32Threads) void dx_f32(const float* __restrict__ Gc,
@@ -894,7 +935,7 @@ __global__ __launch_bounds__(kF32Threads) void dx_f32(const float* __restrict__ 
     }
     __syncthreads();
   }
-  store_acc<1, 1>(dphi, d, m0, mend, n0, d, wm, wn, lane, acc);
+  store_acc<1, 1, 2>(dphi, d, m0, mend, n0, d, wm, wn, lane, acc);
 }
 
 // ------------------------------------------------------------------------------------------------

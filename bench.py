@@ -5,15 +5,28 @@ One step = the whole path over one batch of synthetic input already resident in 
 lrm_plan_quotas -> lrm_score -> lrm_select -> lrm_compact -> lrm_grouped_dw_dx (both FC2
 gradients; --separate-gemms: lrm_grouped_dw -> lrm_grouped_dx).  --overlap runs the score in its
 two halves instead: lrm_score_norms on a second stream beside lrm_plan_quotas (it needs neither
-the routing nor the layout), then lrm_score_combine once both are done.  The rest of the expert backward
-over the same retained rows (activation, FC1 gradients, return to the tokens) is timed after it
-as its own leg ("layer_backward"), outside the step.
+the routing nor the layout), then lrm_score_combine once both are done.  The rest of the expert
+backward over the same retained rows (activation, FC1 gradients, return to the tokens) is timed
+after it as its own leg ("layer_backward"), outside the step.
 
-Default workload: the Qwen3-30B-A3B-shaped share of one GPU (128 experts, 16 local, top-8,
-32768 tokens, h=2048, d_ffn=768, bf16, retention rho = 0.5).  Prints ONE JSON line.
+Default workload: the GLM4.5-106B-A12B-shaped share of one GPU (128 experts, 16 local, top-8,
+32768 tokens, h=4096, d_ffn=1408, bf16, retention rho = 0.5), the largest single-GPU workload.
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 1] [--no-cpu-baseline]
+Timing protocol: the step is captured once in a HIP graph; W warm-up replays, then K timed
+replays, each bracketed by its own HIP events on the launch stream, with a 1 GiB buffer written
+between replays (outside the events) so that no input is served from the 256 MB last-level cache;
+the line reports the mean (value, ms_per_step) and the median / p10 / p90 of the K replays.  Stage
+times come from a separate eager pass with events between the calls (same flush).  The line also
+carries a plain device copy timed the same way (the bandwidth a streaming kernel reaches here),
+the graphics clock sampled while the GEMMs run (MFMA fractions are given against the 2.4 GHz spec
+peak and against that clock), further legs on the Qwen3-30B-A3B share and the extreme-skew sweep,
+and the oracle timed on the host cores (all of them, and one).
+
+Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 2] [--no-cpu-baseline]
                   [--criterion lrm|grad_sq|grad_abs|random] [--quota cap|proportional|waterfill]
+                  [--no-legs] [--flush-mib 1024]
 """
 from __future__ import annotations
 
@@ -28,6 +41,7 @@ import numpy as np
 METRIC = "pairs/s thru LRM score+select+compact+grouped dW/dφ GEMM; % bf16 MFMA peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix-core peaks, TFLOP/s
+SPEC_CLOCK_MHZ = 2400.0        # the clock those peaks assume
 
 STAGES_FUSED = ("plan", "score", "select", "compact", "gemm")
 STAGES_SPLIT = ("plan", "score", "select", "compact", "dw", "dx")
@@ -36,9 +50,9 @@ STAGES_SPLIT = ("plan", "score", "select", "compact", "dw", "dx")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--criterion", default="lrm", choices=["lrm", "grad_sq", "grad_abs", "random"],
                     help="selection score: the LRM, or one of the ablation criteria")
     ap.add_argument("--quota", default="cap", choices=["cap", "proportional", "waterfill"],
@@ -59,9 +73,20 @@ def parse():
     ap.add_argument("--layer-steps", type=int, default=None,
                     help="timed steps of the rest of the expert backward (activation, FC1, return "
                          "to the tokens) on the retained rows (default steps/2; 0 skips it)")
-    ap.add_argument("--copy-calibration-mib", type=int, default=512,
+    ap.add_argument("--copy-calibration-mib", type=int, default=1024,
                     help="after timing, copy a buffer of this size once (a plain copy kernel of "
                          "known traffic, to scale rocprofv3 FETCH_SIZE/WRITE_SIZE); 0 skips it")
+    ap.add_argument("--flush-mib", type=int, default=1024,
+                    help="size of the buffer written between timed steps (0: back to back)")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the Qwen3-share leg and the extreme-skew retention sweep")
+    ap.add_argument("--leg-steps", type=int, default=20,
+                    help="timed steps of each extra leg")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the graphics clock while the GEMMs run")
+    ap.add_argument("--cpu-one-core-seconds", type=float, default=8.0,
+                    help="the oracle's one-core run: repeat its sample until this much time has "
+                         "passed (0 skips it)")
     return ap.parse_args()
 
 
@@ -92,7 +117,13 @@ def algorithmic(w, oracle_like, criterion="lrm"):
     }
 
 
-def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True, graph=True, overlap=False):
+def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True, graph=True, overlap=False,
+              flush=None, gemm_clock=False):
+    """Time the path on workload `w` under quota policy `pol_dict`.  Returns (mean ms per step,
+    stage ms, info) with info holding L, K, per-expert K, per-step times and (gemm_clock) the
+    graphics clock sampled while the one-launch GEMM runs."""
+    if flush is None:
+        flush = make_flush(0)
     import torch
     from backward_token_expert_amd import lrm, path
     from backward_token_expert_amd.path import to_device, to_host
@@ -165,11 +196,13 @@ def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True, graph=Tru
     s = torch.cuda.current_stream()
 
     # Stage times: eager steps with HIP events between the calls, on the stream the kernels are
-    # launched on (the events cost nothing measurable next to the stages).
+    # launched on (the events cost nothing measurable next to the stages); the flush buffer is
+    # written before each step, outside its events.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
            for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
+        flush(i)
         step(evs[i])
     torch.cuda.synchronize()
     stage_ms = {st: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
@@ -178,6 +211,7 @@ def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True, graph=Tru
     # Whole-step time: the step captured once in a HIP graph and replayed (every call of the path
     # is capturable: no allocation, no host synchronisation); --eager times eager launches.
     run_step = step
+    g_gemm = None
     if graph:
         g_step = torch.cuda.CUDAGraph()
         cs = torch.cuda.Stream()
@@ -191,17 +225,9 @@ def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True, graph=Tru
         run_step = g_step.replay
         for _ in range(warmup):
             run_step()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    t_start.record(s)
-    for i in range(steps):
-        run_step()
-    t_end.record(s)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = t_start.elapsed_time(t_end)
+    per, wall = timed_replays(run_step, steps, flush)
+    # back to back (no flush), for comparison only
+    per_warm, _ = timed_replays(run_step, steps, None)
     err = lrm.lrm_read_device_error(b.ws)
     if err:
         raise RuntimeError(f"device error word {err}: {lrm.deverr_names(err)}")
@@ -209,8 +235,128 @@ def gpu_bench(w, pol_dict, steps, warmup, criterion="lrm", fused=True, graph=Tru
     co = to_host(b.cmp_off)
     sel_pair = to_host(b.sel_pair)[:int(co[-1])]
     info = {"L": int(fo[-1]), "K": int(co[-1]), "Ke": np.diff(co),
-            "T_ret": int(np.unique(sel_pair // sp.k).size)}
-    return ms_total / steps, wall / steps * 1e3, stage_ms, info
+            "T_ret": int(np.unique(sel_pair // sp.k).size),
+            "step_ms": per, "warm_step_ms": per_warm, "wall_ms": wall}
+    if gemm_clock and fused:
+        info["clock"] = gemm_clock_sample(
+            lambda st: lrm.lrm_grouped_dw_dx(P, b.Gc, b.Phic, W, b.cmp_off, b.dW, b.dphi, b.ws, st),
+            stage_ms["gemm"])
+    return float(np.mean(per)), stage_ms, info
+
+
+def make_flush(mib):
+    """A callable that writes a `mib` MiB buffer on the current stream (nothing for 0)."""
+    if mib <= 0:
+        return lambda i: None
+    import torch
+    buf = torch.empty(mib << 18, dtype=torch.float32, device="cuda")
+    return lambda i: buf.fill_(float(i))
+
+
+def timed_replays(run_step, steps, flush):
+    """`steps` runs of `run_step`, each bracketed by its own HIP events on the current stream,
+    the flush (if any) written between them outside the events.  Returns the per-step times
+    (ms) and the host wall time per step (ms, flush included)."""
+    import torch
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if flush is not None:
+            flush(i)
+        ev[i][0].record(s)
+        run_step()
+        ev[i][1].record(s)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    return [a.elapsed_time(b) for a, b in ev], wall
+
+
+def step_stats(per):
+    return {"mean": float(np.mean(per)), "median": float(np.median(per)),
+            "p10": float(np.percentile(per, 10)), "p90": float(np.percentile(per, 90)),
+            "n": len(per)}
+
+
+def gemm_clock_sample(launch, ms_per_call, seconds=1.0):
+    """The graphics clock while the one-launch GEMM runs back to back for about `seconds`:
+    amdsmi is polled from a second thread while the host waits for the GPU.  Returns
+    {"MHz_median", "samples", "source"} or None where amdsmi is unavailable."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        h = handles[0]
+        if len(handles) > 1:                     # match the device torch uses by PCI address
+            want = torch.cuda.get_device_properties(0)
+            bus = getattr(want, "pci_bus_id", None)
+            for x in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(x)
+                if bus is not None and int(bdf.split(":")[1], 16) == bus:
+                    h = x
+    except Exception as e:  # noqa: BLE001
+        return {"error": f"amdsmi unavailable: {type(e).__name__}: {e}"[:200]}
+
+    def read():
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
+                v = m.get(key)
+                if isinstance(v, (list, tuple)):
+                    v = [x for x in v if isinstance(x, (int, float)) and 0 < x < 10000]
+                    if v:
+                        return float(np.mean(v)), key
+                elif isinstance(v, (int, float)) and 0 < v < 10000:
+                    return float(v), key
+        except Exception:  # noqa: BLE001
+            pass
+        try:
+            c = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+            v = c.get("clk") if isinstance(c, dict) else None
+            if isinstance(v, (int, float)) and 0 < v < 10000:
+                return float(v), "clock_info.clk"
+        except Exception:  # noqa: BLE001
+            pass
+        return None
+
+    samples, src = [], set()
+    stop = threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            r = read()
+            if r is not None:
+                samples.append(r[0])
+                src.add(r[1])
+            time.sleep(0.005)
+
+    n = max(10, int(seconds * 1e3 / max(ms_per_call, 1e-3)))
+    s = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        launch(s.cuda_stream)
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    for _ in range(n):
+        launch(s.cuda_stream)
+    torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=2.0)
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:  # noqa: BLE001
+        pass
+    if not samples:
+        return {"error": "no clock readings"}
+    # drop the first readings (the launches ramp up) and take the median
+    use = samples[len(samples) // 5:] or samples
+    return {"MHz_median": float(np.median(use)), "samples": len(use), "source": sorted(src),
+            "calls": n}
 
 
 LAYER_STAGES = ("swiglu", "gather", "fc1_gemm", "scatter")
@@ -340,20 +486,38 @@ def synth_keys(sp):
     return synth.pair_keys(sp)
 
 
-def cpu_baseline(w, pol_dict, n_experts, min_seconds, criterion="lrm"):
+def host_cpu():
+    """Model name and the number of host cores this process may run on."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count()
+    return {"model": model, "cores_available": n}
+
+
+def cpu_baseline(w, pol_dict, n_experts, min_seconds, criterion="lrm", threads=None):
     """The oracle, as it stands, on a bounded sample: all counting/planning plus scoring,
     selection, compaction and both GEMMs of the first `n_experts` local experts, repeated until
-    `min_seconds` have passed (at least once); the rate is over all repetitions."""
+    `min_seconds` have passed (at least once); the rate is over all repetitions.  `threads`
+    limits the BLAS thread pool (None: as configured)."""
+    import contextlib
     import oracle as O
     sp = w.spec
     keys = synth_keys(sp) if criterion == "random" else None
-    threads = None
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max((i.get("num_threads", 1) for i in info), default=None)
-    except Exception:
-        pass
+        limit = (threadpoolctl.threadpool_limits(threads) if threads is not None
+                 else contextlib.nullcontext())
+    except Exception:  # noqa: BLE001
+        threadpoolctl, limit = None, contextlib.nullcontext()
 
     def once():
         n = O.routed_counts(w.topk_idx, sp.E)
@@ -369,15 +533,20 @@ def cpu_baseline(w, pol_dict, n_experts, min_seconds, criterion="lrm"):
         O.grouped_dx(Gc, w.W[:ne], off, sp.dtype)
         return ne, int(fwd_off[ne]), int(off[-1])
 
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        ne, pairs, kept = once()
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    return {"value": reps * pairs / dt, "unit": "pairs/s", "cores": threads or os.cpu_count(),
+    with limit:
+        used = None
+        if threadpoolctl is not None:
+            info = threadpoolctl.threadpool_info()
+            used = max((i.get("num_threads", 1) for i in info), default=None)
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            ne, pairs, kept = once()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    return {"value": reps * pairs / dt, "unit": "pairs/s", "cores": used or os.cpu_count(),
             "kind": "oracle",
             "sample": f"fp64 numpy oracle: counts/layout/quotas over all {sp.T * sp.k} pairs, "
                       f"then score/select/compact/dW/dphi for local experts 0..{ne - 1} "
@@ -404,6 +573,48 @@ def recorded_traffic(call, workload):
     return None
 
 
+def fractions(st, a, dtype, clock_mhz=None):
+    """HBM fraction of score+select+compact and MFMA fraction of the GEMMs from stage times."""
+    t_ssc = (st["score"] + st["select"] + st["compact"]) * 1e-3
+    by = a["score"] + a["select"] + a["compact"]
+    t_g = (st["gemm"] if "gemm" in st else st["dw"] + st["dx"]) * 1e-3
+    fl = a["flops_dw"] + a["flops_dx"]
+    out = {"score_select_compact_GBps": by / t_ssc / 1e9,
+           "score_select_compact_hbm_frac": by / t_ssc / 1e9 / HBM_PEAK_GBS,
+           "gemms_TFLOPs": fl / t_g / 1e12,
+           "gemms_mfma_frac": fl / t_g / 1e12 / MFMA_PEAK_TFLOPS[dtype]}
+    if clock_mhz:
+        out["gemms_mfma_frac_at_measured_clock"] = (
+            fl / t_g / 1e12 / (MFMA_PEAK_TFLOPS[dtype] * clock_mhz / SPEC_CLOCK_MHZ))
+    return out
+
+
+def leg(w, pol, steps, warmup, crit, fused, graph, flush, label):
+    """One extra timed workload / policy: value, per-step statistics, stages and fractions."""
+    ms, stages, info = gpu_bench(w, pol, steps, warmup, crit, fused, graph, False, flush)
+    alg = algorithmic(w, info, crit)
+    return {"workload": w.spec.name, "policy": label, "value": info["L"] / (ms * 1e-3),
+            "unit": "pairs/s", "ms_per_step": ms, "step_ms": step_stats(info["step_ms"]),
+            "L_pairs": info["L"], "K_retained": info["K"],
+            "retained_rows_per_s": info["K"] / (ms * 1e-3), "stages_ms": stages,
+            "fractions": fractions(stages, alg, w.spec.dtype)}
+
+
+def copy_ceiling(flush, mib=1024, reps=10):
+    """A plain device-to-device copy of `mib` MiB timed like the step (events around each copy,
+    the flush between copies): bytes read + written per second."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    per, _ = timed_replays(lambda: dst.copy_(src), reps, flush)
+    del src, dst
+    med = float(np.median(per))
+    return {"GBps": 2 * n / (med * 1e-3) / 1e9, "bytes_moved": 2 * n, "median_ms": med,
+            "kernel": "torch copy_ (device to device)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -417,27 +628,20 @@ def main():
     crit = args.criterion
     fused = not args.separate_gemms
     overlap = args.overlap
-    ms, wall_ms, stages, info = gpu_bench(w, pol, args.steps, args.warmup, crit, fused,
-                                          not args.eager, overlap)
+    graph = not args.eager
+    flush = make_flush(args.flush_mib)
+    ms, stages, info = gpu_bench(w, pol, args.steps, args.warmup, crit, fused, graph, overlap,
+                                 flush, gemm_clock=not args.no_clock)
     alg = algorithmic(w, info, crit)
     L, K = info["L"], info["K"]
+    clock = info.get("clock") or {}
+    clk = clock.get("MHz_median")
     # rho = 1 (full retention) on the same input
     n1 = max(3, args.steps // 2) if args.rho1_steps is None else args.rho1_steps
     if n1 > 0:
         pol_full = synth.policy(sp, full=True)
-        ms1, _, stages1, info1 = gpu_bench(w, pol_full, n1, 2, crit, fused, not args.eager,
-                                           overlap)
+        ms1, stages1, info1 = gpu_bench(w, pol_full, n1, 2, crit, fused, graph, overlap, flush)
         alg1 = algorithmic(w, info1, crit)
-
-    def fractions(st, a, dtype):
-        t_ssc = (st["score"] + st["select"] + st["compact"]) * 1e-3
-        by = a["score"] + a["select"] + a["compact"]
-        t_g = (st["gemm"] if "gemm" in st else st["dw"] + st["dx"]) * 1e-3
-        fl = a["flops_dw"] + a["flops_dx"]
-        return {"score_select_compact_GBps": by / t_ssc / 1e9,
-                "score_select_compact_hbm_frac": by / t_ssc / 1e9 / HBM_PEAK_GBS,
-                "gemms_TFLOPs": fl / t_g / 1e12,
-                "gemms_mfma_frac": fl / t_g / 1e12 / MFMA_PEAK_TFLOPS[dtype]}
 
     if fused:
         dom_call = "lrm_grouped_dw_dx"
@@ -447,6 +651,12 @@ def main():
         dom_call = {"dw": "lrm_grouped_dw", "dx": "lrm_grouped_dx"}[dom]
         ach = alg["flops_" + dom] / (stages[dom] * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[sp.dtype]
+    roof = {"bound": "mfma", "kernel": dom_call, "achieved": ach, "peak": peak,
+            "unit": "TFLOP/s", "frac": ach / peak,
+            "traffic": recorded_traffic(dom_call, sp.name)}
+    if clk:
+        roof["frac_at_measured_clock"] = ach / (peak * clk / SPEC_CLOCK_MHZ)
+        roof["measured_clock_MHz"] = clk
     out = {
         "metric": METRIC,
         "value": L / (ms * 1e-3),
@@ -464,26 +674,47 @@ def main():
                    "local_experts": sp.E_loc, "h": sp.h, "d_ffn": sp.d,
                    "rho": f"{pol['rho_num']}/{pol['rho_den']}", "quota": args.quota,
                    "criterion": crit, "L_pairs": L, "K_retained": K},
-        "roofline": {"bound": "mfma", "kernel": dom_call,
-                     "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
-                     "traffic": recorded_traffic(dom_call, sp.name)},
+        "roofline": roof,
+        "step_ms": step_stats(info["step_ms"]),
+        "step_ms_back_to_back": step_stats(info["warm_step_ms"]),
         "retained_rows_per_s": K / (ms * 1e-3),
-        "timing": "eager launches" if args.eager else "replays of one captured HIP graph",
+        "timing": ("eager launches" if args.eager else "replays of one captured HIP graph") +
+                  (f"; {args.flush_mib} MiB written between timed steps" if args.flush_mib > 0
+                   else "; back to back"),
         "overlap": ("lrm_score_norms on a second stream beside lrm_plan_quotas; stage times from "
                     "eager steps with the two halves in sequence") if overlap and crit == "lrm"
                    else None,
-        "wall_ms_per_step": wall_ms,
+        "wall_ms_per_step": info["wall_ms"],
         "stages_ms": stages,
-        "fractions": fractions(stages, alg, sp.dtype),
+        "fractions": fractions(stages, alg, sp.dtype, clk),
+        "gpu_clock": clock or None,
     }
     if n1 > 0:
         out["rho1"] = {"value": info1["L"] / (ms1 * 1e-3), "ms_per_step": ms1,
+                       "step_ms": step_stats(info1["step_ms"]),
                        "K_retained": info1["K"], "stages_ms": stages1,
-                       "fractions": fractions(stages1, alg1, sp.dtype)}
+                       "fractions": fractions(stages1, alg1, sp.dtype, clk)}
     nl = max(3, args.steps // 2) if args.layer_steps is None else args.layer_steps
     if nl > 0:
         out["layer_backward"] = layer_bench(w, pol, nl, 2, crit)
     out["admission"] = admission_bench(w, 20)
+    out["copy_ceiling"] = copy_ceiling(flush)
+    if not args.no_legs:
+        legs = {}
+        if args.config != 1:
+            w1 = synth.make(1)
+            legs["qwen3_share"] = leg(w1, synth.policy(w1.spec), args.leg_steps, 3, "lrm", fused,
+                                      graph, flush, "rho 1/2 (cap)")
+            del w1
+        w3 = synth.make(3)
+        sweep = [leg(w3, synth.policy(w3.spec, full=True), args.leg_steps, 3, "lrm", fused,
+                     graph, flush, "full retention")]
+        for num, den in synth.RHO_SWEEP_3:
+            sweep.append(leg(w3, synth.policy(w3.spec, rho=(num, den)), args.leg_steps, 3, "lrm",
+                             fused, graph, flush, f"rho {num}/{den} (cap)"))
+        legs["extreme_skew_sweep"] = sweep
+        del w3
+        out["legs"] = legs
     if args.copy_calibration_mib > 0:
         import torch
         n = args.copy_calibration_mib << 20
@@ -494,8 +725,13 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = n
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, pol, args.cpu_sample_experts,
-                                           args.cpu_min_seconds, crit)
+        cb = cpu_baseline(w, pol, args.cpu_sample_experts, args.cpu_min_seconds, crit)
+        cb["host_cpu"] = host_cpu()
+        if args.cpu_one_core_seconds > 0:
+            one = cpu_baseline(w, pol, 1, args.cpu_one_core_seconds, crit, threads=1)
+            cb["one_core"] = {"value": one["value"], "unit": one["unit"], "cores": one["cores"],
+                              "sample": one["sample"]}
+        out["cpu_baseline"] = cb
     print(json.dumps(out))
 
 

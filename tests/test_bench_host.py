@@ -22,8 +22,10 @@ def test_committed_traffic_record_matches_the_gemm_sources():
     # sources; bench.py reports the traffic only while that digest matches the tree
     sys.path.insert(0, ROOT)
     import bench
-    wl = "qwen3-30b-a3b share E128/16 top8 T32768 h2048 d768"
-    for call in ("lrm_grouped_dw_dx", "lrm_grouped_fc1_dw_dx"):
-        t = bench.recorded_traffic(call, wl)
-        assert t is not None and t > 1e9, call
+    import synth
+    for cfg in (2, 1):                            # the headline workload and the Qwen3 share
+        wl = synth.spec(cfg).name
+        for call in ("lrm_grouped_dw_dx", "lrm_grouped_fc1_dw_dx"):
+            t = bench.recorded_traffic(call, wl)
+            assert t is not None and t > 1e9, (cfg, call)
     assert bench.recorded_traffic("lrm_grouped_dw_dx", "no such workload") is None
