@@ -9,6 +9,7 @@ from . import lrm, path  # noqa: F401
 from .lrm import (LRM_BF16, LRM_F32, Admission, LrmError, Problem, QuotaPolicy,  # noqa: F401
                   load_library, lrm_admit_quotas, make_admission,
                   lrm_compact, lrm_gather_tokens, lrm_grouped_dw, lrm_grouped_dw_dx,
+                  lrm_grouped_dw_dx_noalloc,
                   lrm_grouped_dx, lrm_grouped_fc1_dw, lrm_grouped_fc1_dw_dx, lrm_grouped_fc1_dx,
                   lrm_plan_quotas, lrm_scatter_tokens, lrm_swiglu_backward,
                   lrm_read_device_error, lrm_score, lrm_score_combine, lrm_score_criterion,

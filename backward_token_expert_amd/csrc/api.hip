@@ -214,6 +214,18 @@ lrm_status lrm_grouped_dw_dx(const lrm_problem* problem, const void* Gc, const v
                                     stream, 2));
 }
 
+lrm_status lrm_grouped_dw_dx_noalloc(const lrm_problem* problem, const void* Gc,
+                                     const void* Phic, const void* W, const int32_t* cmp_off,
+                                     float* dW, float* dphi, hipStream_t stream) {
+  LRM_TRY(check_problem(problem));
+  if (!Gc || !Phic || !W || !cmp_off || !dW || !dphi) return LRM_ERR_INVALID_ARGUMENT;
+  if (!aligned16(Gc) || !aligned16(Phic) || !aligned16(W) || !aligned16(dW) || !aligned16(dphi))
+    return LRM_ERR_UNSUPPORTED;
+  if (lrm::noalloc_layout(*problem).total > lrm::kNoallocScratchBytes)
+    return LRM_ERR_WORKSPACE_TOO_SMALL;
+  return from_hip(lrm::launch_gemms_noalloc(*problem, Gc, Phic, W, cmp_off, dW, dphi, stream));
+}
+
 lrm_status lrm_swiglu_backward(const lrm_problem* problem, const int32_t* sel_row,
                                 const int32_t* cmp_off, const float* dphi, const void* ac,
                                 void* dH, void* ws, size_t ws_bytes, hipStream_t stream) {

@@ -30,6 +30,8 @@
 // Expert sizes stay on the device: schedules are built by one-workgroup kernels from cmp_off; a
 // zero-length segment writes zeros.  No atomics on the outputs (only on gemm_fused's unit
 // counters): every output element is owned by one workgroup, so results are bitwise deterministic.
+#include <mutex>
+
 #include "lrm_device.hpp"
 #include "lrm_internal.hpp"
 
@@ -672,7 +674,7 @@ constexpr int kDwJobCost = 8;
 
 __device__ __forceinline__ void dw_schedule_body(const int32_t* __restrict__ cmp_off, int E_loc,
                                                  int K_cap, int groups, int gpx,
-                                                 int32_t* __restrict__ sched) {
+                                                 int32_t* __restrict__ sched, int allow_split) {
   constexpr int kG = kMaxXcd * kMaxGroupsPerXcd;
   __shared__ int rows[1024], by_rank[1024];
   __shared__ int load[kG], first[kG], count[kG];
@@ -720,7 +722,7 @@ __device__ __forceinline__ void dw_schedule_body(const int32_t* __restrict__ cmp
   __syncthreads();
   int worst = 0;
   for (int g = 0; g < groups; ++g) worst = load[g] > worst ? load[g] : worst;
-  const bool fill = (int64_t)worst * 4 > (int64_t)T * 5 && groups - 1 <= kMaxDwSlots;
+  const bool fill = allow_split && (int64_t)worst * 4 > (int64_t)T * 5 && groups - 1 <= kMaxDwSlots;
   const int64_t jpg = dw_jobs_per_group(E_loc);
   auto put = [&](int g, int idx, int kb, int kend, int slot) {
     int32_t* jb = sched + kDwHeader + (int64_t)g * jpg * 4 + 4 * idx;
@@ -985,7 +987,7 @@ __device__ __forceinline__ void dx_schedule_body(const int32_t* __restrict__ cmp
 __global__ __launch_bounds__(1024) void dw_schedule(const int32_t* __restrict__ cmp_off, int E_loc,
                                                     int K_cap, int groups, int gpx,
                                                     int32_t* __restrict__ sched) {
-  dw_schedule_body(cmp_off, E_loc, K_cap, groups, gpx, sched);
+  dw_schedule_body(cmp_off, E_loc, K_cap, groups, gpx, sched, 1);
 }
 
 __global__ __launch_bounds__(1024) void dx_schedule(const int32_t* __restrict__ cmp_off, int E_loc,
@@ -997,15 +999,16 @@ __global__ __launch_bounds__(1024) void dx_schedule(const int32_t* __restrict__ 
 
 // Both schedules of the one-launch GEMMs in one launch of two workgroups: workgroup 0 builds the
 // dW job lists, workgroup 1 the dphi tile table (and resets the unit counters); they write
-// disjoint workspace regions.
+// disjoint workspace regions.  allow_split = 0 keeps every expert whole (no partial slots).
 __global__ __launch_bounds__(1024) void gemm_schedules(const int32_t* __restrict__ cmp_off,
                                                        int E_loc, int K_cap, int groups, int gpx,
                                                        int32_t* __restrict__ sched, int tm,
                                                        int64_t max_tiles,
                                                        int32_t* __restrict__ tiles,
-                                                       int32_t* __restrict__ queue) {
+                                                       int32_t* __restrict__ queue,
+                                                       int allow_split) {
   if (blockIdx.x == 0)
-    dw_schedule_body(cmp_off, E_loc, K_cap, groups, gpx, sched);
+    dw_schedule_body(cmp_off, E_loc, K_cap, groups, gpx, sched, allow_split);
   else
     dx_schedule_body(cmp_off, E_loc, K_cap, tm, max_tiles, tiles, queue);
 }
@@ -1077,6 +1080,7 @@ void launch_dw_t(const lrm_problem& p, const void* Gc, const void* Phic, const i
                      p.h, p.d, slots, dW);
 }
 
+// slots == nullptr: experts are never split along K (no partial slots, no fix-up launch).
 template <class CW, class CX, int kLayer>
 void launch_fused_t(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
                     const int32_t* cmp_off, int32_t* sched, int32_t* tiles, int32_t* queue,
@@ -1085,12 +1089,14 @@ void launch_fused_t(const lrm_problem& p, const void* Gc, const void* Phic, cons
   const int gpx = groups_per_die<CW>(p, g);
   static_assert(kThreadsPerSchedule == 1024, "one block shape for both schedules");
   hipLaunchKernelGGL(gemm_schedules, dim3(2), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap,
-                     g.nxcd * gpx, gpx, sched, CX::BM, max_tiles, tiles, queue);
+                     g.nxcd * gpx, gpx, sched, CX::BM, max_tiles, tiles, queue,
+                     slots != nullptr ? 1 : 0);
   hipLaunchKernelGGL((gemm_fused<CW, CX, stages_for<CW>(), kLayer>), dim3(g.blocks), dim3(CW::THREADS), 0,
                      s, (const uint16_t*)Gc, (const uint16_t*)Phic, (const uint16_t*)W, cmp_off,
                      sched, tiles, queue, g.nxcd, p.E_loc, p.K_cap, p.h, p.d, dW, slots, dphi);
-  hipLaunchKernelGGL(dw_fixup, dim3(kMaxDwSlots * kFixupBlocks), dim3(256), 0, s, sched, p.E_loc,
-                     p.h, p.d, slots, dW);
+  if (slots != nullptr)
+    hipLaunchKernelGGL(dw_fixup, dim3(kMaxDwSlots * kFixupBlocks), dim3(256), 0, s, sched,
+                       p.E_loc, p.h, p.d, slots, dW);
 }
 
 template <class C>
@@ -1149,19 +1155,12 @@ hipError_t launch_dx(const lrm_problem& p, const void* Gc, const void* W, const 
   return hipGetLastError();
 }
 
+// The one-launch bf16 GEMMs on explicit schedule buffers (slots == nullptr: no expert splits).
 template <int kLayer>
-hipError_t launch_gemms_t(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
-                          const int32_t* cmp_off, float* dW, float* dphi, char* ws,
-                          const WsLayout& wl, hipStream_t s) {
-  if (p.dtype != LRM_BF16) {
-    const hipError_t e = launch_dw(p, Gc, Phic, cmp_off, dW, ws, wl, s);
-    return e != hipSuccess ? e : launch_dx(p, Gc, W, cmp_off, dphi, ws, wl, s);
-  }
+void launch_fused_bf16(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
+                       const int32_t* cmp_off, float* dW, float* dphi, int32_t* sched,
+                       int32_t* tiles, int32_t* queue, float* slots, hipStream_t s) {
   const Grid g = persistent_grid();
-  int32_t* sched = (int32_t*)(ws + wl.order);
-  int32_t* tiles = (int32_t*)(ws + wl.tiles);
-  int32_t* queue = (int32_t*)(ws + wl.err) + kQueueWord;
-  float* slots = (float*)(ws + wl.dwslots);
   static_assert(TileW_dX::BM == Tile128_dX::BM && TileW_dX::BM >= kDxTileM, "row tile");
   const int64_t max_tiles = ((int64_t)p.K_cap + TileW_dX::BM - 1) / TileW_dX::BM + p.E_loc;
   switch (pick_width(p.d)) {
@@ -1170,6 +1169,19 @@ hipError_t launch_gemms_t(const lrm_problem& p, const void* Gc, const void* Phic
     case 2: launch_fused_t<Tile192_dW, Tile192_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
     default: launch_fused_t<Tile128_dW, Tile128_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
   }
+}
+
+template <int kLayer>
+hipError_t launch_gemms_t(const lrm_problem& p, const void* Gc, const void* Phic, const void* W,
+                          const int32_t* cmp_off, float* dW, float* dphi, char* ws,
+                          const WsLayout& wl, hipStream_t s) {
+  if (p.dtype != LRM_BF16) {
+    const hipError_t e = launch_dw(p, Gc, Phic, cmp_off, dW, ws, wl, s);
+    return e != hipSuccess ? e : launch_dx(p, Gc, W, cmp_off, dphi, ws, wl, s);
+  }
+  launch_fused_bf16<kLayer>(p, Gc, Phic, W, cmp_off, dW, dphi, (int32_t*)(ws + wl.order),
+                            (int32_t*)(ws + wl.tiles), (int32_t*)(ws + wl.err) + kQueueWord,
+                            (float*)(ws + wl.dwslots), s);
   return hipGetLastError();
 }
 
@@ -1178,6 +1190,87 @@ hipError_t launch_gemms(const lrm_problem& p, const void* Gc, const void* Phic, 
                         const WsLayout& wl, hipStream_t s, int layer) {
   return layer == 1 ? launch_gemms_t<1>(p, Gc, Phic, W, cmp_off, dW, dphi, ws, wl, s)
                     : launch_gemms_t<2>(p, Gc, Phic, W, cmp_off, dW, dphi, ws, wl, s);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Allocation-free variant of the FC2 GEMMs (lrm_grouped_dw_dx_noalloc).
+//
+// The only scratch the one-launch GEMMs need besides the caller's buffers is the schedule: the dW
+// job lists, the dphi tile table and the per-die unit counters.  Here it lives in `scratch`, a
+// file-scope device array of kNoallocScratchBytes that each GPU holds for the life of the
+// process.  In host code `scratch` names a host-side stand-in; its device address on the current
+// GPU is looked up once per device with hipGetSymbolAddress and only that address is passed to
+// kernels.  Experts are never split along K in this variant (splitting needs h x d float32
+// partial slots per split piece), so there is no fix-up launch.  Every call rewrites the schedule
+// and the schedule kernel resets the counters; calls that overlap on one GPU share the array and
+// race.
+// ------------------------------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+char* g_scratch_addr[kMaxDevices] = {};
+
+hipError_t scratch_address(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = (char*)ptr;
+  }
+  *out = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+NoallocLayout noalloc_layout(const lrm_problem& p) {
+  NoallocLayout l{};
+  const int tm = p.dtype == LRM_BF16 ? TileW_dX::BM : FBM;
+  l.max_tiles = ((int64_t)p.K_cap + tm - 1) / tm + p.E_loc;
+  size_t off = 0;
+  l.queue = off;
+  off += 256;
+  l.sched = off;
+  off = align_up(off + (size_t)(kDwHeader + (int64_t)kMaxXcd * kMaxGroupsPerXcd *
+                                             dw_jobs_per_group(p.E_loc) * 4) * 4, 256);
+  l.tiles = off;
+  off = align_up(off + (size_t)(1 + 2 * l.max_tiles) * 4, 256);
+  l.total = off;
+  return l;
+}
+
+hipError_t launch_gemms_noalloc(const lrm_problem& p, const void* Gc, const void* Phic,
+                                const void* W, const int32_t* cmp_off, float* dW, float* dphi,
+                                hipStream_t s) {
+  const NoallocLayout l = noalloc_layout(p);
+  if (l.total > kNoallocScratchBytes) return hipErrorInvalidValue;  // checked by the caller too
+  char* base = nullptr;
+  const hipError_t e = scratch_address(&base);
+  if (e != hipSuccess) return e;
+  int32_t* sched = (int32_t*)(base + l.sched);
+  int32_t* tiles = (int32_t*)(base + l.tiles);
+  int32_t* queue = (int32_t*)(base + l.queue);
+  if (p.dtype == LRM_BF16) {
+    launch_fused_bf16<2>(p, Gc, Phic, W, cmp_off, dW, dphi, sched, tiles, queue, nullptr, s);
+  } else {
+    const dim3 gw((p.d + FBN - 1) / FBN, (p.h + FBM - 1) / FBM, p.E_loc);
+    hipLaunchKernelGGL(dw_f32, gw, dim3(kF32Threads), 0, s, (const float*)Gc, (const float*)Phic,
+                       cmp_off, p.K_cap, p.h, p.d, dW);
+    hipLaunchKernelGGL(dx_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, FBM,
+                       l.max_tiles, tiles, nullptr);
+    const dim3 gx((unsigned)l.max_tiles, (p.d + FBN - 1) / FBN);
+    hipLaunchKernelGGL(dx_f32, gx, dim3(kF32Threads), 0, s, (const float*)Gc, (const float*)W,
+                       cmp_off, tiles, p.K_cap, p.h, p.d, dphi);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace lrm

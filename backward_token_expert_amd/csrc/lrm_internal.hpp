@@ -76,6 +76,22 @@ inline WsLayout ws_layout(const lrm_problem& p) {
   return w;
 }
 
+// Allocation-free FC2 GEMMs: the schedule lives in a static device array of this many bytes (one
+// per GPU), laid out as below; devices with ids up to kMaxDevices - 1 are supported.
+constexpr size_t kNoallocScratchBytes = size_t(1) << 20;
+constexpr int kMaxDevices = 64;
+struct NoallocLayout {
+  size_t queue;   // int32 [kMaxXcd] unit counters of the one-launch kernel
+  size_t sched;   // int32 dW schedule (header, per-group job lists)
+  size_t tiles;   // int32 [1 + 2*max_tiles] dphi tile table
+  size_t total;
+  int64_t max_tiles;
+};
+NoallocLayout noalloc_layout(const lrm_problem& p);
+hipError_t launch_gemms_noalloc(const lrm_problem& p, const void* Gc, const void* Phic,
+                                const void* W, const int32_t* cmp_off, float* dW, float* dphi,
+                                hipStream_t s);
+
 // Kernel launchers (one per translation unit).  Each returns the hipError_t of its launches.
 hipError_t launch_plan(const lrm_problem& p, const lrm_quota_policy& pol, const int32_t* topk_idx,
                        int32_t* counts, int32_t* fwd_off, int32_t* row_pair, int32_t* quota,

@@ -23,7 +23,7 @@ EXPORTS = ("lrm_workspace_bytes", "lrm_plan_quotas", "lrm_admit_quotas", "lrm_sc
            "lrm_select", "lrm_compact", "lrm_grouped_dw", "lrm_grouped_dx", "lrm_grouped_dw_dx",
            "lrm_swiglu_backward", "lrm_gather_tokens", "lrm_grouped_fc1_dw", "lrm_grouped_fc1_dx",
            "lrm_grouped_fc1_dw_dx", "lrm_scatter_tokens", "lrm_read_device_error",
-           "lrm_status_string")
+           "lrm_status_string", "lrm_grouped_dw_dx_noalloc")
 
 QUOTA_KINDS = {"cap": 0, "proportional": 1, "waterfill": 2}
 CRITERIA = {"lrm": 0, "grad_sq": 1, "grad_abs": 2, "random": 3}
@@ -97,6 +97,7 @@ def load_library(path: Optional[str] = None):
     lib.lrm_grouped_dw.argtypes = [PP] + [vp] * 5 + [sz, vp]
     lib.lrm_grouped_dx.argtypes = [PP] + [vp] * 5 + [sz, vp]
     lib.lrm_grouped_dw_dx.argtypes = [PP] + [vp] * 7 + [sz, vp]
+    lib.lrm_grouped_dw_dx_noalloc.argtypes = [PP] + [vp] * 6 + [vp]
     lib.lrm_swiglu_backward.argtypes = [PP] + [vp] * 6 + [sz, vp]
     lib.lrm_gather_tokens.argtypes = [PP] + [vp] * 5 + [sz, vp]
     lib.lrm_grouped_fc1_dw.argtypes = [PP] + [vp] * 5 + [sz, vp]
@@ -226,6 +227,14 @@ def lrm_grouped_dw_dx(problem, Gc, Phic, W, cmp_off, dW, dphi, ws, stream=None):
                                       _ptr(cmp_off), _ptr(dW), _ptr(dphi), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream)),
            "lrm_grouped_dw_dx")
+
+
+def lrm_grouped_dw_dx_noalloc(problem, Gc, Phic, W, cmp_off, dW, dphi, stream=None):
+    lib = load_library()
+    _check(lib, lib.lrm_grouped_dw_dx_noalloc(ctypes.byref(problem), _ptr(Gc), _ptr(Phic), _ptr(W),
+                                              _ptr(cmp_off), _ptr(dW), _ptr(dphi),
+                                              _stream(stream)),
+           "lrm_grouped_dw_dx_noalloc")
 
 
 def lrm_admit_quotas(problem, admission, fwd_off, quota, cmp_off, admitted, ws, stream=None):

@@ -361,6 +361,27 @@ lrm_status lrm_grouped_dw_dx(const lrm_problem* problem, const void* Gc, const v
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * lrm_grouped_dw_dx without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Computes dW and
+ * dphi as lrm_grouped_dw_dx does, from the same inputs, but never splits an expert's rows across
+ * workgroup groups, so where lrm_grouped_dw_dx would split (strongly skewed expert sizes) dW may
+ * differ from it in rounding; elsewhere the results are equal bit for bit.
+ *  - The GEMM schedule lives in a static device array of 1 MiB that each GPU holds until the
+ *    process ends.  Problems whose schedule does not fit return LRM_ERR_WORKSPACE_TOO_SMALL
+ *    without enqueuing anything: at E_loc = 16 that is K_cap above 33,001,216 rows (bf16) or
+ *    8,250,304 rows (fp32); more local experts lower the bound (about 1.6e7 bf16 rows at
+ *    E_loc = 1024).
+ *  - The call itself allocates nothing; its first call on a device looks up the array's device
+ *    address (make that first call outside graph capture).
+ *  - All calls on one GPU share the array: calls that overlap on one GPU (different streams
+ *    without ordering) race and give undefined results.  Calls ordered on one stream are safe.
+ * Arguments, layouts and alignment requirements as lrm_grouped_dw_dx.
+ */
+lrm_status lrm_grouped_dw_dx_noalloc(const lrm_problem* problem, const void* Gc, const void* Phic,
+                                     const void* W, const int32_t* cmp_off, float* dW,
+                                     float* dphi, hipStream_t stream);
+
+/*
  * Backward of the SwiGLU activation over the retained rows (LRMoE Sec. 3.1: the activation
  * function uses the same retained identities as FC2).  For i < K, with r = sel_row[i], a =
  * ac[r][0:d], c = ac[r][d:2d] and g = dphi[i] (float32, as lrm_grouped_dx writes it):

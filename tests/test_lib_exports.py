@@ -138,3 +138,17 @@ def test_admission_struct_and_validation_on_host():
     assert call(bte.make_admission(ok, 1 << 40, comm_per_row=(1 << 32) + 1)) == 1
     assert call(bte.make_admission(ok, 1 << 40), ws_bytes=1024) == 3
     assert lib.lrm_admit_quotas(P, None, fake, fake, fake, fake, fake, n, None) == 1
+
+
+def test_noalloc_gemm_rejects_problems_beyond_its_scratch_on_host():
+    # lrm_grouped_dw_dx_noalloc keeps its schedule in a 1 MiB static device buffer: a retained-row
+    # capacity whose tile table cannot fit is refused before any launch (WORKSPACE_TOO_SMALL, 3)
+    bte.load_library()
+    fake = 0x100000   # never dereferenced
+    P = lrm.make_problem(65536, 8, 128, 0, 16, 2048, 768, "bf16", 2 ** 25, 2 ** 26)
+    with pytest.raises(lrm.LrmError, match=r"\(status 3\)"):
+        lrm.lrm_grouped_dw_dx_noalloc(P, fake, fake, fake, fake, fake, fake, stream=0)
+    # null pointers are refused first (INVALID_ARGUMENT, 1)
+    Q = lrm.make_problem(4096, 8, 128, 0, 16, 2048, 768, "bf16", 32768, 32768)
+    with pytest.raises(lrm.LrmError, match=r"\(status 1\)"):
+        lrm.lrm_grouped_dw_dx_noalloc(Q, fake, None, fake, fake, fake, fake, stream=0)
