@@ -24,6 +24,7 @@ lrm_status check_problem(const lrm_problem* p) {
   if ((int64_t)p->T * p->k > INT32_MAX) return LRM_ERR_UNSUPPORTED;
   if (p->dtype != LRM_F32 && p->dtype != LRM_BF16) return LRM_ERR_UNSUPPORTED;
   if (p->h % 8 != 0 || p->d % 8 != 0) return LRM_ERR_UNSUPPORTED;
+  if (p->h > (1 << 23) || p->d > (1 << 23)) return LRM_ERR_UNSUPPORTED;
   if (p->E > 4096 || p->E_loc > 1024) return LRM_ERR_UNSUPPORTED;
   return LRM_OK;
 }

@@ -31,6 +31,7 @@
 // zero-length segment writes zeros.  No atomics on the outputs (only on gemm_fused's unit
 // counters): every output element is owned by one workgroup, so results are bitwise deterministic.
 #include <mutex>
+#include <type_traits>
 
 #include "lrm_device.hpp"
 #include "lrm_internal.hpp"
@@ -103,9 +104,19 @@ __device__ __forceinline__ int swz_mnk(int row, int k) {
 // range.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, int64_t bytes) {
-  const int n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n, 0x00020000);
+constexpr int64_t kMaxWindow = 0x7FFFFFF0;
+
+// A wave-uniform pointer, held in scalar registers.
+__device__ __forceinline__ const char* uniform(const char* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Buffer resource over [base, base + bytes), bytes in [0, kMaxWindow].
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
 }
 
 // The load is written as inline assembly: the compiler then does not track it as an LDS write
@@ -233,14 +244,23 @@ __device__ __forceinline__ bf16x8 read_b(uint32_t st, const FragOffsets<C>& f, i
 // fragment a0c already in registers), reading the current slice's later A rows just ahead of their
 // use and the next slice's fragments (bn, a0n) along the way, so at most 2 NT + 2 fragments are
 // live.  Scheduling groups alternate one MFMA with LDS reads, so the reads hide behind the matrix
-// work.
-template <class C, int HC, int HN, int NT>
+// work.  `hook` runs once, after the MFMAs of the first A row have been issued (the second half
+// step issues the ring's next loads there, behind matrix work instead of in front of it); a
+// wavefront without live column sub-tiles (NT = 0) only runs the hook.
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+template <class C, int HC, int HN, int NT, class Hook>
 __device__ __forceinline__ void half_step(uint32_t sc, uint32_t sn, const FragOffsets<C>& fo,
                                           const bf16x8 (&bc)[C::NT], const bf16x8& a0c,
                                           bf16x8 (&bn)[C::NT], bf16x8& a0n,
-                                          f32x16 (&acc)[C::MT][C::NT]) {
+                                          f32x16 (&acc)[C::MT][C::NT], const Hook& hook) {
   // NT (<= C::NT): the live column sub-tiles; the dead ones are neither read nor multiplied
   constexpr int MT = C::MT;
+  constexpr int kReadA = C::AKMN ? 2 : 1;   // LDS read instructions per A fragment
+  constexpr int kReads = kReadA * MT + 2 * NT;  // LDS read instructions per slice
+  constexpr bool kHook = !std::is_same<Hook, NoHook>::value;
   if constexpr (NT > 0) {
     bf16x8 a = a0c;
 #pragma unroll
@@ -255,15 +275,40 @@ __device__ __forceinline__ void half_step(uint32_t sc, uint32_t sn, const FragOf
       for (int j = 0; j < NT; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bc[j], acc[i][j], 0, 0, 0);
       if (i + 1 < MT) a = an;
-    }
-    constexpr int kReads = (C::AKMN ? 2 : 1) * MT + 2 * NT;  // LDS read instructions per slice
-    constexpr int kMfma = MT * NT;
-    constexpr int per = (kReads + kMfma - 1) / kMfma;
+      if (kHook && i == 0) {
+        // LDS reads issued with row 0: A row 1 and the B fragments dealt to row 0
+        constexpr int r0 = (MT > 1 ? kReadA : 0) + 2 * ((NT + MT - 1) / MT);
+        constexpr int per0 = (r0 + NT - 1) / NT;
 #pragma unroll
-    for (int q = 0; q < kMfma; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+        for (int q = 0; q < NT; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, per0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        hook();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
+    if constexpr (kHook && MT > 1) {
+      constexpr int r1 = kReads - ((MT > 1 ? kReadA : 0) + 2 * ((NT + MT - 1) / MT));
+      constexpr int kMfma = (MT - 1) * NT;
+      constexpr int per = (r1 + kMfma - 1) / kMfma;
+#pragma unroll
+      for (int q = 0; q < kMfma; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+      }
+    } else if constexpr (!kHook) {
+      constexpr int kMfma = MT * NT;
+      constexpr int per = (kReads + kMfma - 1) / kMfma;
+#pragma unroll
+      for (int q = 0; q < kMfma; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, per, 0);
+      }
+    }
+  } else {
+    hook();
   }
 }
 
@@ -336,40 +381,53 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Issues the DMA loads of one K step.  kmn operands move their buffer window down the K rows; the
 // [mn][k] operand moves its window along the rows and masks the chunks past kend when the step is
 // partial.  Past the end of the K range every load falls outside its window and writes zeros.
+// prepare() forms the next step's buffer resources (scalar work only), fire() issues its loads,
+// advance() moves to the step after; the mainloop places the scalar work where matrix work hides
+// it.
 template <class C>
 struct Loader {
   uint32_t oa[C::IA], ob[C::IB];
   int kca[C::IA];
-  const char* pa;  // window starts for the next step
+  const char* pa;  // window bases of the next step
   const char* pb;
-  int64_t ra, rb;  // bytes left in each window
-  int64_t sa, sb;  // bytes the windows move per step
+  int64_t sa, sb;  // bytes the bases move per step
+  int rowa, rowb;  // [k][mn] operands: bytes per K row
+  int ra;          // [mn][k] A: bytes from pa to the end of the tile's last row (<= kMaxWindow)
   int k0, kend;
+  int na, nb;      // window bytes of the next step (prepare())
 
   __device__ __forceinline__ void init(const Operands& o, int w, int lane) {
     if constexpr (C::AKMN) {
       dma_offs_kmn<C::BM, C::IA>(o.lda, o.a_mn0, o.a_mnend, w, lane, oa);
       pa = (const char*)(o.A + (int64_t)o.kbeg * o.lda);
-      ra = (int64_t)(o.kend - o.kbeg) * o.lda * 2;
+      rowa = (int)(o.lda * 2);
       sa = (int64_t)kBK * o.lda * 2;
     } else {
       dma_offs_mnk<C::IA>(o.lda, w, lane, oa, kca);
       pa = (const char*)(o.A + (int64_t)o.a_mn0 * o.lda + o.kbeg);
-      ra = (int64_t)(o.a_mnend - o.a_mn0) * o.lda * 2 - (int64_t)o.kbeg * 2;
+      const int64_t r = (int64_t)(o.a_mnend - o.a_mn0) * o.lda * 2 - (int64_t)o.kbeg * 2;
+      ra = (int)(r <= 0 ? 0 : (r > kMaxWindow ? kMaxWindow : r));
       sa = kBK * 2;
     }
     dma_offs_kmn<C::BN, C::IB>(o.ldb, o.b_mn0, o.b_mnend, w, lane, ob);
     pb = (const char*)(o.B + (int64_t)o.kbeg * o.ldb);
-    rb = (int64_t)(o.kend - o.kbeg) * o.ldb * 2;
+    rowb = (int)(o.ldb * 2);
     sb = (int64_t)kBK * o.ldb * 2;
     k0 = o.kbeg;
     kend = o.kend;
   }
 
+  __device__ __forceinline__ void prepare() {
+    int rows = kend - k0;
+    rows = rows < 0 ? 0 : (rows > kBK ? kBK : rows);
+    na = C::AKMN ? rows * rowa : ra;
+    nb = rows * rowb;
+  }
+
   // wa / wb: LDS byte addresses of this wave's first 1 KiB block of the A / B part of the stage.
-  __device__ __forceinline__ void issue(uint32_t wa, uint32_t wb) {
-    const __amdgpu_buffer_rsrc_t r_a = make_rsrc((const uint16_t*)pa, ra);
-    const __amdgpu_buffer_rsrc_t r_b = make_rsrc((const uint16_t*)pb, rb);
+  __device__ __forceinline__ void fire(uint32_t wa, uint32_t wb) const {
+    const __amdgpu_buffer_rsrc_t r_a = make_rsrc(uniform(pa), __builtin_amdgcn_readfirstlane(na));
+    const __amdgpu_buffer_rsrc_t r_b = make_rsrc(uniform(pb), __builtin_amdgcn_readfirstlane(nb));
     if (C::AKMN || k0 + kBK <= kend) {
       static_for<C::IA>([&](auto j) { dma16<decltype(j)::value * 1024>(r_a, wa, oa[decltype(j)::value]); });
     } else {
@@ -379,10 +437,12 @@ struct Loader {
       });
     }
     static_for<C::IB>([&](auto j) { dma16<decltype(j)::value * 1024>(r_b, wb, ob[decltype(j)::value]); });
+  }
+
+  __device__ __forceinline__ void advance() {
     pa += sa;
     pb += sb;
-    ra = ra > sa ? ra - sa : 0;
-    rb = rb > sb ? rb - sb : 0;
+    if constexpr (!C::AKMN) ra = ra > kBK * 2 ? ra - kBK * 2 : 0;
     k0 += kBK;
   }
 };
@@ -411,7 +471,12 @@ __device__ __forceinline__ void mainloop(const Operands& o, uint32_t ring, const
   // this wave's first DMA block inside a stage, for the A and the B part
   const uint32_t blk_a = w * C::IA * 1024, blk_b = R::A_BYTES + w * C::IB * 1024;
 #pragma unroll
-  for (int st = 0; st < S - 1; ++st) ld.issue(ring + st * R::STG + blk_a, ring + st * R::STG + blk_b);
+  for (int st = 0; st < S - 1; ++st) {
+    ld.prepare();
+    ld.fire(ring + st * R::STG + blk_a, ring + st * R::STG + blk_b);
+    ld.advance();
+  }
+  ld.prepare();
   wait_vm<(S - 2) * I>();
   lds_barrier();
   uint32_t rd = ring;                        // stage kt
@@ -424,18 +489,21 @@ __device__ __forceinline__ void mainloop(const Operands& o, uint32_t ring, const
   }
   for (int kt = 0; kt < nk; ++kt) {
     // first half: slice 0 of stage kt; reads slice 1 of the same stage
-    half_step<C, 0, 1, NTA>(rd, rd, fo, bA, aA, bB, aB, acc);
+    half_step<C, 0, 1, NTA>(rd, rd, fo, bA, aA, bB, aB, acc, NoHook{});
     __builtin_amdgcn_sched_barrier(0);
     // middle: stage kt+1 complete for every wave; stage kt-1 free
     wait_vm<(S - 3) * I>();
     lds_barrier();
-    ld.issue(wr + blk_a, wr + blk_b);
     const uint32_t rn = rd + R::STG == ring + R::BYTES ? ring : rd + R::STG;
+    __builtin_amdgcn_sched_barrier(0);
+    // second half: slice 1 of stage kt; reads slice 0 of stage kt+1 (unused after the last
+    // step); the loads of step kt+S-1 into stage kt-1 go out after its first A row's MFMAs
+    const uint32_t wa = wr + blk_a, wb = wr + blk_b;
+    half_step<C, 1, 0, NTA>(rd, rn, fo, bB, aB, bA, aA, acc, [&] { ld.fire(wa, wb); });
+    __builtin_amdgcn_sched_barrier(0);
+    ld.advance();
+    ld.prepare();
     wr = wr + R::STG == ring + R::BYTES ? ring : wr + R::STG;
-    __builtin_amdgcn_sched_barrier(0);
-    // second half: slice 1 of stage kt; reads slice 0 of stage kt+1 (unused after the last step)
-    half_step<C, 1, 0, NTA>(rd, rn, fo, bB, aB, bA, aA, acc);
-    __builtin_amdgcn_sched_barrier(0);
     rd = rn;
   }
   wait_vm<0>();

@@ -72,18 +72,17 @@ def stats_table(path: str) -> str:
 
 
 def read_counters(root: str):
-    """{kernel: {counter: [per-dispatch values]}} and the per-dispatch durations (ns)."""
+    """{kernel: {counter: [per-dispatch values]}} and {kernel: {counter: [per-dispatch durations
+    (ns) of the dispatches that counter was read on]}}."""
     vals = collections.defaultdict(lambda: collections.defaultdict(list))
-    durs = collections.defaultdict(list)
+    durs = collections.defaultdict(lambda: collections.defaultdict(list))
     for f in sorted(glob.glob(os.path.join(root, "p*", "*counter_collection.csv"))):
-        seen = set()
         for r in csv.DictReader(open(f)):
             n = short_name(r["Kernel_Name"])
             vals[n][r["Counter_Name"]].append(float(r["Counter_Value"]))
-            key = (f, r["Dispatch_Id"])
-            if key not in seen and "Start_Timestamp" in r:
-                seen.add(key)
-                durs[n].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            if "Start_Timestamp" in r:
+                durs[n][r["Counter_Name"]].append(
+                    int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     return vals, durs
 
 
@@ -102,9 +101,11 @@ def counters_report(root: str, copy_bytes: int, workload: str):
     lines = [f"Copy calibration: a {copy_bytes} B copy reads FETCH_SIZE {cf:.0f} KiB and "
              f"WRITE_SIZE {cw:.0f} KiB, so FETCH_SIZE x {fs:.3f} and WRITE_SIZE x {ws:.3f} give "
              "bytes.", "",
-             "| kernel | dispatches | MFMA busy % | wait-inst % | L2 hit % | LDS bank conflicts | "
-             "FETCH KiB | WRITE KiB | HBM MB (calibrated) |",
-             "|---|---|---|---|---|---|---|---|---|"]
+             "Clock: GRBM_GUI_ACTIVE (GPU cycles, summed over the 8 XCDs) / 8 / the dispatch's "
+             "duration.", "",
+             "| kernel | dispatches | clock MHz | MFMA busy % | wait-inst % | L2 hit % | "
+             "LDS bank conflicts | FETCH KiB | WRITE KiB | HBM MB (calibrated) |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
 
     def avg(d, c):
         v = d.get(c)
@@ -124,16 +125,21 @@ def counters_report(root: str, copy_bytes: int, workload: str):
         hit, miss = avg(d, "TCC_HIT_sum"), avg(d, "TCC_MISS_sum")
         fe, wr = avg(d, "FETCH_SIZE"), avg(d, "WRITE_SIZE")
         conf = avg(d, "SQ_LDS_BANK_CONFLICT")
+        dd = durs.get(k, {}).get("GRBM_GUI_ACTIVE", [])
+        clk = (sum(d["GRBM_GUI_ACTIVE"]) / 8 / sum(dd) * 1e3
+               if gui and dd and sum(dd) > 0 else None)
         mb = (fe * 1024 * fs + wr * 1024 * ws) / 1e6 if fe is not None and wr is not None else None
         f = lambda x, p=1: "–" if x is None else f"{x:.{p}f}"
         n = max((len(v) for v in d.values()), default=0)
-        lines.append(f"| {k} | {n} | {f(mfp)} | {f(100 * wi / wc if wi is not None and wc else None)} | "
+        lines.append(f"| {k} | {n} | {f(clk, 0)} | {f(mfp)} | "
+                     f"{f(100 * wi / wc if wi is not None and wc else None)} | "
                      f"{f(100 * hit / (hit + miss) if hit is not None and miss is not None else None)} | "
                      f"{f(conf, 0)} | {f(fe, 0)} | {f(wr, 0)} | {f(mb)} |")
         for call, (names, _) in GEMM_KERNELS.items():
             if re.match(names, k) and mb is not None:
                 rec["kernels"][call] = {"kernel": k, "traffic_bytes": mb * 1e6,
                                         "fetch_bytes": fe * 1024 * fs, "write_bytes": wr * 1024 * ws,
+                                        "clock_mhz": clk, "mfma_busy_pct": mfp,
                                         "source_sha256": source_digest(call)}
     return "\n".join(lines), rec
 

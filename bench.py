@@ -355,7 +355,8 @@ def gemm_clock_sample(launch, ms_per_call, seconds=1.0):
         return {"error": "no clock readings"}
     # drop the first readings (the launches ramp up) and take the median
     use = samples[len(samples) // 5:] or samples
-    return {"MHz_median": float(np.median(use)), "samples": len(use), "source": sorted(src),
+    return {"MHz_median": float(np.median(use)), "MHz_p10": float(np.percentile(use, 10)),
+            "MHz_p90": float(np.percentile(use, 90)), "samples": len(use), "source": sorted(src),
             "calls": n}
 
 
@@ -554,10 +555,10 @@ def cpu_baseline(w, pol_dict, n_experts, min_seconds, criterion="lrm", threads=N
                       f"{dt:.1f} s"}
 
 
-def recorded_traffic(call, workload):
-    """HBM bytes per launch of `call`'s kernel from the committed rocprofv3 counter summaries
-    (profiles/*.md, `traffic-record:` lines), or None when no record matches the workload and
-    the current sources of the kernel."""
+def recorded_counters(call, workload):
+    """The committed rocprofv3 counter record (profiles/*.md, `traffic-record:` lines) of `call`'s
+    kernel on `workload` -- HBM bytes per launch, the clock during the kernel, MFMA busy -- or
+    None when no record matches the workload and the current sources of the kernel."""
     import glob
     from backward_token_expert_amd.rocprof_summary import source_digest
     here = os.path.dirname(os.path.abspath(__file__))
@@ -569,8 +570,14 @@ def recorded_traffic(call, workload):
             rec = json.loads(line[len("traffic-record: "):])
             k = rec.get("kernels", {}).get(call)
             if rec.get("workload") == workload and k and k.get("source_sha256") == digest:
-                return k["traffic_bytes"]
+                return k
     return None
+
+
+def recorded_traffic(call, workload):
+    """HBM bytes per launch of `call`'s kernel from the committed counter record, or None."""
+    k = recorded_counters(call, workload)
+    return None if k is None else k["traffic_bytes"]
 
 
 def fractions(st, a, dtype, clock_mhz=None):
@@ -651,12 +658,20 @@ def main():
         dom_call = {"dw": "lrm_grouped_dw", "dx": "lrm_grouped_dx"}[dom]
         ach = alg["flops_" + dom] / (stages[dom] * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[sp.dtype]
+    rec = recorded_counters(dom_call, sp.name)
     roof = {"bound": "mfma", "kernel": dom_call, "achieved": ach, "peak": peak,
             "unit": "TFLOP/s", "frac": ach / peak,
-            "traffic": recorded_traffic(dom_call, sp.name)}
+            "traffic": None if rec is None else rec["traffic_bytes"]}
+    # the clock during this kernel: from its counter record (GPU cycles / duration), else the
+    # clock amdsmi reported while it ran
+    if rec is not None and rec.get("clock_mhz"):
+        clk, clk_src = rec["clock_mhz"], "rocprofv3 GRBM_GUI_ACTIVE / duration (profiles/)"
+    else:
+        clk_src = "amdsmi current_gfxclks while the kernel ran" if clk else None
     if clk:
         roof["frac_at_measured_clock"] = ach / (peak * clk / SPEC_CLOCK_MHZ)
         roof["measured_clock_MHz"] = clk
+        roof["clock_source"] = clk_src
     out = {
         "metric": METRIC,
         "value": L / (ms * 1e-3),

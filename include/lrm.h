@@ -67,8 +67,8 @@
  *  - Host-side validation returns LRM_ERR_INVALID_ARGUMENT (null pointer, non-positive sizes,
  *    k > E, e_lo + E_loc > E, rho_den <= 0, an unknown quota kind or criterion, caps too small
  *    for the problem) or
- *    LRM_ERR_UNSUPPORTED (pointer not 16-byte aligned, h or d not a multiple of 8, unknown dtype,
- *    E > 4096 or E_loc > 1024).  Launch failures return LRM_ERR_HIP.  Nothing is enqueued when a
+ *    LRM_ERR_UNSUPPORTED (pointer not 16-byte aligned, h or d not a multiple of 8 or above
+ *    2^23, unknown dtype, E > 4096 or E_loc > 1024).  Launch failures return LRM_ERR_HIP.  Nothing is enqueued when a
  *    call returns an error.
  *  - Device-detected violations set error bits instead of faulting; results are then unspecified
  *    but every access stays inside the buffers described here.
