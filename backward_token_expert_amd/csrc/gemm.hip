@@ -37,6 +37,15 @@
 #include "lrm_internal.hpp"
 
 namespace lrm {
+
+#ifdef LRM_TIMELINE
+// Profiling builds only (build.py defines=("LRM_TIMELINE",), see timeline.py): per-workgroup
+// timestamps of the one-launch GEMMs, from the 100 MHz clock: [0] start, [1] end of the dW share,
+// [2] exit, [3] dphi units claimed, then (start, unit) of the first kTimelineUnits units.
+constexpr int kTimelineWGs = 1024, kTimelineWords = 64, kTimelineUnits = 28;
+__device__ unsigned long long g_timeline[kTimelineWGs * kTimelineWords];
+#endif
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -608,29 +617,34 @@ __global__ __launch_bounds__(C::THREADS) void dw_bf16(const uint16_t* __restrict
   dw_jobs<C, S>(Gc, Phic, sched, nxcd, E_loc, K_cap, h, d, dW, slots, lds_addr(ring));
 }
 
-// dW of each split expert += its partial slots, in piece order (kFixupBlocks blocks per expert).
-constexpr int kFixupBlocks = 512;
+// dW of each split expert += its partial slots, in piece order.  A fixed grid of kFixupBlocks
+// workgroups strides over the split experts' elements (the expert loop is uniform), so the launch
+// is small when nothing is split -- the usual case -- and still spreads a split expert's h x d
+// elements over the whole chip.
+constexpr int kFixupBlocks = 1024;
 
 __global__ __launch_bounds__(256) void dw_fixup(const int32_t* __restrict__ sched, int E_loc,
                                                 int h, int d,
                                                 const float* __restrict__ slots,
                                                 float* __restrict__ dW) {
-  const int sp = blockIdx.x / kFixupBlocks, part = blockIdx.x % kFixupBlocks;
-  if (sp >= sched[2]) return;
-  const int e = sched[4 + 3 * sp], first = sched[5 + 3 * sp], extra = sched[6 + 3 * sp];
-  if (e < 0 || e >= E_loc || first < 0 || extra < 0 || first + extra > kMaxDwSlots) return;
+  const int nsplit = sched[2];
   const int64_t n4 = (int64_t)h * d / 4;
-  float4* out = (float4*)(dW + (int64_t)e * h * d);
-  for (int64_t q = (int64_t)part * 256 + threadIdx.x; q < n4; q += (int64_t)kFixupBlocks * 256) {
-    float4 v = out[q];
-    for (int k = 0; k < extra; ++k) {
-      const float4 a = ((const float4*)(slots + (int64_t)(first + k) * h * d))[q];
-      v.x += a.x;
-      v.y += a.y;
-      v.z += a.z;
-      v.w += a.w;
+  for (int sp = 0; sp < nsplit && sp < kMaxDwSlots; ++sp) {
+    const int e = sched[4 + 3 * sp], first = sched[5 + 3 * sp], extra = sched[6 + 3 * sp];
+    if (e < 0 || e >= E_loc || first < 0 || extra < 0 || first + extra > kMaxDwSlots) continue;
+    float4* out = (float4*)(dW + (int64_t)e * h * d);
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n4;
+         q += (int64_t)kFixupBlocks * 256) {
+      float4 v = out[q];
+      for (int k = 0; k < extra; ++k) {
+        const float4 a = ((const float4*)(slots + (int64_t)(first + k) * h * d))[q];
+        v.x += a.x;
+        v.y += a.y;
+        v.z += a.z;
+        v.w += a.w;
+      }
+      out[q] = v;
     }
-    out[q] = v;
   }
 }
 
@@ -702,7 +716,15 @@ __global__ __launch_bounds__(CW::THREADS) void gemm_fused(
   // barrier below
   volatile int* claimed = (volatile int*)ring;
   const uint32_t ring_addr = lds_addr(ring);
+#ifdef LRM_TIMELINE
+  unsigned long long* stamp = g_timeline + (size_t)(blockIdx.x % kTimelineWGs) * kTimelineWords;
+  if (threadIdx.x == 0) stamp[0] = __builtin_amdgcn_s_memrealtime();
+#endif
   dw_jobs<CW, S>(Gc, Phic, sched, nxcd, E_loc, K_cap, h, d, dW, slots, ring_addr);
+#ifdef LRM_TIMELINE
+  if (threadIdx.x == 0) stamp[1] = __builtin_amdgcn_s_memrealtime();
+  int claims = 0;
+#endif
   const int tn = (d + CX::BN - 1) / CX::BN;
   const int total = tiles[0] * tn, per = (total + nxcd - 1) / nxcd;
   const int x = blockIdx.x % nxcd;
@@ -723,8 +745,21 @@ __global__ __launch_bounds__(CW::THREADS) void gemm_fused(
     const int u = __builtin_amdgcn_readfirstlane(*claimed);
     __syncthreads();
     if (u < 0) break;
+#ifdef LRM_TIMELINE
+    if (threadIdx.x == 0 && claims < kTimelineUnits) {
+      stamp[4 + 2 * claims] = __builtin_amdgcn_s_memrealtime();
+      stamp[5 + 2 * claims] = (unsigned long long)u;
+    }
+    ++claims;
+#endif
     dx_unit<CX, S>(Gc, W, cmp_off, tiles, u, K_cap, h, d, dphi, ring_addr, acc);
   }
+#ifdef LRM_TIMELINE
+  if (threadIdx.x == 0) {
+    stamp[2] = __builtin_amdgcn_s_memrealtime();
+    stamp[3] = (unsigned long long)claims;
+  }
+#endif
 }
 
 // dW schedule (one workgroup, one thread per expert rank).  A job (one expert, or a piece of one
@@ -1144,7 +1179,7 @@ void launch_dw_t(const lrm_problem& p, const void* Gc, const void* Phic, const i
   hipLaunchKernelGGL((dw_bf16<C, stages_for<C>()>), dim3(g.blocks), dim3(C::THREADS), 0, s,
                      (const uint16_t*)Gc, (const uint16_t*)Phic, sched, g.nxcd, p.E_loc, p.K_cap,
                      p.h, p.d, dW, slots);
-  hipLaunchKernelGGL(dw_fixup, dim3(kMaxDwSlots * kFixupBlocks), dim3(256), 0, s, sched, p.E_loc,
+  hipLaunchKernelGGL(dw_fixup, dim3(kFixupBlocks), dim3(256), 0, s, sched, p.E_loc,
                      p.h, p.d, slots, dW);
 }
 
@@ -1163,7 +1198,7 @@ void launch_fused_t(const lrm_problem& p, const void* Gc, const void* Phic, cons
                      s, (const uint16_t*)Gc, (const uint16_t*)Phic, (const uint16_t*)W, cmp_off,
                      sched, tiles, queue, g.nxcd, p.E_loc, p.K_cap, p.h, p.d, dW, slots, dphi);
   if (slots != nullptr)
-    hipLaunchKernelGGL(dw_fixup, dim3(kMaxDwSlots * kFixupBlocks), dim3(256), 0, s, sched,
+    hipLaunchKernelGGL(dw_fixup, dim3(kFixupBlocks), dim3(256), 0, s, sched,
                        p.E_loc, p.h, p.d, slots, dW);
 }
 
@@ -1274,6 +1309,17 @@ hipError_t launch_gemms(const lrm_problem& p, const void* Gc, const void* Phic, 
 // race.
 // ------------------------------------------------------------------------------------------------
 static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+#ifdef LRM_TIMELINE
+// Profiling builds only: copies the timestamp table (kTimelineWGs x kTimelineWords) to the host
+// after the device is idle.
+extern "C" int lrm_timeline_read(unsigned long long* host, size_t words) {
+  if (words > (size_t)kTimelineWGs * kTimelineWords) return 1;
+  if (hipDeviceSynchronize() != hipSuccess) return 2;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_timeline), words * 8, 0,
+                             hipMemcpyDeviceToHost) != hipSuccess ? 3 : 0;
+}
+#endif
 
 namespace {
 
