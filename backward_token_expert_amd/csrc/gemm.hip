@@ -21,7 +21,8 @@
 //        cut along K into pieces whose later partial sums dw_fixup adds in piece order), and a
 //        group walks the tiles of one job together, so every row of Gc/Phic is fetched from HBM
 //        once per group and the other tiles of that job hit in L2;
-//   dphi each die takes a contiguous range of (row tile, column tile) units, columns fastest, so
+//   dphi each die takes a contiguous range of (row tile, column tile) units (columns fastest, or
+//        blocked for wide products, see dx_unit), so
 //        a row tile's Gc rows and the expert's W stay in that die's L2; the one-launch kernel
 //        (gemm_fused) runs its dW share first and then claims dphi units from these ranges.
 // Global loads are issued S - 1 K steps ahead of their use through a ring of S LDS stages (S = 4
@@ -648,7 +649,9 @@ __global__ __launch_bounds__(256) void dw_fixup(const int32_t* __restrict__ sche
   }
 }
 
-// dphi units = (row tile from the tile table, column tile), columns fastest: unit u covers rows
+constexpr int kDxBlockRows = 8;
+
+// dphi units = (row tile from the tile table, column tile), blocked: unit u covers rows
 // [m0, min(m0 + BM, end of its expert's segment)) and columns [n0, n0 + BN).
 template <class C, int S>
 __device__ __forceinline__ void dx_unit(const uint16_t* __restrict__ Gc,
@@ -661,7 +664,15 @@ __device__ __forceinline__ void dx_unit(const uint16_t* __restrict__ Gc,
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), wm = w / C::WN, wn = w % C::WN;
   const FragOffsets<C> fo = frag_offsets<C>(wm, wn, lane);
-  const int mt = u / tn, n0 = (u % tn) * C::BN;
+  // Wide products (4 column tiles or more) take their units in blocks of kDxBlockRows row
+  // tiles -- within a block rows fastest, then columns -- so that the units in flight on a die
+  // span a few column panels of W and a block's row panels instead of every panel of W; narrower
+  // ones take columns fastest (blocks of one row).  The last block may have fewer rows.
+  const int rows = tiles[0];
+  const int R = tn >= 4 ? kDxBlockRows : 1;
+  const int blk = u / (R * tn), within = u - blk * R * tn;
+  const int rb = rows - blk * R < R ? rows - blk * R : R;
+  const int mt = blk * R + within % rb, n0 = (within / rb) * C::BN;
   const int e = tiles[1 + 2 * mt], m0 = tiles[2 + 2 * mt];
   int mend = cmp_off[e + 1];
   mend = mend > K_cap ? K_cap : mend;

@@ -72,6 +72,17 @@ def run(cfg: int, reps: int):
           "columns: median |")
     print("|---|---|---|---|---|---|---|---|---|")
     per_die = None
+    rows = int(sum((int(k) + 255) // 256 for k in np.diff(co)))
+
+    def col_of(u):
+        # the column tile of dphi unit u, as the kernel maps units (blocks of 8 row tiles, rows
+        # fastest, for 4 column tiles or more; columns fastest otherwise)
+        R = 8 if tn >= 4 else 1
+        blk = u // (R * tn)
+        within = u - blk * R * tn
+        rb = np.minimum(rows - blk * R, R)
+        return within // rb
+
     for rep in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -94,7 +105,7 @@ def run(cfg: int, reps: int):
                 te = us(t[i, 4 + 2 * (j + 1)]) if j + 1 < n else ex[i]
                 units.append((int(t[i, 5 + 2 * j]), te - ts))
         units = np.array(units) if units else np.zeros((0, 2))
-        dead = (units[:, 0] % tn == tn - 1) & (sp.d % 384 != 0) if tn else np.zeros(len(units), bool)
+        dead = (col_of(units[:, 0]) == tn - 1) & (sp.d % 384 != 0) if tn else np.zeros(len(units), bool)
         full = units[~dead, 1]
         part = units[dead, 1]
         fmt = lambda a, f: f"{f(a):.0f}" if len(a) else "-"  # noqa: E731
