@@ -42,8 +42,11 @@ namespace lrm {
 #ifdef LRM_TIMELINE
 // Profiling builds only (build.py defines=("LRM_TIMELINE",), see timeline.py): per-workgroup
 // timestamps of the one-launch GEMMs, from the 100 MHz clock: [0] start, [1] end of the dW share,
-// [2] exit, [3] dphi units claimed, then (start, unit) of the first kTimelineUnits units.
+// [2] exit, [3] dphi units claimed, then (start, unit) of the first kTimelineUnits units; words
+// 60 and 61 hold the shader-clock counter (s_memtime) at start and exit, the last two the hardware's
+// XCC_ID (the die) and HW_ID (CU, SIMD and shader engine) registers.
 constexpr int kTimelineWGs = 1024, kTimelineWords = 64, kTimelineUnits = 28;
+static_assert(4 + 2 * kTimelineUnits <= kTimelineWords - 4, "unit stamps end before the last four words");
 __device__ unsigned long long g_timeline[kTimelineWGs * kTimelineWords];
 #endif
 
@@ -729,7 +732,12 @@ __global__ __launch_bounds__(CW::THREADS) void gemm_fused(
   const uint32_t ring_addr = lds_addr(ring);
 #ifdef LRM_TIMELINE
   unsigned long long* stamp = g_timeline + (size_t)(blockIdx.x % kTimelineWGs) * kTimelineWords;
-  if (threadIdx.x == 0) stamp[0] = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    stamp[0] = __builtin_amdgcn_s_memrealtime();
+    stamp[kTimelineWords - 4] = __builtin_amdgcn_s_memtime();
+    stamp[kTimelineWords - 2] = __builtin_amdgcn_s_getreg((15 << 11) | 20);  // XCC_ID[15:0]
+    stamp[kTimelineWords - 1] = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID[31:0]
+  }
 #endif
   dw_jobs<CW, S>(Gc, Phic, sched, nxcd, E_loc, K_cap, h, d, dW, slots, ring_addr);
 #ifdef LRM_TIMELINE
@@ -769,6 +777,7 @@ __global__ __launch_bounds__(CW::THREADS) void gemm_fused(
   if (threadIdx.x == 0) {
     stamp[2] = __builtin_amdgcn_s_memrealtime();
     stamp[3] = (unsigned long long)claims;
+    stamp[kTimelineWords - 3] = __builtin_amdgcn_s_memtime();
   }
 #endif
 }

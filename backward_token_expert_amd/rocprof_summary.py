@@ -35,10 +35,31 @@ GEMM_KERNELS = {"lrm_grouped_dw": (r"(dw_bf16|dw_f32)\b", "gemm.hip"),
 _SHARED = ("lrm_device.hpp", "lrm_internal.hpp")
 
 
+def _without_profiling_blocks(text: str) -> str:
+    """Drop `#ifdef LRM_TIMELINE ... #endif` blocks (nesting-aware): they exist only in the
+    profiling build, so they do not change the kernels the counters were taken on."""
+    out, depth = [], 0
+    for line in text.splitlines():
+        t = line.strip()
+        if depth == 0 and t.startswith("#ifdef LRM_TIMELINE"):
+            depth = 1
+            continue
+        if depth > 0:
+            if t.startswith("#if"):
+                depth += 1
+            elif t.startswith("#endif"):
+                depth -= 1
+            continue
+        out.append(line)
+    return "\n".join(out)
+
+
 def _code_only(text: str) -> str:
-    """Source text without comments and blank space, so that comment edits keep the digest."""
+    """Source text without comments, blank space and profiling-build blocks, so that comment
+    edits and timeline instrumentation keep the digest."""
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
+    text = _without_profiling_blocks(text)
     return " ".join(text.split())
 
 

@@ -10,7 +10,9 @@ claims each dphi unit and when it exits.  `run` loads that build in place of lib
 path once on a workload, then times the GEMM call `--reps` times and prints a markdown summary:
 kernel span, when the dW shares end (per die), idle tail, and the dphi units' durations, split
 into units whose last column sub-tile is dead and the rest.  The timestamps cost one scalar
-clock read and one store per event, a few per unit of 100-250 us.
+clock read and one store per event, a few per unit of 100-250 us.  The run also reports which die
+and CU each workgroup ran on (the XCC_ID and HW_ID registers, read once at its start) and the
+shader clock over its life (s_memtime cycles over the 100 MHz clock's elapsed time).
 """
 from __future__ import annotations
 
@@ -118,6 +120,21 @@ def run(cfg: int, reps: int):
         per_die = [float(np.median(dwe[x == k])) for k in range(8)]
     print(f"\ndW share end per die (median over its workgroups, last rep): "
           f"{[round(v) for v in per_die]}")
+    # where the workgroups ran: XCC_ID is the die; HW_ID bits 8-15 hold the CU, shader array and
+    # shader engine ids
+    xcc = (t[:, WORDS - 2] & 0xF).astype(int)
+    cu = ((t[:, WORDS - 1] >> 8) & 0xFF).astype(int)
+    same = int((xcc == np.arange(nwg) % 8).sum())
+    per = [len(set(cu[xcc == k].tolist())) for k in range(8)]
+    # shader clock over each workgroup's life: s_memtime cycles / 100 MHz-clock time
+    cyc = (t[:, WORDS - 3] - t[:, WORDS - 4]).astype(float)
+    sec = (t[:, 2] - t[:, 0]).astype(float) / 100e6
+    mhz = cyc / np.maximum(sec, 1e-9) / 1e6
+    print(f"\nShader clock over each workgroup's life (s_memtime cycles / elapsed time, last rep): "
+          f"median {np.median(mhz):.0f} MHz, p10 {np.percentile(mhz, 10):.0f}, "
+          f"p90 {np.percentile(mhz, 90):.0f}.")
+    print(f"\nDies: {same} of {nwg} workgroups ran on die (workgroup id mod 8); workgroups per die "
+          f"{np.bincount(xcc, minlength=8).tolist()}, distinct CUs per die {per}.")
 
 
 def main():

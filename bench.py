@@ -281,9 +281,10 @@ def step_stats(per):
 
 
 def gemm_clock_sample(launch, ms_per_call, seconds=1.0):
-    """The graphics clock while the one-launch GEMM runs back to back for about `seconds`:
-    amdsmi is polled from a second thread while the host waits for the GPU.  Returns
-    {"MHz_median", "samples", "source"} or None where amdsmi is unavailable."""
+    """The graphics clock and the socket power while the one-launch GEMM runs back to back for
+    about `seconds`: amdsmi is polled from a second thread while the host waits for the GPU.
+    Returns {"MHz_median", "socket_W_median", "power_cap_W", "samples", "source", ...} or
+    {"error": ...} where amdsmi is unavailable."""
     import threading
     import torch
     try:
@@ -301,9 +302,21 @@ def gemm_clock_sample(launch, ms_per_call, seconds=1.0):
     except Exception as e:  # noqa: BLE001
         return {"error": f"amdsmi unavailable: {type(e).__name__}: {e}"[:200]}
 
+    cap_w = None
+    try:
+        c = amdsmi.amdsmi_get_power_cap_info(h)
+        if isinstance(c, dict) and isinstance(c.get("power_cap"), (int, float)) and c["power_cap"] > 0:
+            cap_w = float(c["power_cap"]) / 1e6          # reported in microwatts
+    except Exception:  # noqa: BLE001
+        pass
+    power = []
+
     def read():
         try:
             m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            pw = m.get("current_socket_power")
+            if isinstance(pw, (int, float)) and 0 < pw < 10000:
+                power.append(float(pw))
             for key in ("current_gfxclks", "current_gfxclk", "average_gfxclk_frequency"):
                 v = m.get(key)
                 if isinstance(v, (list, tuple)):
@@ -355,9 +368,11 @@ def gemm_clock_sample(launch, ms_per_call, seconds=1.0):
         return {"error": "no clock readings"}
     # drop the first readings (the launches ramp up) and take the median
     use = samples[len(samples) // 5:] or samples
+    pw = power[len(power) // 5:] or power
     return {"MHz_median": float(np.median(use)), "MHz_p10": float(np.percentile(use, 10)),
             "MHz_p90": float(np.percentile(use, 90)), "samples": len(use), "source": sorted(src),
-            "calls": n}
+            "calls": n, "socket_W_median": float(np.median(pw)) if pw else None,
+            "power_cap_W": cap_w}
 
 
 LAYER_STAGES = ("swiglu", "gather", "fc1_gemm", "scatter")
