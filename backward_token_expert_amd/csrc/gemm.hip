@@ -576,8 +576,14 @@ __device__ __forceinline__ void store_acc(float* __restrict__ out, int64_t ldo, 
 // dW: persistent.  The workgroups of a die form gpx groups of gs = nb / gpx; group g has a list of
 // jobs (expert, K range, output) built by dw_schedule, and its workgroups take the units
 // u = j, j + gs, ... of that list (unit = job-major, tile-minor), so they sweep one job's tiles
-// together and its rows come from HBM once per group.  A job whose output is a slot writes a
-// partial sum of a split expert there (dw_fixup adds it); otherwise it writes dW directly.
+// together and its rows come from HBM once per group.  A job's tiles are ordered in column strips
+// of kDwStrip column tiles, row by row within a strip: the gs tiles in flight then cover a block of
+// about gs / kDwStrip row tiles by kDwStrip column tiles, whose operand panels a die's L2 holds,
+// instead of a few whole rows of tiles when the product is wide.  A job whose output is a slot
+// writes a partial sum of a split expert there (dw_fixup adds it); otherwise it writes dW
+// directly.
+constexpr int kDwStrip = 4;
+
 template <class C, int S>
 __device__ __forceinline__ void dw_jobs(const uint16_t* __restrict__ Gc,
                                         const uint16_t* __restrict__ Phic,
@@ -600,7 +606,9 @@ __device__ __forceinline__ void dw_jobs(const uint16_t* __restrict__ Gc,
     // a record outside the buffers (never written so by dw_schedule) is skipped, not followed
     if (e < 0 || e >= E_loc || kb < 0 || ke < kb || ke > K_cap || slot < -1 || slot >= kMaxDwSlots)
       continue;
-    const int m0 = (local / tn) * C::BM, n0 = (local % tn) * C::BN;
+    const int strip = local / (tm * kDwStrip), within = local - strip * tm * kDwStrip;
+    const int sw = tn - strip * kDwStrip < kDwStrip ? tn - strip * kDwStrip : kDwStrip;
+    const int m0 = (within / sw) * C::BM, n0 = (strip * kDwStrip + within % sw) * C::BN;
     const Operands o{Gc, h, m0, h, Phic, d, n0, d, kb, ke};
     zero_acc(acc);
     mainloop_live<C, S>(live_cols<C>(wn, d - n0), o, ring_addr, fo, w, lane, acc);
