@@ -584,37 +584,55 @@ __device__ __forceinline__ void store_acc(float* __restrict__ out, int64_t ldo, 
 // directly.
 constexpr int kDwStrip = 4;
 
-template <class C, int S>
-__device__ __forceinline__ void dw_jobs(const uint16_t* __restrict__ Gc,
-                                        const uint16_t* __restrict__ Phic,
-                                        const int32_t* __restrict__ sched, int nxcd, int E_loc,
-                                        int K_cap, int h, int d, float* __restrict__ dW,
-                                        float* __restrict__ slots, uint32_t ring_addr) {
-  const int tn = (d + C::BN - 1) / C::BN, tm = (h + C::BM - 1) / C::BM, tpe = tm * tn;
+// This workgroup's share of the dW units: group `grp`'s job list, and units j, j + gs, ...
+struct DwPlan {
+  const int32_t* jobs;
+  int tn, tm, tpe, units, j, gs;
+};
+
+template <class C>
+__device__ __forceinline__ DwPlan dw_plan(const int32_t* __restrict__ sched, int nxcd, int E_loc,
+                                          int h, int d) {
+  DwPlan p;
+  p.tn = (d + C::BN - 1) / C::BN;
+  p.tm = (h + C::BM - 1) / C::BM;
+  p.tpe = p.tm * p.tn;
   const int x = blockIdx.x % nxcd, i = blockIdx.x / nxcd, nb = gridDim.x / nxcd;
-  const int gpx = sched[1], gs = nb / gpx, grp = x * gpx + i / gs, j = i % gs;
-  const int units = sched[4 + 3 * kMaxDwSlots + grp] * tpe;
-  const int32_t* jobs = sched + kDwHeader + (int64_t)grp * dw_jobs_per_group(E_loc) * 4;
+  const int gpx = sched[1];
+  p.gs = nb / gpx;
+  const int grp = x * gpx + i / p.gs;
+  p.j = i % p.gs;
+  p.units = sched[4 + 3 * kMaxDwSlots + grp] * p.tpe;
+  p.jobs = sched + kDwHeader + (int64_t)grp * dw_jobs_per_group(E_loc) * 4;
+  return p;
+}
+
+// Unit u (job u / tpe, tile u % tpe) of a group's job list `jobs` (nothing for a skip record).
+template <class C, int S>
+__device__ __forceinline__ void dw_unit(const int32_t* __restrict__ jobs, int tm, int tn, int u,
+                                       const uint16_t* __restrict__ Gc,
+                                       const uint16_t* __restrict__ Phic, int E_loc, int K_cap,
+                                       int h, int d, float* __restrict__ dW,
+                                       float* __restrict__ slots, uint32_t ring_addr,
+                                       f32x16 (&acc)[C::MT][C::NT]) {
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), wm = w / C::WN, wn = w % C::WN;
   const FragOffsets<C> fo = frag_offsets<C>(wm, wn, lane);
-  f32x16 acc[C::MT][C::NT];
-  for (int u = j; u < units; u += gs) {
-    const int32_t* jb = jobs + 4 * (u / tpe);
-    const int e = jb[0], kb = jb[1], ke = jb[2], slot = jb[3], local = u % tpe;
-    if (slot == -2) continue;  // an empty piece of a split expert
-    // a record outside the buffers (never written so by dw_schedule) is skipped, not followed
-    if (e < 0 || e >= E_loc || kb < 0 || ke < kb || ke > K_cap || slot < -1 || slot >= kMaxDwSlots)
-      continue;
-    const int strip = local / (tm * kDwStrip), within = local - strip * tm * kDwStrip;
-    const int sw = tn - strip * kDwStrip < kDwStrip ? tn - strip * kDwStrip : kDwStrip;
-    const int m0 = (within / sw) * C::BM, n0 = (strip * kDwStrip + within % sw) * C::BN;
-    const Operands o{Gc, h, m0, h, Phic, d, n0, d, kb, ke};
-    zero_acc(acc);
-    mainloop_live<C, S>(live_cols<C>(wn, d - n0), o, ring_addr, fo, w, lane, acc);
-    float* out = slot < 0 ? dW + (int64_t)e * h * d : slots + (int64_t)slot * h * d;
-    store_acc<C::MT, C::NT, C::WN>(out, d, m0, h, n0, d, wm, wn, lane, acc);
-  }
+  const int tpe = tm * tn;
+  const int32_t* jb = jobs + 4 * (u / tpe);
+  const int e = jb[0], kb = jb[1], ke = jb[2], slot = jb[3], local = u % tpe;
+  if (slot == -2) return;  // an empty piece of a split expert
+  // a record outside the buffers (never written so by dw_schedule) is skipped, not followed
+  if (e < 0 || e >= E_loc || kb < 0 || ke < kb || ke > K_cap || slot < -1 || slot >= kMaxDwSlots)
+    return;
+  const int strip = local / (tm * kDwStrip), within = local - strip * tm * kDwStrip;
+  const int sw = tn - strip * kDwStrip < kDwStrip ? tn - strip * kDwStrip : kDwStrip;
+  const int m0 = (within / sw) * C::BM, n0 = (strip * kDwStrip + within % sw) * C::BN;
+  const Operands o{Gc, h, m0, h, Phic, d, n0, d, kb, ke};
+  zero_acc(acc);
+  mainloop_live<C, S>(live_cols<C>(wn, d - n0), o, ring_addr, fo, w, lane, acc);
+  float* out = slot < 0 ? dW + (int64_t)e * h * d : slots + (int64_t)slot * h * d;
+  store_acc<C::MT, C::NT, C::WN>(out, d, m0, h, n0, d, wm, wn, lane, acc);
 }
 
 template <class C, int S>
@@ -626,7 +644,11 @@ __global__ __launch_bounds__(C::THREADS) void dw_bf16(const uint16_t* __restrict
                                                      float* __restrict__ slots) {
   using R = Ring<C, S>;
   __shared__ __attribute__((aligned(1024))) uint16_t ring[R::BYTES / 2];
-  dw_jobs<C, S>(Gc, Phic, sched, nxcd, E_loc, K_cap, h, d, dW, slots, lds_addr(ring));
+  const DwPlan pl = dw_plan<C>(sched, nxcd, E_loc, h, d);
+  f32x16 acc[C::MT][C::NT];
+  for (int u = pl.j; u < pl.units; u += pl.gs)
+    dw_unit<C, S>(pl.jobs, pl.tm, pl.tn, u, Gc, Phic, E_loc, K_cap, h, d, dW, slots,
+                  lds_addr(ring), acc);
 }
 
 // dW of each split expert += its partial slots, in piece order.  A fixed grid of kFixupBlocks
@@ -635,18 +657,17 @@ __global__ __launch_bounds__(C::THREADS) void dw_bf16(const uint16_t* __restrict
 // elements over the whole chip.
 constexpr int kFixupBlocks = 1024;
 
-__global__ __launch_bounds__(256) void dw_fixup(const int32_t* __restrict__ sched, int E_loc,
-                                                int h, int d,
-                                                const float* __restrict__ slots,
-                                                float* __restrict__ dW) {
+// Thread t of n adds the split experts' partial slots to dW (h * d a multiple of 4).
+__device__ __forceinline__ void fixup_split_experts(const int32_t* __restrict__ sched, int E_loc,
+                                                    int h, int d, const float* __restrict__ slots,
+                                                    float* __restrict__ dW, int64_t t, int64_t n) {
   const int nsplit = sched[2];
   const int64_t n4 = (int64_t)h * d / 4;
   for (int sp = 0; sp < nsplit && sp < kMaxDwSlots; ++sp) {
     const int e = sched[4 + 3 * sp], first = sched[5 + 3 * sp], extra = sched[6 + 3 * sp];
     if (e < 0 || e >= E_loc || first < 0 || extra < 0 || first + extra > kMaxDwSlots) continue;
     float4* out = (float4*)(dW + (int64_t)e * h * d);
-    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n4;
-         q += (int64_t)kFixupBlocks * 256) {
+    for (int64_t q = t; q < n4; q += n) {
       float4 v = out[q];
       for (int k = 0; k < extra; ++k) {
         const float4 a = ((const float4*)(slots + (int64_t)(first + k) * h * d))[q];
@@ -658,6 +679,14 @@ __global__ __launch_bounds__(256) void dw_fixup(const int32_t* __restrict__ sche
       out[q] = v;
     }
   }
+}
+
+__global__ __launch_bounds__(256) void dw_fixup(const int32_t* __restrict__ sched, int E_loc,
+                                                int h, int d,
+                                                const float* __restrict__ slots,
+                                                float* __restrict__ dW) {
+  fixup_split_experts(sched, E_loc, h, d, slots, dW, (int64_t)blockIdx.x * 256 + threadIdx.x,
+                      (int64_t)kFixupBlocks * 256);
 }
 
 constexpr int kDxBlockRows = 8;
@@ -712,58 +741,101 @@ __global__ __launch_bounds__(C::THREADS) void dx_bf16(const uint16_t* __restrict
     dx_unit<C, S>(Gc, W, cmp_off, tiles, u, K_cap, h, d, dphi, lds_addr(ring), acc);
 }
 
-// dW and dphi in one persistent launch (same tile shape, CW and CX differ only in the row
-// operand's orientation).  Each workgroup first runs its share of the dW jobs exactly as dw_bf16
-// does, then claims dphi units one at a time: from its own die's contiguous range (a counter per
-// die in the workspace, reset by dx_schedule), and once that is exhausted from the other dies' in
-// turn.  The workgroups whose dW share ends early (light groups) thus take more dphi units, and
-// dphi's last partial round is spread over whoever is free.  Each unit is computed whole by the
-// workgroup that claims it, in the same order as in dx_bf16, so results do not depend on which
-// workgroup runs it.  A claim tries every die once, so every workgroup leaves when all ranges are
-// exhausted.
-// kLayer (2: FC2, 1: FC1) only separates the two layers' launches in profiles.
-template <class CW, class CX, int S, int kLayer>
-__global__ __launch_bounds__(CW::THREADS) void gemm_fused(
-    const uint16_t* __restrict__ Gc, const uint16_t* __restrict__ Phic,
-    const uint16_t* __restrict__ W, const int32_t* __restrict__ cmp_off,
-    const int32_t* __restrict__ sched, const int32_t* __restrict__ tiles, int32_t* __restrict__ queue,
-    int nxcd, int E_loc, int K_cap, int h, int d, float* __restrict__ dW,
-    float* __restrict__ slots, float* __restrict__ dphi) {
-  static_assert(CW::BM == CX::BM && CW::BN == CX::BN && CW::THREADS == CX::THREADS, "one shape");
-  using R = Ring<CW, S>;
-  static_assert(Ring<CX, S>::BYTES == R::BYTES, "one ring");
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[R::BYTES / 2];
-  // the claimed unit is broadcast through the ring's first word: every mainloop ends with its
-  // loads drained and a barrier, and the next one starts writing the ring only after the second
-  // barrier below
-  volatile int* claimed = (volatile int*)ring;
-  const uint32_t ring_addr = lds_addr(ring);
+// Arguments of the one-launch GEMMs.
+struct FusedArgs {
+  const uint16_t* Gc;
+  const uint16_t* Phic;
+  const uint16_t* W;
+  const int32_t* cmp_off;
+  const int32_t* sched;
+  const int32_t* tiles;
+  int32_t* queue;
+  int nxcd, E_loc, K_cap, h, d;
+  float* dW;
+  float* slots;
+  float* dphi;
+};
+
+// The work loop of gemm_fused.  MIX (store-bound products: dW jobs that average fewer K steps than
+// a job's fixed cost, such as a whole layer with many empty experts; dw_schedule sets the flag):
+// every workgroup starts with a dphi unit, then alternates dW and dphi units, and takes its dW
+// units from one counter over all groups' lists instead of its group's fixed share.  The dphi
+// units, whose reads would wait behind the flood of dW tile stores, then start first and the
+// stores fill in around them on whichever workgroups are free.  Otherwise a workgroup runs its
+// group's dW units first, in step with the group (for L2 reuse), then claims dphi units.
+template <class CW, class CX, int S, bool MIX>
+__device__ __forceinline__ void fused_loop(const FusedArgs& a, volatile int* claimed,
+                                           uint32_t ring_addr, f32x16 (&acc)[CX::MT][CX::NT],
+                                           unsigned long long* stamp) {
 #ifdef LRM_TIMELINE
-  unsigned long long* stamp = g_timeline + (size_t)(blockIdx.x % kTimelineWGs) * kTimelineWords;
-  if (threadIdx.x == 0) {
-    stamp[0] = __builtin_amdgcn_s_memrealtime();
-    stamp[kTimelineWords - 4] = __builtin_amdgcn_s_memtime();
-    stamp[kTimelineWords - 2] = __builtin_amdgcn_s_getreg((15 << 11) | 20);  // XCC_ID[15:0]
-    stamp[kTimelineWords - 1] = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID[31:0]
-  }
-#endif
-  dw_jobs<CW, S>(Gc, Phic, sched, nxcd, E_loc, K_cap, h, d, dW, slots, ring_addr);
-#ifdef LRM_TIMELINE
-  if (threadIdx.x == 0) stamp[1] = __builtin_amdgcn_s_memrealtime();
   int claims = 0;
+#else
+  (void)stamp;
 #endif
-  const int tn = (d + CX::BN - 1) / CX::BN;
-  const int total = tiles[0] * tn, per = (total + nxcd - 1) / nxcd;
-  const int x = blockIdx.x % nxcd;
-  f32x16 acc[CX::MT][CX::NT];
+  const DwPlan pl = dw_plan<CW>(a.sched, a.nxcd, a.E_loc, a.h, a.d);
+  const int tn = (a.d + CX::BN - 1) / CX::BN;
+  const int total = a.tiles[0] * tn, per = (total + a.nxcd - 1) / a.nxcd;
+  const int x = blockIdx.x % a.nxcd;
+  if constexpr (!MIX) {
+    // the group's dW units, then dphi claims until every range is exhausted
+    for (int u = pl.j; u < pl.units; u += pl.gs)
+      dw_unit<CW, S>(pl.jobs, pl.tm, pl.tn, u, a.Gc, a.Phic, a.E_loc, a.K_cap, a.h, a.d, a.dW,
+                     a.slots, ring_addr, acc);
+#ifdef LRM_TIMELINE
+    if (threadIdx.x == 0) stamp[1] = __builtin_amdgcn_s_memrealtime();
+#endif
+  }
+  int u_dw = pl.j;
+  bool dw_left = MIX, dx_left = true, dx_next = MIX;
   for (;;) {
+    if (dw_left && !(dx_next && dx_left)) {
+      const int32_t* jobs = pl.jobs;
+      int u = u_dw;
+      if constexpr (MIX) {
+        // claim v of the counter: unit v - (units of the groups before g) of group g
+        if (threadIdx.x == 0) {
+          int v = atomicAdd(&a.queue[kMaxXcd], 1), g = 0;
+          const int G = a.sched[0];
+          for (; g < G && g < kMaxXcd * kMaxGroupsPerXcd; ++g) {
+            const int n = a.sched[4 + 3 * kMaxDwSlots + g] * pl.tpe;
+            if (v < n) break;
+            v -= n;
+          }
+          claimed[0] = g < G && g < kMaxXcd * kMaxGroupsPerXcd ? g : -1;
+          claimed[1] = v;
+        }
+        __syncthreads();
+        const int g = __builtin_amdgcn_readfirstlane(claimed[0]);
+        u = __builtin_amdgcn_readfirstlane(claimed[1]);
+        __syncthreads();
+        if (g < 0) {
+          dw_left = false;
+#ifdef LRM_TIMELINE
+          if (threadIdx.x == 0) stamp[1] = __builtin_amdgcn_s_memrealtime();
+#endif
+          continue;
+        }
+        jobs = a.sched + kDwHeader + (int64_t)g * dw_jobs_per_group(a.E_loc) * 4;
+      } else {
+        u_dw += pl.gs;
+        dw_left = u_dw < pl.units;
+      }
+      dw_unit<CW, S>(jobs, pl.tm, pl.tn, u, a.Gc, a.Phic, a.E_loc, a.K_cap, a.h, a.d, a.dW,
+                     a.slots, ring_addr, acc);
+      dx_next = MIX;
+#ifdef LRM_TIMELINE
+      if (threadIdx.x == 0 && !dw_left) stamp[1] = __builtin_amdgcn_s_memrealtime();
+#endif
+      continue;
+    }
+    if (!dx_left) break;  // and no dW unit is left either
     if (threadIdx.x == 0) {
       int u = -1;
-      for (int k = 0; k < nxcd && u < 0; ++k) {
-        const int y = x + k < nxcd ? x + k : x + k - nxcd;
+      for (int k = 0; k < a.nxcd && u < 0; ++k) {
+        const int y = x + k < a.nxcd ? x + k : x + k - a.nxcd;
         const int lo = y * per, cnt = (lo + per < total ? lo + per : total) - lo;
         if (cnt <= 0) continue;
-        const int v = atomicAdd(&queue[y], 1);
+        const int v = atomicAdd(&a.queue[y], 1);
         if (v < cnt) u = lo + v;
       }
       *claimed = u;
@@ -771,7 +843,10 @@ __global__ __launch_bounds__(CW::THREADS) void gemm_fused(
     __syncthreads();
     const int u = __builtin_amdgcn_readfirstlane(*claimed);
     __syncthreads();
-    if (u < 0) break;
+    if (u < 0) {
+      dx_left = false;
+      continue;
+    }
 #ifdef LRM_TIMELINE
     if (threadIdx.x == 0 && claims < kTimelineUnits) {
       stamp[4 + 2 * claims] = __builtin_amdgcn_s_memrealtime();
@@ -779,12 +854,76 @@ __global__ __launch_bounds__(CW::THREADS) void gemm_fused(
     }
     ++claims;
 #endif
-    dx_unit<CX, S>(Gc, W, cmp_off, tiles, u, K_cap, h, d, dphi, ring_addr, acc);
+    dx_unit<CX, S>(a.Gc, a.W, a.cmp_off, a.tiles, u, a.K_cap, a.h, a.d, a.dphi, ring_addr, acc);
+    dx_next = false;
   }
+#ifdef LRM_TIMELINE
+  if (threadIdx.x == 0) stamp[3] = (unsigned long long)claims;
+#endif
+}
+
+// dW and dphi in one persistent launch (same tile shape, CW and CX differ only in the row
+// operand's orientation), kPart 0.  Each workgroup runs its share of the dW units exactly as
+// dw_bf16 does, then claims dphi units one at a time: from its own die's contiguous range (a
+// counter per die in the workspace, reset by dx_schedule), and once that is exhausted from the
+// other dies' in turn.  A second launch of the same shape (kPart 1) follows it: for store-bound
+// products (fused_loop's MIX, flagged by dw_schedule) the first launch returns at once and the
+// second runs the product; otherwise the second adds the split experts' partial slots (dw_fixup's
+// work) and returns.  Two specialised kernels instead of one with both loops keep the register
+// allocation of the common path as it is.  With solo set (no second launch) the first launch
+// runs every product the common way.  The workgroups whose dW share ends early (light groups) thus take more dphi units, and
+// dphi's last partial round is spread over whoever is free.  Each unit is computed whole by the
+// workgroup that claims it, in the same order as in dx_bf16, so results do not depend on which
+// workgroup runs it.  A claim tries every die once, so every workgroup leaves when all ranges are
+// exhausted.
+// kLayer (2: FC2, 1: FC1) only separates the two layers' launches in profiles.
+template <class CW, class CX, int S, int kLayer, int kPart>
+__global__ __launch_bounds__(CW::THREADS) void gemm_fused(
+    const uint16_t* __restrict__ Gc, const uint16_t* __restrict__ Phic,
+    const uint16_t* __restrict__ W, const int32_t* __restrict__ cmp_off,
+    const int32_t* __restrict__ sched, const int32_t* __restrict__ tiles, int32_t* __restrict__ queue,
+    int nxcd, int E_loc, int K_cap, int h, int d, float* __restrict__ dW,
+    float* __restrict__ slots, float* __restrict__ dphi, int solo) {
+  const FusedArgs a{Gc, Phic, W, cmp_off, sched, tiles, queue, nxcd, E_loc, K_cap, h, d, dW, slots,
+                    dphi};
+  static_assert(CW::BM == CX::BM && CW::BN == CX::BN && CW::THREADS == CX::THREADS, "one shape");
+  static_assert(CW::MT == CX::MT && CW::NT == CX::NT, "one accumulator array for both");
+  using R = Ring<CW, S>;
+  static_assert(Ring<CX, S>::BYTES == R::BYTES, "one ring");
+  const bool mix = a.sched[3] != 0 && !solo;
+  if constexpr (kPart == 0) {
+    if (mix) return;  // the second launch runs this product
+  } else {
+    if (!mix) {
+      if (a.slots != nullptr)
+        fixup_split_experts(a.sched, a.E_loc, a.h, a.d, a.slots, a.dW,
+                            (int64_t)blockIdx.x * CW::THREADS + threadIdx.x,
+                            (int64_t)gridDim.x * CW::THREADS);
+      return;
+    }
+  }
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[R::BYTES / 2];
+  // claimed units are broadcast through the ring's first two words: every mainloop ends with its
+  // loads drained and a barrier, and the next one starts writing the ring only after the second
+  // barrier of a claim
+  volatile int* claimed = (volatile int*)ring;
+  const uint32_t ring_addr = lds_addr(ring);
+  unsigned long long* stamp = nullptr;
+#ifdef LRM_TIMELINE
+  stamp = g_timeline + (size_t)(blockIdx.x % kTimelineWGs) * kTimelineWords;
+  if (threadIdx.x == 0) {
+    stamp[0] = __builtin_amdgcn_s_memrealtime();
+    stamp[1] = stamp[0];  // replaced when the last dW unit of this workgroup ends
+    stamp[kTimelineWords - 4] = __builtin_amdgcn_s_memtime();
+    stamp[kTimelineWords - 2] = __builtin_amdgcn_s_getreg((15 << 11) | 20);  // XCC_ID[15:0]
+    stamp[kTimelineWords - 1] = __builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID[31:0]
+  }
+#endif
+  f32x16 acc[CX::MT][CX::NT];
+  fused_loop<CW, CX, S, kPart == 1>(a, claimed, ring_addr, acc, stamp);
 #ifdef LRM_TIMELINE
   if (threadIdx.x == 0) {
     stamp[2] = __builtin_amdgcn_s_memrealtime();
-    stamp[3] = (unsigned long long)claims;
     stamp[kTimelineWords - 3] = __builtin_amdgcn_s_memtime();
   }
 #endif
@@ -853,7 +992,11 @@ __device__ __forceinline__ void dw_schedule_body(const int32_t* __restrict__ cmp
   __syncthreads();
   int worst = 0;
   for (int g = 0; g < groups; ++g) worst = load[g] > worst ? load[g] : worst;
-  const bool fill = allow_split && (int64_t)worst * 4 > (int64_t)T * 5 && groups - 1 <= kMaxDwSlots;
+  // store-bound (the second fused launch runs it with dynamic dW claims, which need no splits):
+  // the jobs' K steps (total - kDwJobCost * E_loc) sum to less than their fixed costs
+  const bool mix = total - kDwJobCost * E_loc < kDwJobCost * E_loc;
+  const bool fill = allow_split && !mix && (int64_t)worst * 4 > (int64_t)T * 5 &&
+                    groups - 1 <= kMaxDwSlots;
   const int64_t jpg = dw_jobs_per_group(E_loc);
   auto put = [&](int g, int idx, int kb, int kend, int slot) {
     int32_t* jb = sched + kDwHeader + (int64_t)g * jpg * 4 + 4 * idx;
@@ -918,6 +1061,7 @@ __device__ __forceinline__ void dw_schedule_body(const int32_t* __restrict__ cmp
   if (tid == 0) {
     sched[0] = groups;
     sched[1] = gpx;
+    sched[3] = mix ? 1 : 0;
   }
   if (tid < groups) sched[4 + 3 * kMaxDwSlots + tid] = count[tid];
 }
@@ -1081,7 +1225,7 @@ __device__ __forceinline__ void dx_schedule_body(const int32_t* __restrict__ cmp
                                                  int32_t* __restrict__ queue) {
   __shared__ int sh[32];
   const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
-  if (queue && tid < kMaxXcd) queue[tid] = 0;  // unit counters of the fused launch
+  if (queue && tid <= kMaxXcd) queue[tid] = 0;  // unit counters of the fused launch (dphi per die, dW)
   int base_tiles = 0;
   for (int e0 = 0; e0 < E_loc; e0 += 1024) {
     const int e = e0 + tid;
@@ -1222,12 +1366,17 @@ void launch_fused_t(const lrm_problem& p, const void* Gc, const void* Phic, cons
   hipLaunchKernelGGL(gemm_schedules, dim3(2), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap,
                      g.nxcd * gpx, gpx, sched, CX::BM, max_tiles, tiles, queue,
                      slots != nullptr ? 1 : 0);
-  hipLaunchKernelGGL((gemm_fused<CW, CX, stages_for<CW>(), kLayer>), dim3(g.blocks), dim3(CW::THREADS), 0,
-                     s, (const uint16_t*)Gc, (const uint16_t*)Phic, (const uint16_t*)W, cmp_off,
-                     sched, tiles, queue, g.nxcd, p.E_loc, p.K_cap, p.h, p.d, dW, slots, dphi);
-  if (slots != nullptr)
-    hipLaunchKernelGGL(dw_fixup, dim3(kFixupBlocks), dim3(256), 0, s, sched,
-                       p.E_loc, p.h, p.d, slots, dW);
+  // without partial slots (the allocation-free entry) one launch runs every product
+  const int solo = slots == nullptr ? 1 : 0;
+  hipLaunchKernelGGL((gemm_fused<CW, CX, stages_for<CW>(), kLayer, 0>), dim3(g.blocks),
+                     dim3(CW::THREADS), 0, s, (const uint16_t*)Gc, (const uint16_t*)Phic,
+                     (const uint16_t*)W, cmp_off, sched, tiles, queue, g.nxcd, p.E_loc, p.K_cap,
+                     p.h, p.d, dW, slots, dphi, solo);
+  if (!solo)
+    hipLaunchKernelGGL((gemm_fused<CW, CX, stages_for<CW>(), kLayer, 1>), dim3(g.blocks),
+                       dim3(CW::THREADS), 0, s, (const uint16_t*)Gc, (const uint16_t*)Phic,
+                       (const uint16_t*)W, cmp_off, sched, tiles, queue, g.nxcd, p.E_loc,
+                       p.K_cap, p.h, p.d, dW, slots, dphi, 0);
 }
 
 template <class C>

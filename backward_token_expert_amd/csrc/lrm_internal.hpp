@@ -27,6 +27,7 @@ __host__ __device__ inline int64_t dw_jobs_per_group(int E_loc) { return (int64_
 
 // Word of the workspace header where the fused GEMM launch keeps its kMaxXcd unit counters.
 constexpr int kQueueWord = 8;
+static_assert((kQueueWord + kMaxXcd + 1) * 4 <= 256, "the unit counters fit the 256-byte header");
 
 // Layout of the caller-provided workspace (byte offsets, all 256-byte aligned).
 struct WsLayout {
@@ -81,7 +82,7 @@ inline WsLayout ws_layout(const lrm_problem& p) {
 constexpr size_t kNoallocScratchBytes = size_t(1) << 20;
 constexpr int kMaxDevices = 64;
 struct NoallocLayout {
-  size_t queue;   // int32 [kMaxXcd] unit counters of the one-launch kernel
+  size_t queue;   // int32 [kMaxXcd + 1] unit counters of the one-launch kernel (dphi per die, dW)
   size_t sched;   // int32 dW schedule (header, per-group job lists)
   size_t tiles;   // int32 [1 + 2*max_tiles] dphi tile table
   size_t total;

@@ -26,12 +26,14 @@ import re
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 
-# C-ABI entry point -> (pattern of its GEMM kernels' short names, translation unit); the one-launch
-# kernel's last template argument tells FC2's launches (2) from FC1's (1)
+# C-ABI entry point -> (pattern of its GEMM kernels' short names, translation unit).  The one-launch
+# GEMMs are two launches of gemm_fused (last template argument 0 and 1: one of them runs the
+# product, the other returns at once or adds split experts' partial sums), whose counters are
+# summed; the argument before it tells FC2's launches (2) from FC1's (1).
 GEMM_KERNELS = {"lrm_grouped_dw": (r"(dw_bf16|dw_f32)\b", "gemm.hip"),
                 "lrm_grouped_dx": (r"(dx_bf16|dx_f32)\b", "gemm.hip"),
-                "lrm_grouped_dw_dx": (r"gemm_fused<.*, 2>$", "gemm.hip"),
-                "lrm_grouped_fc1_dw_dx": (r"gemm_fused<.*, 1>$", "gemm.hip")}
+                "lrm_grouped_dw_dx": (r"gemm_fused<.*, 2, [01]>$", "gemm.hip"),
+                "lrm_grouped_fc1_dw_dx": (r"gemm_fused<.*, 1, [01]>$", "gemm.hip")}
 _SHARED = ("lrm_device.hpp", "lrm_internal.hpp")
 
 
@@ -78,7 +80,7 @@ def source_digest(call: str) -> str:
 
 def short_name(n: str) -> str:
     n = n.replace("lrm::(anonymous namespace)::", "").replace("void ", "")
-    return re.sub(r"\(.*", "", n)[:60]
+    return re.sub(r"\(.*", "", n)[:90]
 
 
 def stats_table(path: str) -> str:
@@ -158,10 +160,18 @@ def counters_report(root: str, copy_bytes: int, workload: str):
                      f"{f(conf, 0)} | {f(fe, 0)} | {f(wr, 0)} | {f(mb)} |")
         for call, (names, _) in GEMM_KERNELS.items():
             if re.match(names, k) and mb is not None:
-                rec["kernels"][call] = {"kernel": k, "traffic_bytes": mb * 1e6,
-                                        "fetch_bytes": fe * 1024 * fs, "write_bytes": wr * 1024 * ws,
-                                        "clock_mhz": clk, "mfma_busy_pct": mfp,
-                                        "source_sha256": source_digest(call)}
+                r = rec["kernels"].setdefault(call, {"kernels": [], "traffic_bytes": 0.0,
+                                                     "fetch_bytes": 0.0, "write_bytes": 0.0,
+                                                     "source_sha256": source_digest(call)})
+                r["kernels"].append(k)
+                r["traffic_bytes"] += mb * 1e6
+                r["fetch_bytes"] += fe * 1024 * fs
+                r["write_bytes"] += wr * 1024 * ws
+                # clock and MFMA busy of the launch that ran the product (the busier one)
+                if gui is not None and gui > r.get("_gui", -1.0):
+                    r.update({"_gui": gui, "kernel": k, "clock_mhz": clk, "mfma_busy_pct": mfp})
+    for r in rec["kernels"].values():
+        r.pop("_gui", None)
     return "\n".join(lines), rec
 
 

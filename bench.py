@@ -624,17 +624,21 @@ def leg(w, pol, steps, warmup, crit, fused, graph, flush, label):
 
 def copy_ceiling(flush, mib=1024, reps=10):
     """A plain device-to-device copy of `mib` MiB timed like the step (events around each copy,
-    the flush between copies): bytes read + written per second."""
+    the flush between copies): bytes read + written per second; and a fill of the same buffer,
+    the write-only rate."""
     import torch
     n = mib << 20
     src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)
     per, _ = timed_replays(lambda: dst.copy_(src), reps, flush)
+    fill, _ = timed_replays(lambda: dst.fill_(2.0), reps, flush)
     del src, dst
-    med = float(np.median(per))
+    med, fmed = float(np.median(per)), float(np.median(fill))
     return {"GBps": 2 * n / (med * 1e-3) / 1e9, "bytes_moved": 2 * n, "median_ms": med,
-            "kernel": "torch copy_ (device to device)"}
+            "kernel": "torch copy_ (device to device)",
+            "fill_GBps": n / (fmed * 1e-3) / 1e9, "fill_median_ms": fmed,
+            "fill_kernel": "torch fill_ (writes only)"}
 
 
 def main():
