@@ -349,12 +349,13 @@ lrm_status lrm_grouped_dx(const lrm_problem* problem, const void* Gc, const void
 
 /*
  * Both grouped FC2 gradients in one call: dW exactly as lrm_grouped_dw and dphi exactly as
- * lrm_grouped_dx (same arguments, same results bit for bit), computed by one persistent launch
+ * lrm_grouped_dx (same arguments, same results bit for bit), computed by one persistent kernel
  * for bf16 inputs: workgroups whose share of the weight-gradient tiles ends early take
  * input-gradient tiles, so neither product leaves the device partly idle while the other still
- * has work (LRMoE Sec. 3.4: all expert-backward GEMMs run over the retained rows only).  fp32
- * inputs run the two products one after the other.  Requires Gc, Phic, W, dW, dphi 16-byte
- * aligned.
+ * has work (LRMoE Sec. 3.4: all expert-backward GEMMs run over the retained rows only).  When the
+ * weight-gradient stores dominate (few retained rows per expert), the input-gradient tiles start
+ * first and both kinds are taken from shared counters.  fp32 inputs run the two products one
+ * after the other.  Requires Gc, Phic, W, dW, dphi 16-byte aligned.
  */
 lrm_status lrm_grouped_dw_dx(const lrm_problem* problem, const void* Gc, const void* Phic,
                              const void* W, const int32_t* cmp_off, float* dW, float* dphi,
@@ -436,7 +437,7 @@ lrm_status lrm_grouped_fc1_dx(const lrm_problem* problem, const void* dH, const 
                               hipStream_t stream);
 
 /* Both FC1 gradients in one call: results bit for bit those of the two calls above (one
- * persistent launch for bf16, as lrm_grouped_dw_dx). */
+ * persistent kernel for bf16, as lrm_grouped_dw_dx). */
 lrm_status lrm_grouped_fc1_dw_dx(const lrm_problem* problem, const void* dH, const void* Xc,
                                  const void* W1, const int32_t* cmp_off, float* dW1, float* dX,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
