@@ -619,10 +619,14 @@ GEMM_SHAPES = [
     ([70, 0, 130], 4096, 1408),
     ([40, 0, 0, 200], 256, 256),
     ([16500, 16524], 256, 768),
-    # many experts on 256 x 384 tiles: the dW schedule's contiguous fill with split experts,
-    # empty pieces (skip records) and empty experts
+    # many small experts on 256 x 384 tiles: store-bound (the jobs' K steps sum to less than their
+    # fixed costs), so the one-launch form starts with dphi units and claims dW units from one
+    # counter; empty experts write zeros
     ([2000, 1500, 0, 3, 40, 700, 1] + [5] * 40 + [0] * 10, 2048, 768),
     ([2500, 30, 0, 1200, 64, 0] + [33] * 20, 2048, 768),
+    # one expert far above the fair share, not store-bound: the dW schedule's contiguous fill
+    # splits it along K into partial slots that the one-launch form's second launch adds up
+    ([12000] + [40] * 15, 2048, 768),
 ]
 
 
