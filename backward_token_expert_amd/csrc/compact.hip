@@ -100,10 +100,13 @@ __global__ __launch_bounds__(kBlock) void compact_rows_phi(
   if (bad) set_error(err, bad);
 }
 
-// Pass 2: one wavefront per token.  GC = 16-byte chunks of g_t each lane keeps in registers
-// (rows up to GC * 64 chunks; loaded non-temporally, as nothing reads them again); GC = 0
-// re-reads g_t for every kept pair (wider rows).
-template <bool kBF16, int GC>
+// Pass 2: one wavefront per token.  The row g_t is taken in groups of kGroup * 64 16-byte chunks:
+// each group is loaded once (non-temporally, as nothing reads it again), kept in registers and
+// written, scaled, to every kept row of the token.  Small groups keep the kernel at 8 waves per
+// SIMD (holding a whole 8 KB row per lane left it at 3), which keeps more loads in flight.
+constexpr int kGroup = 4;
+
+template <bool kBF16>
 __global__ __launch_bounds__(kBlock) void compact_tokens_g(
     const int32_t* __restrict__ inv, const int32_t* __restrict__ sel_pair,
     const int32_t* __restrict__ cmp_off, int E_loc, int K_cap, int T, int k,
@@ -115,8 +118,6 @@ __global__ __launch_bounds__(kBlock) void compact_tokens_g(
   const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
   const int64_t w0 = (int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
   for (int64_t t = w0; t < T; t += nw) {
-    uint4 x[GC > 0 ? GC : 1];
-    bool loaded = false;
     for (int j0 = 0; j0 < k; j0 += kWave) {
       const int j = j0 + lane;
       const int64_t p = t * k + j;
@@ -129,31 +130,26 @@ __global__ __launch_bounds__(kBlock) void compact_tokens_g(
           a = topk_w[p];
         }
       }
-      uint64_t m = ballot(i >= 0);
+      const uint64_t m = ballot(i >= 0);
       if (m == 0) continue;
       const uint4* gs = g + t * gch;
-      if (GC > 0 && !loaded) {
+      for (int c0 = 0; c0 < gch; c0 += kGroup * kWave) {
+        uint4 x[kGroup];
 #pragma unroll
-        for (int c = 0; c < (GC > 0 ? GC : 1); ++c) {
-          const int ch = lane + c * kWave;
+        for (int c = 0; c < kGroup; ++c) {
+          const int ch = c0 + lane + c * kWave;
           x[c] = ch < gch ? load_nt(gs + ch) : make_uint4(0, 0, 0, 0);
         }
-        loaded = true;
-      }
-      while (m) {
-        const int jj = __builtin_ctzll(m);
-        m &= m - 1;
-        const int ii = __shfl(i, jj, kWave);
-        const float aa = __shfl(a, jj, kWave);
-        uint4* gd = Gc + (int64_t)ii * gch;
-        if (GC > 0) {
+        for (uint64_t mm = m; mm; mm &= mm - 1) {
+          const int jj = __builtin_ctzll(mm);
+          const int ii = __shfl(i, jj, kWave);
+          const float aa = __shfl(a, jj, kWave);
+          uint4* gd = Gc + (int64_t)ii * gch;
 #pragma unroll
-          for (int c = 0; c < (GC > 0 ? GC : 1); ++c) {
-            const int ch = lane + c * kWave;
+          for (int c = 0; c < kGroup; ++c) {
+            const int ch = c0 + lane + c * kWave;
             if (ch < gch) gd[ch] = scale_chunk<kBF16>(x[c], aa);
           }
-        } else {
-          for (int ch = lane; ch < gch; ch += kWave) gd[ch] = scale_chunk<kBF16>(gs[ch], aa);
         }
       }
     }
@@ -175,15 +171,8 @@ void launch_tokens(const lrm_problem& p, const int32_t* inv, const int32_t* sel_
                    int32_t* err, hipStream_t s) {
   const int64_t tb = ((int64_t)p.T + kWavesPerBlock - 1) / kWavesPerBlock;
   const unsigned nblk = (unsigned)(tb < 16384 ? tb : 16384);
-  if (gch <= 4 * kWave)
-    hipLaunchKernelGGL((compact_tokens_g<kBF16, 4>), dim3(nblk), dim3(kBlock), 0, s, inv, sel_pair,
-                       cmp_off, p.E_loc, p.K_cap, p.T, p.k, topk_w, g, gch, Gc, err);
-  else if (gch <= 8 * kWave)
-    hipLaunchKernelGGL((compact_tokens_g<kBF16, 8>), dim3(nblk), dim3(kBlock), 0, s, inv, sel_pair,
-                       cmp_off, p.E_loc, p.K_cap, p.T, p.k, topk_w, g, gch, Gc, err);
-  else
-    hipLaunchKernelGGL((compact_tokens_g<kBF16, 0>), dim3(nblk), dim3(kBlock), 0, s, inv, sel_pair,
-                       cmp_off, p.E_loc, p.K_cap, p.T, p.k, topk_w, g, gch, Gc, err);
+  hipLaunchKernelGGL((compact_tokens_g<kBF16>), dim3(nblk), dim3(kBlock), 0, s, inv, sel_pair,
+                     cmp_off, p.E_loc, p.K_cap, p.T, p.k, topk_w, g, gch, Gc, err);
 }
 
 }  // namespace
