@@ -59,9 +59,11 @@ def _check_pair(sp, P, b, inp):
     return same
 
 
-# (workload, T of the first call, T of the second call, full retention)
+# (workload, T of the first call, T of the second call, full retention).  The whole layer (4) is
+# store-bound: the workspace call runs it dphi-first with dW units claimed from one counter, the
+# allocation-free call in the common order, so the two orders are checked against each other.
 CASES = [(1, 4096, 1024, False), (0, 4096, 1024, False), (3, 8192, 2048, True),
-         (2, 1024, 512, False)]
+         (2, 1024, 512, False), (4, 4096, 1024, False)]
 
 
 @pytest.mark.parametrize("cfg,T1,T2,full", CASES, ids=[f"cfg{c[0]}" for c in CASES])
