@@ -756,13 +756,17 @@ struct FusedArgs {
   float* dphi;
 };
 
-// The work loop of gemm_fused.  MIX (store-bound products: dW jobs that average fewer K steps than
-// a job's fixed cost, such as a whole layer with many empty experts; dw_schedule sets the flag):
-// every workgroup starts with a dphi unit, then alternates dW and dphi units, and takes its dW
-// units from one counter over all groups' lists instead of its group's fixed share.  The dphi
-// units, whose reads would wait behind the flood of dW tile stores, then start first and the
-// stores fill in around them on whichever workgroups are free.  Otherwise a workgroup runs its
-// group's dW units first, in step with the group (for L2 reuse), then claims dphi units.
+// The work loop of gemm_fused.  MIX (dw_schedule sets the flag): every workgroup starts with a
+// dphi unit, then alternates dW and dphi units, and takes its dW units from one counter over all
+// groups' lists instead of its group's fixed share.  Flag 1, store-bound products (dW jobs that
+// average fewer K steps than a job's fixed cost, such as a whole layer with many empty experts):
+// the dphi units, whose reads would wait behind the flood of dW tile stores, start first and the
+// stores fill in around them on whichever workgroups are free; the counter walks the groups'
+// lists one after the other.  Flag 2, one round of dphi units that would otherwise run after the
+// dW shares and set the end of the launch (a few experts holding most rows): the counter walks
+// the experts largest first, so the free workgroups start the longest dW jobs at once.
+// Otherwise a workgroup runs its group's dW units first, in step with the group (for L2 reuse),
+// then claims dphi units.
 template <class CW, class CX, int S, bool MIX>
 __device__ __forceinline__ void fused_loop(const FusedArgs& a, volatile int* claimed,
                                            uint32_t ring_addr, f32x16 (&acc)[CX::MT][CX::NT],
@@ -792,16 +796,26 @@ __device__ __forceinline__ void fused_loop(const FusedArgs& a, volatile int* cla
       const int32_t* jobs = pl.jobs;
       int u = u_dw;
       if constexpr (MIX) {
-        // claim v of the counter: unit v - (units of the groups before g) of group g
         if (threadIdx.x == 0) {
-          int v = atomicAdd(&a.queue[kMaxXcd], 1), g = 0;
           const int G = a.sched[0];
-          for (; g < G && g < kMaxXcd * kMaxGroupsPerXcd; ++g) {
-            const int n = a.sched[4 + 3 * kMaxDwSlots + g] * pl.tpe;
-            if (v < n) break;
-            v -= n;
+          int v = atomicAdd(&a.queue[kMaxXcd], 1), g = 0;
+          if (a.sched[3] == 2) {
+            // claim v: tile v % tpe of the expert of rank v / tpe (largest first), found where
+            // the snake deal put it: group g, job j of that group's list
+            const int r = v / pl.tpe, n2 = 2 * G, q = r % n2;
+            const int j = 2 * (r / n2) + (q >= G ? 1 : 0);
+            g = r < a.E_loc ? (q < G ? q : n2 - 1 - q) : -1;
+            v = j * pl.tpe + (v - r * pl.tpe);
+          } else {
+            // claim v: unit v - (units of the groups before g) of group g
+            for (; g < G && g < kMaxXcd * kMaxGroupsPerXcd; ++g) {
+              const int n = a.sched[4 + 3 * kMaxDwSlots + g] * pl.tpe;
+              if (v < n) break;
+              v -= n;
+            }
+            if (g >= G || g >= kMaxXcd * kMaxGroupsPerXcd) g = -1;
           }
-          claimed[0] = g < G && g < kMaxXcd * kMaxGroupsPerXcd ? g : -1;
+          claimed[0] = g;
           claimed[1] = v;
         }
         __syncthreads();
@@ -866,8 +880,9 @@ __device__ __forceinline__ void fused_loop(const FusedArgs& a, volatile int* cla
 // operand's orientation), kPart 0.  Each workgroup runs its share of the dW units exactly as
 // dw_bf16 does, then claims dphi units one at a time: from its own die's contiguous range (a
 // counter per die in the workspace, reset by dx_schedule), and once that is exhausted from the
-// other dies' in turn.  A second launch of the same shape (kPart 1) follows it: for store-bound
-// products (fused_loop's MIX, flagged by dw_schedule) the first launch returns at once and the
+// other dies' in turn.  A second launch of the same shape (kPart 1) follows it: for the products
+// dw_schedule flags (fused_loop's MIX: store-bound, or one round of dphi units) the first launch
+// returns at once and the
 // second runs the product; otherwise the second adds the split experts' partial slots (dw_fixup's
 // work) and returns.  Two specialised kernels instead of one with both loops keep the register
 // allocation of the common path as it is.  With solo set (no second launch) the first launch
@@ -942,13 +957,54 @@ __global__ __launch_bounds__(CW::THREADS) void gemm_fused(
 // Every step is a closed form or a workgroup scan, so the schedule costs a few barriers.
 constexpr int kDwJobCost = 8;
 
+// What the dW schedule needs to know of the one-launch form's dphi units (wgs = 0: no such form).
+struct DxShape {
+  int wgs;    // workgroups of the persistent grid
+  int bm;     // rows per dphi unit
+  int tn;     // column tiles per row tile
+  int steps;  // K steps of a dphi unit
+  int tpe;    // dW tiles per job
+};
+
+// The two orders of the one-launch form when its U dphi units fit in one round of the grid
+// (U <= wgs, so each workgroup runs at most one), estimated in K steps (a unit costs its steps
+// plus kDwJobCost; a dW job's cost c covers each of its tpe tiles):
+//  * dW first: a workgroup's part of its group's load (share: the fill's T or the snake deal's
+//    heaviest group), then one dphi unit;
+//  * dphi first: the whole work spread over the grid, but no less than one dphi unit or the
+//    costliest job, nor -- when more dW tiles than the free workgroups cost more than a dphi unit
+//    -- than a dphi unit followed by the costliest job.
+// Thread r holds the rank-r expert's `rows` and cost `c`, cmax is the largest cost; every thread
+// of the workgroup calls.  One scan sums both counts: row tiles in bits 0-19 (each expert's
+// count capped at 1023, which still exceeds any grid, so the sum stays below 2^20), jobs longer
+// than a dphi unit from bit 20 (at most E_loc <= 1024).
+__device__ __forceinline__ bool dx_first_ends_sooner(const DxShape& dx, int rows, int c, int cmax,
+                                                     int total, int share, int groups, int* sh) {
+  const int kd = dx.steps + kDwJobCost;
+  const int rt = (rows + dx.bm - 1) / dx.bm;
+  int both = 0;
+  block_exclusive_scan_1024((rt < 1023 ? rt : 1023) + (c > kd ? 1 << 20 : 0), sh, &both);
+  const int row_tiles = both & ((1 << 20) - 1), nlong = both >> 20;
+  const int64_t U = (int64_t)row_tiles * dx.tn, wgs = dx.wgs;
+  if (U > wgs || U == 0) return false;
+  const int64_t gsz = wgs / groups;
+  const int64_t dw_first = ((int64_t)share * dx.tpe + gsz - 1) / gsz + kd;
+  int64_t dx_first = ((int64_t)total * dx.tpe + U * kd + wgs - 1) / wgs;
+  dx_first = dx_first > kd ? dx_first : kd;
+  dx_first = dx_first > cmax ? dx_first : cmax;
+  if ((int64_t)nlong * dx.tpe > wgs - U && dx_first < kd + cmax) dx_first = kd + cmax;
+  return dx_first < dw_first;
+}
+
 __device__ __forceinline__ void dw_schedule_body(const int32_t* __restrict__ cmp_off, int E_loc,
                                                  int K_cap, int groups, int gpx,
-                                                 int32_t* __restrict__ sched, int allow_split) {
+                                                 int32_t* __restrict__ sched, int allow_split,
+                                                 const DxShape& dx) {
   constexpr int kG = kMaxXcd * kMaxGroupsPerXcd;
   __shared__ int rows[1024], by_rank[1024];
   __shared__ int load[kG], first[kG], count[kG];
   __shared__ int sh[40];
+  __shared__ int cmax;
   const int tid = threadIdx.x;
   int mine = 0;
   if (tid < E_loc) {
@@ -989,14 +1045,26 @@ __device__ __forceinline__ void dw_schedule_body(const int32_t* __restrict__ cmp
   const int T = total > 0 ? (total + groups - 1) / groups : 1;
   const int n2 = 2 * groups, q = r % n2, gs = q < groups ? q : n2 - 1 - q;
   if (e >= 0) atomicAdd(&load[gs], c);
+  if (r == 0) cmax = c;  // rank 0 holds the most rows, so the costliest job
   __syncthreads();
   int worst = 0;
   for (int g = 0; g < groups; ++g) worst = load[g] > worst ? load[g] : worst;
-  // store-bound (the second fused launch runs it with dynamic dW claims, which need no splits):
-  // the jobs' K steps (total - kDwJobCost * E_loc) sum to less than their fixed costs
-  const bool mix = total - kDwJobCost * E_loc < kDwJobCost * E_loc;
-  const bool fill = allow_split && !mix && (int64_t)worst * 4 > (int64_t)T * 5 &&
-                    groups - 1 <= kMaxDwSlots;
+  const bool split_pays = allow_split && (int64_t)worst * 4 > (int64_t)T * 5 &&
+                          groups - 1 <= kMaxDwSlots;
+  // dphi first (the second fused launch, with dynamic dW claims, which need no splits) when the
+  // products are store-bound: the jobs' K steps (total - kDwJobCost * E_loc) sum to less than
+  // their fixed costs; or when the one-launch form's dphi units fit in one round of the grid and
+  // starting them first is estimated to end sooner
+  // (flag 1: dW units claimed group by group, which spreads the heavy jobs among the light ones;
+  // flag 2: largest expert first, so that the jobs longer than a dphi unit start at once)
+  int mix = total - kDwJobCost * E_loc < kDwJobCost * E_loc ? 1 : 0;
+  // a job of cost c holds more than 32 (c - kDwJobCost - 1) rows, so the dphi units number at
+  // least tn * 32 * (total - (kDwJobCost + 1) * E_loc) / bm: when that exceeds the grid, skip
+  if (!mix && dx.wgs > 0 &&
+      (int64_t)dx.tn * kBK * (total - (kDwJobCost + 1) * E_loc) <= (int64_t)dx.wgs * dx.bm &&
+      dx_first_ends_sooner(dx, e >= 0 ? n : 0, c, cmax, total, split_pays ? T : worst, groups, sh))
+    mix = 2;
+  const bool fill = split_pays && !mix;
   const int64_t jpg = dw_jobs_per_group(E_loc);
   auto put = [&](int g, int idx, int kb, int kend, int slot) {
     int32_t* jb = sched + kDwHeader + (int64_t)g * jpg * 4 + 4 * idx;
@@ -1061,7 +1129,7 @@ __device__ __forceinline__ void dw_schedule_body(const int32_t* __restrict__ cmp
   if (tid == 0) {
     sched[0] = groups;
     sched[1] = gpx;
-    sched[3] = mix ? 1 : 0;
+    sched[3] = mix;
   }
   if (tid < groups) sched[4 + 3 * kMaxDwSlots + tid] = count[tid];
 }
@@ -1259,10 +1327,12 @@ __device__ __forceinline__ void dx_schedule_body(const int32_t* __restrict__ cmp
   if (tid == 0) tiles[0] = (int)(base_tiles < max_tiles ? base_tiles : max_tiles);
 }
 
+// dx: the one-launch form's dphi units of the same product, so that the separate dW call splits
+// experts exactly when the one-launch form does and both give the same bits.
 __global__ __launch_bounds__(1024) void dw_schedule(const int32_t* __restrict__ cmp_off, int E_loc,
                                                     int K_cap, int groups, int gpx,
-                                                    int32_t* __restrict__ sched) {
-  dw_schedule_body(cmp_off, E_loc, K_cap, groups, gpx, sched, 1);
+                                                    int32_t* __restrict__ sched, DxShape dx) {
+  dw_schedule_body(cmp_off, E_loc, K_cap, groups, gpx, sched, 1, dx);
 }
 
 __global__ __launch_bounds__(1024) void dx_schedule(const int32_t* __restrict__ cmp_off, int E_loc,
@@ -1281,9 +1351,9 @@ __global__ __launch_bounds__(1024) void gemm_schedules(const int32_t* __restrict
                                                        int64_t max_tiles,
                                                        int32_t* __restrict__ tiles,
                                                        int32_t* __restrict__ queue,
-                                                       int allow_split) {
+                                                       int allow_split, DxShape dx) {
   if (blockIdx.x == 0)
-    dw_schedule_body(cmp_off, E_loc, K_cap, groups, gpx, sched, allow_split);
+    dw_schedule_body(cmp_off, E_loc, K_cap, groups, gpx, sched, allow_split, dx);
   else
     dx_schedule_body(cmp_off, E_loc, K_cap, tm, max_tiles, tiles, queue);
 }
@@ -1342,12 +1412,19 @@ int groups_per_die(const lrm_problem& p, const Grid& g) {
   return 1;
 }
 
+// The dphi units of the one-launch form on the same grid (its dphi tile has the dW tile's shape).
+template <class C>
+DxShape dx_shape(const lrm_problem& p, const Grid& g) {
+  return DxShape{g.blocks, C::BM, (p.d + C::BN - 1) / C::BN, (p.h + kBK - 1) / kBK,
+                 ((p.h + C::BM - 1) / C::BM) * ((p.d + C::BN - 1) / C::BN)};
+}
+
 template <class C>
 void launch_dw_t(const lrm_problem& p, const void* Gc, const void* Phic, const int32_t* cmp_off,
                  int32_t* sched, float* dW, float* slots, const Grid& g, hipStream_t s) {
   const int gpx = groups_per_die<C>(p, g);
   hipLaunchKernelGGL(dw_schedule, dim3(1), dim3(kThreadsPerSchedule), 0, s, cmp_off, p.E_loc,
-                     p.K_cap, g.nxcd * gpx, gpx, sched);
+                     p.K_cap, g.nxcd * gpx, gpx, sched, dx_shape<C>(p, g));
   hipLaunchKernelGGL((dw_bf16<C, stages_for<C>()>), dim3(g.blocks), dim3(C::THREADS), 0, s,
                      (const uint16_t*)Gc, (const uint16_t*)Phic, sched, g.nxcd, p.E_loc, p.K_cap,
                      p.h, p.d, dW, slots);
@@ -1365,7 +1442,7 @@ void launch_fused_t(const lrm_problem& p, const void* Gc, const void* Phic, cons
   static_assert(kThreadsPerSchedule == 1024, "one block shape for both schedules");
   hipLaunchKernelGGL(gemm_schedules, dim3(2), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap,
                      g.nxcd * gpx, gpx, sched, CX::BM, max_tiles, tiles, queue,
-                     slots != nullptr ? 1 : 0);
+                     slots != nullptr ? 1 : 0, dx_shape<CW>(p, g));
   // without partial slots (the allocation-free entry) one launch runs every product
   const int solo = slots == nullptr ? 1 : 0;
   hipLaunchKernelGGL((gemm_fused<CW, CX, stages_for<CW>(), kLayer, 0>), dim3(g.blocks),

@@ -34,7 +34,7 @@ def build():
     return B.build(out=LIB, defines=("LRM_TIMELINE",), build_dir=OUT_DIR)
 
 
-def run(cfg: int, reps: int):
+def run(cfg: int, reps: int, rho=None):
     if not os.path.exists(LIB):
         raise SystemExit(f"{LIB} is missing: run `python -m backward_token_expert_amd.timeline build`")
     if ROOT not in sys.path:
@@ -51,7 +51,7 @@ def run(cfg: int, reps: int):
     sp = w.spec
     L_cap = sp.T * min(sp.k, sp.E_loc)
     P = lrm.make_problem(sp.T, sp.k, sp.E, sp.e_lo, sp.E_loc, sp.h, sp.d, sp.dtype, L_cap, L_cap)
-    pol = synth.policy(sp)
+    pol = synth.policy(sp, rho=rho)
     phi = np.concatenate([w.phi, np.zeros((L_cap - w.phi.shape[0], sp.d), w.phi.dtype)])
     idx, tw, g, ph, W = (to_device(a) for a in (w.topk_idx, w.topk_w, w.g, phi, w.W))
     b = path.DeviceBuffers(P)
@@ -64,9 +64,10 @@ def run(cfg: int, reps: int):
     co = to_host(b.cmp_off)
     nwg = torch.cuda.get_device_properties(0).multi_processor_count
     tn = (sp.d + 383) // 384 if sp.d >= 384 else None
-    print(f"# gemm_fused timeline -- {sp.name}, rho {sp.rho_num}/{sp.rho_den}\n")
+    rho_opt = f" --rho {pol['rho_num']}/{pol['rho_den']}" if rho is not None else ""
+    print(f"# gemm_fused timeline -- {sp.name}, rho {pol['rho_num']}/{pol['rho_den']}\n")
     print(f"Command (R = repository root):\n\n```\npython -m backward_token_expert_amd.timeline build\n"
-          f"python -m backward_token_expert_amd.timeline run --config {cfg} --reps {reps}\n```\n")
+          f"python -m backward_token_expert_amd.timeline run --config {cfg} --reps {reps}{rho_opt}\n```\n")
     print(f"K = {int(co[-1])}; per-expert K = {np.diff(co).tolist()}; {nwg} workgroups "
           f"(one per CU, dies = workgroup id mod 8). Times in us from the first workgroup's start.\n")
     print("| rep | call (events) | kernel span | dW share ends: min / median / max | exits: min / "
@@ -144,11 +145,13 @@ def main():
     r = sub.add_parser("run")
     r.add_argument("--config", type=int, default=2)
     r.add_argument("--reps", type=int, default=3)
+    r.add_argument("--rho", default=None, help="retention fraction num/den (default: the workload's)")
     a = ap.parse_args()
     if a.cmd == "build":
         print("built", build())
     else:
-        run(a.config, a.reps)
+        rho = tuple(int(v) for v in a.rho.split("/")) if a.rho else None
+        run(a.config, a.reps, rho)
 
 
 if __name__ == "__main__":

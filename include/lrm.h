@@ -353,9 +353,11 @@ lrm_status lrm_grouped_dx(const lrm_problem* problem, const void* Gc, const void
  * for bf16 inputs: workgroups whose share of the weight-gradient tiles ends early take
  * input-gradient tiles, so neither product leaves the device partly idle while the other still
  * has work (LRMoE Sec. 3.4: all expert-backward GEMMs run over the retained rows only).  When the
- * weight-gradient stores dominate (few retained rows per expert), the input-gradient tiles start
- * first and both kinds are taken from shared counters.  fp32 inputs run the two products one
- * after the other.  Requires Gc, Phic, W, dW, dphi 16-byte aligned.
+ * weight-gradient stores dominate (few retained rows per expert), or when the input-gradient
+ * tiles fit in one round of the device and starting them first is estimated to end sooner (a few
+ * experts holding most retained rows), the input-gradient tiles start first and both kinds are
+ * taken from shared counters.  fp32 inputs run the two products one after the other.  Requires
+ * Gc, Phic, W, dW, dphi 16-byte aligned.
  */
 lrm_status lrm_grouped_dw_dx(const lrm_problem* problem, const void* Gc, const void* Phic,
                              const void* W, const int32_t* cmp_off, float* dW, float* dphi,

@@ -627,6 +627,10 @@ GEMM_SHAPES = [
     # one expert far above the fair share, not store-bound: the dW schedule's contiguous fill
     # splits it along K into partial slots that the one-launch form's second launch adds up
     ([12000] + [40] * 15, 2048, 768),
+    # a few large experts whose dphi units fit in one round of the grid (90 units on 256
+    # workgroups): the schedule estimates that starting them first ends sooner, so the one-launch
+    # form takes the dphi-first order with dW tiles claimed largest expert first, unsplit
+    ([1568] * 5 + [702, 250, 76, 14, 10, 2, 3, 1, 0, 0, 0], 2048, 768),
 ]
 
 
