@@ -966,14 +966,19 @@ struct DxShape {
   int tpe;    // dW tiles per job
 };
 
-// The two orders of the one-launch form when its U dphi units fit in one round of the grid
-// (U <= wgs, so each workgroup runs at most one), estimated in K steps (a unit costs its steps
-// plus kDwJobCost; a dW job's cost c covers each of its tpe tiles):
+// The two orders of the one-launch form, estimated in K steps (a unit costs its steps plus
+// kDwJobCost; a dW job's cost c covers each of its tpe tiles).  When its U dphi units fit in one
+// round of the grid (U <= wgs, so each workgroup runs at most one):
 //  * dW first: a workgroup's part of its group's load (share: the fill's T or the snake deal's
 //    heaviest group), then one dphi unit;
 //  * dphi first: the whole work spread over the grid, but no less than one dphi unit or the
 //    costliest job, nor -- when more dW tiles than the free workgroups cost more than a dphi unit
 //    -- than a dphi unit followed by the costliest job.
+// With several rounds of dphi units both orders spread the same work; what differs is the end.
+// Dynamic dphi claims after the dW shares end with the last dphi units, about half a unit after
+// the mean (kd / 2); dphi first ends with dW tiles claimed largest expert first, which cost at
+// most cmax.  dphi first is taken when the difference, (kd - cmax) / 2, exceeds 2 % of the
+// spread work (it pays for the dW claims' looser L2 reuse).
 // Thread r holds the rank-r expert's `rows` and cost `c`, cmax is the largest cost; every thread
 // of the workgroup calls.  One scan sums both counts: row tiles in bits 0-19 (each expert's
 // count capped at 1023, which still exceeds any grid, so the sum stays below 2^20), jobs longer
@@ -986,7 +991,11 @@ __device__ __forceinline__ bool dx_first_ends_sooner(const DxShape& dx, int rows
   block_exclusive_scan_1024((rt < 1023 ? rt : 1023) + (c > kd ? 1 << 20 : 0), sh, &both);
   const int row_tiles = both & ((1 << 20) - 1), nlong = both >> 20;
   const int64_t U = (int64_t)row_tiles * dx.tn, wgs = dx.wgs;
-  if (U > wgs || U == 0) return false;
+  if (U == 0) return false;
+  if (U > wgs) {
+    const int64_t spread = ((int64_t)total * dx.tpe + U * kd) / wgs;
+    return (int64_t)(kd - cmax) * 25 > spread;
+  }
   const int64_t gsz = wgs / groups;
   const int64_t dw_first = ((int64_t)share * dx.tpe + gsz - 1) / gsz + kd;
   int64_t dx_first = ((int64_t)total * dx.tpe + U * kd + wgs - 1) / wgs;
@@ -1059,9 +1068,11 @@ __device__ __forceinline__ void dw_schedule_body(const int32_t* __restrict__ cmp
   // flag 2: largest expert first, so that the jobs longer than a dphi unit start at once)
   int mix = total - kDwJobCost * E_loc < kDwJobCost * E_loc ? 1 : 0;
   // a job of cost c holds more than 32 (c - kDwJobCost - 1) rows, so the dphi units number at
-  // least tn * 32 * (total - (kDwJobCost + 1) * E_loc) / bm: when that exceeds the grid, skip
+  // least tn * 32 * (total - (kDwJobCost + 1) * E_loc) / bm: when that exceeds the grid and no
+  // job costs less than a dphi unit, the estimate cannot pick dphi first and is skipped
   if (!mix && dx.wgs > 0 &&
-      (int64_t)dx.tn * kBK * (total - (kDwJobCost + 1) * E_loc) <= (int64_t)dx.wgs * dx.bm &&
+      ((int64_t)dx.tn * kBK * (total - (kDwJobCost + 1) * E_loc) <= (int64_t)dx.wgs * dx.bm ||
+       cmax < dx.steps + kDwJobCost) &&
       dx_first_ends_sooner(dx, e >= 0 ? n : 0, c, cmax, total, split_pays ? T : worst, groups, sh))
     mix = 2;
   const bool fill = split_pays && !mix;

@@ -631,6 +631,9 @@ GEMM_SHAPES = [
     # workgroups): the schedule estimates that starting them first ends sooner, so the one-launch
     # form takes the dphi-first order with dW tiles claimed largest expert first, unsplit
     ([1568] * 5 + [702, 250, 76, 14, 10, 2, 3, 1, 0, 0, 0], 2048, 768),
+    # many short experts, more dphi units than workgroups (280 on 256) and every dW job cheaper
+    # than a dphi unit: the dphi-first order again, now over more than one round
+    ([300] * 70, 2048, 768),
 ]
 
 
