@@ -1058,8 +1058,20 @@ __device__ __forceinline__ void dw_schedule_body(const int32_t* __restrict__ cmp
   __syncthreads();
   int worst = 0;
   for (int g = 0; g < groups; ++g) worst = load[g] > worst ? load[g] : worst;
-  const bool split_pays = allow_split && (int64_t)worst * 4 > (int64_t)T * 5 &&
-                          groups - 1 <= kMaxDwSlots;
+  bool split_pays = allow_split && (int64_t)worst * 4 > (int64_t)T * 5 &&
+                    groups - 1 <= kMaxDwSlots;
+  if (split_pays && dx.wgs > 0) {
+    // In the one-launch form the dphi units claimed after the dW shares absorb an uneven deal
+    // when the heaviest group's share, per workgroup, stays within 3/4 of the work a workgroup
+    // averages (dW and dphi spread over the grid): splitting would then only add the fix-up.
+    int row_tiles = 0;
+    const int rt = (e >= 0 ? n + dx.bm - 1 : 0) / dx.bm;
+    block_exclusive_scan_1024(rt < 1023 ? rt : 1023, sh, &row_tiles);
+    const int64_t spread = ((int64_t)total * dx.tpe +
+                            (int64_t)row_tiles * dx.tn * (dx.steps + kDwJobCost)) / dx.wgs;
+    const int64_t heavy = (int64_t)worst * dx.tpe / (dx.wgs / groups);
+    if (heavy * 4 <= spread * 3) split_pays = false;
+  }
   // dphi first (the second fused launch, with dynamic dW claims, which need no splits) when the
   // products are store-bound: the jobs' K steps (total - kDwJobCost * E_loc) sum to less than
   // their fixed costs; or when the one-launch form's dphi units fit in one round of the grid and
