@@ -604,7 +604,9 @@ def fractions(st, a, dtype, clock_mhz=None):
     out = {"score_select_compact_GBps": by / t_ssc / 1e9,
            "score_select_compact_hbm_frac": by / t_ssc / 1e9 / HBM_PEAK_GBS,
            "gemms_TFLOPs": fl / t_g / 1e12,
-           "gemms_mfma_frac": fl / t_g / 1e12 / MFMA_PEAK_TFLOPS[dtype]}
+           "gemms_mfma_frac": fl / t_g / 1e12 / MFMA_PEAK_TFLOPS[dtype],
+           # the GEMMs' algorithmic bytes per second: the bound when the dW stores dominate
+           "gemms_GBps": (a["dw"] + a["dx"]) / t_g / 1e9}
     if clock_mhz:
         out["gemms_mfma_frac_at_measured_clock"] = (
             fl / t_g / 1e12 / (MFMA_PEAK_TFLOPS[dtype] * clock_mhz / SPEC_CLOCK_MHZ))
@@ -739,7 +741,20 @@ def main():
             w1 = synth.make(1)
             legs["qwen3_share"] = leg(w1, synth.policy(w1.spec), args.leg_steps, 3, "lrm", fused,
                                       graph, flush, "rho 1/2 (cap)")
+            legs["qwen3_share_full"] = leg(w1, synth.policy(w1.spec, full=True), args.leg_steps,
+                                           3, "lrm", fused, graph, flush, "full retention")
             del w1
+        # every other workload at its own retention and at full retention
+        for cfg, key in ((0, "fp32_small"), (4, "whole_layer"), (5, "deepseek_v2_share")):
+            if cfg == args.config:
+                continue
+            wc = synth.make(cfg)
+            pc = synth.policy(wc.spec)
+            own = f"rho {pc['rho_num']}/{pc['rho_den']} (cap)"
+            legs[key] = [leg(wc, pc, args.leg_steps, 3, "lrm", fused, graph, flush, own),
+                         leg(wc, synth.policy(wc.spec, full=True), args.leg_steps, 3, "lrm",
+                             fused, graph, flush, "full retention")]
+            del wc
         w3 = synth.make(3)
         sweep = [leg(w3, synth.policy(w3.spec, full=True), args.leg_steps, 3, "lrm", fused,
                      graph, flush, "full retention")]
