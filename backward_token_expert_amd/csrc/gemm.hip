@@ -1223,17 +1223,50 @@ __device__ __forceinline__ void mma_step_f32(const float* __restrict__ sa,
   }
 }
 
+// dW, fp32: one workgroup per 64 x 64 tile of one job.  Without a schedule (sched == nullptr) the
+// job of blockIdx.z is expert blockIdx.z over its whole K range, written to dW.  With one,
+// blockIdx.z walks dw_schedule's job lists group after group: an expert, or a piece of one along
+// K whose partial sum goes to a slot that dw_fixup adds in piece order, so that one large expert
+// no longer sets the end of the launch.
 __global__ __launch_bounds__(kF32Threads) void dw_f32(const float* __restrict__ Gc,
                                                   const float* __restrict__ Phic,
                                                   const int32_t* __restrict__ cmp_off, int K_cap,
-                                                  int h, int d, float* __restrict__ dW) {
+                                                  int h, int d, float* __restrict__ dW,
+                                                  const int32_t* __restrict__ sched, int E_loc,
+                                                  float* __restrict__ slots) {
   __shared__ __attribute__((aligned(16))) float sa[2][BKF * PF];
   __shared__ __attribute__((aligned(16))) float sb[2][BKF * PF];
-  const int e = blockIdx.z, m0 = blockIdx.y * FBM, n0 = blockIdx.x * FBN;
+  const int m0 = blockIdx.y * FBM, n0 = blockIdx.x * FBN;
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave, wm = wv >> 1, wn = wv & 1;
-  int s = cmp_off[e], t = cmp_off[e + 1];
-  s = s < 0 ? 0 : (s > K_cap ? K_cap : s);
-  t = t < s ? s : (t > K_cap ? K_cap : t);
+  int e, s, t;
+  float* out;
+  if (sched == nullptr) {
+    e = blockIdx.z;
+    s = cmp_off[e];
+    t = cmp_off[e + 1];
+    s = s < 0 ? 0 : (s > K_cap ? K_cap : s);
+    t = t < s ? s : (t > K_cap ? K_cap : t);
+    out = dW + (int64_t)e * h * d;
+  } else {
+    const int G = sched[0];
+    int z = blockIdx.z, g = 0;
+    for (; g < G && g < kMaxXcd * kMaxGroupsPerXcd; ++g) {
+      const int c = sched[4 + 3 * kMaxDwSlots + g];
+      if (z < c) break;
+      z -= c;
+    }
+    if (g >= G || g >= kMaxXcd * kMaxGroupsPerXcd) return;  // past the last job
+    const int32_t* jb = sched + kDwHeader + (int64_t)g * dw_jobs_per_group(E_loc) * 4 + 4 * z;
+    e = jb[0];
+    s = jb[1];
+    t = jb[2];
+    const int slot = jb[3];
+    if (slot == -2) return;  // an empty piece of a split expert
+    // a record outside the buffers (never written so by dw_schedule) is skipped, not followed
+    if (e < 0 || e >= E_loc || s < 0 || t < s || t > K_cap || slot < -1 || slot >= kMaxDwSlots)
+      return;
+    out = slot < 0 ? dW + (int64_t)e * h * d : slots + (int64_t)slot * h * d;
+  }
   f32x16 acc[1][1];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[0][0][r] = 0.0f;
@@ -1256,16 +1289,26 @@ __global__ __launch_bounds__(kF32Threads) void dw_f32(const float* __restrict__ 
     if (kt + 1 < nk) st_kmn_f32(isA ? sa[cur ^ 1] : sb[cur ^ 1], blk, v);
     __syncthreads();
   }
-  store_acc<1, 1, 2>(dW + (int64_t)e * h * d, d, m0, h, n0, d, wm, wn, lane, acc);
+  store_acc<1, 1, 2>(out, d, m0, h, n0, d, wm, wn, lane, acc);
 }
 
+// dphi, fp32: one workgroup per 64 x 64 tile of the tile table.  With fix_sched set (both products
+// in one call, launched right after dw_f32) the workgroups first add the split experts' partial
+// slots into dW, dw_fixup's work, which saves that launch when nothing is split.
 __global__ __launch_bounds__(kF32Threads) void dx_f32(const float* __restrict__ Gc,
                                                   const float* __restrict__ W,
                                                   const int32_t* __restrict__ cmp_off,
                                                   const int32_t* __restrict__ tiles, int K_cap,
-                                                  int h, int d, float* __restrict__ dphi) {
+                                                  int h, int d, float* __restrict__ dphi,
+                                                  const int32_t* __restrict__ fix_sched, int E_loc,
+                                                  const float* __restrict__ slots,
+                                                  float* __restrict__ dW) {
   __shared__ __attribute__((aligned(16))) float sa[2][BKF * PF];
   __shared__ __attribute__((aligned(16))) float sb[2][BKF * PF];
+  if (fix_sched != nullptr)
+    fixup_split_experts(fix_sched, E_loc, h, d, slots, dW,
+                        ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * kF32Threads + threadIdx.x,
+                        (int64_t)gridDim.x * gridDim.y * kF32Threads);
   const int tile = blockIdx.x;
   if (tile >= tiles[0]) return;
   const int e = tiles[1 + 2 * tile], m0 = tiles[2 + 2 * tile];
@@ -1502,9 +1545,17 @@ hipError_t launch_dw(const lrm_problem& p, const void* Gc, const void* Phic, con
       default: launch_dw_t<Tile128_dW>(p, Gc, Phic, cmp_off, sched, dW, slots, g, s); break;
     }
   } else {
-    const dim3 grid((p.d + FBN - 1) / FBN, (p.h + FBM - 1) / FBM, p.E_loc);
+    // kMaxXcd groups share the cost; the contiguous fill splits an expert above 5/4 of a share
+    // into at most kMaxXcd - 1 extra pieces, so the jobs number at most E_loc + kMaxXcd - 1
+    int32_t* sched = (int32_t*)(ws + wl.order);
+    float* slots = (float*)(ws + wl.dwslots);
+    hipLaunchKernelGGL(dw_schedule, dim3(1), dim3(kThreadsPerSchedule), 0, s, cmp_off, p.E_loc,
+                       p.K_cap, kMaxXcd, 1, sched, DxShape{0, 1, 1, 0, 0});
+    const dim3 grid((p.d + FBN - 1) / FBN, (p.h + FBM - 1) / FBM, p.E_loc + kMaxXcd - 1);
     hipLaunchKernelGGL(dw_f32, grid, dim3(kF32Threads), 0, s, (const float*)Gc, (const float*)Phic,
-                       cmp_off, p.K_cap, p.h, p.d, dW);
+                       cmp_off, p.K_cap, p.h, p.d, dW, (const int32_t*)sched, p.E_loc, slots);
+    hipLaunchKernelGGL(dw_fixup, dim3(kFixupBlocks), dim3(256), 0, s, sched, p.E_loc, p.h, p.d,
+                       slots, dW);
   }
   return hipGetLastError();
 }
@@ -1530,7 +1581,8 @@ hipError_t launch_dx(const lrm_problem& p, const void* Gc, const void* W, const 
                        wl.max_tiles, tiles, nullptr);
     const dim3 grid((unsigned)wl.max_tiles, (p.d + FBN - 1) / FBN);
     hipLaunchKernelGGL(dx_f32, grid, dim3(kF32Threads), 0, s, (const float*)Gc, (const float*)W,
-                       cmp_off, tiles, p.K_cap, p.h, p.d, dphi);
+                       cmp_off, tiles, p.K_cap, p.h, p.d, dphi, (const int32_t*)nullptr, 0,
+                       (const float*)nullptr, (float*)nullptr);
   }
   return hipGetLastError();
 }
@@ -1556,8 +1608,22 @@ hipError_t launch_gemms_t(const lrm_problem& p, const void* Gc, const void* Phic
                           const int32_t* cmp_off, float* dW, float* dphi, char* ws,
                           const WsLayout& wl, hipStream_t s) {
   if (p.dtype != LRM_BF16) {
-    const hipError_t e = launch_dw(p, Gc, Phic, cmp_off, dW, ws, wl, s);
-    return e != hipSuccess ? e : launch_dx(p, Gc, W, cmp_off, dphi, ws, wl, s);
+    // fp32: both schedules in one launch, the dW jobs (experts split along K as the separate
+    // call splits them), then the dphi tiles, whose workgroups first add the partial slots
+    int32_t* sched = (int32_t*)(ws + wl.order);
+    int32_t* tiles = (int32_t*)(ws + wl.tiles);
+    float* slots = (float*)(ws + wl.dwslots);
+    hipLaunchKernelGGL(gemm_schedules, dim3(2), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap,
+                       kMaxXcd, 1, sched, FBM, wl.max_tiles, tiles, (int32_t*)nullptr, 1,
+                       DxShape{0, 1, 1, 0, 0});
+    const dim3 gw((p.d + FBN - 1) / FBN, (p.h + FBM - 1) / FBM, p.E_loc + kMaxXcd - 1);
+    hipLaunchKernelGGL(dw_f32, gw, dim3(kF32Threads), 0, s, (const float*)Gc, (const float*)Phic,
+                       cmp_off, p.K_cap, p.h, p.d, dW, (const int32_t*)sched, p.E_loc, slots);
+    const dim3 gx((unsigned)wl.max_tiles, (p.d + FBN - 1) / FBN);
+    hipLaunchKernelGGL(dx_f32, gx, dim3(kF32Threads), 0, s, (const float*)Gc, (const float*)W,
+                       cmp_off, tiles, p.K_cap, p.h, p.d, dphi, (const int32_t*)sched, p.E_loc,
+                       (const float*)slots, dW);
+    return hipGetLastError();
   }
   launch_fused_bf16<kLayer>(p, Gc, Phic, W, cmp_off, dW, dphi, (int32_t*)(ws + wl.order),
                             (int32_t*)(ws + wl.tiles), (int32_t*)(ws + wl.err) + kQueueWord,
@@ -1654,12 +1720,14 @@ hipError_t launch_gemms_noalloc(const lrm_problem& p, const void* Gc, const void
   } else {
     const dim3 gw((p.d + FBN - 1) / FBN, (p.h + FBM - 1) / FBM, p.E_loc);
     hipLaunchKernelGGL(dw_f32, gw, dim3(kF32Threads), 0, s, (const float*)Gc, (const float*)Phic,
-                       cmp_off, p.K_cap, p.h, p.d, dW);
+                       cmp_off, p.K_cap, p.h, p.d, dW, (const int32_t*)nullptr, p.E_loc,
+                       (float*)nullptr);
     hipLaunchKernelGGL(dx_schedule, dim3(1), dim3(1024), 0, s, cmp_off, p.E_loc, p.K_cap, FBM,
                        l.max_tiles, tiles, nullptr);
     const dim3 gx((unsigned)l.max_tiles, (p.d + FBN - 1) / FBN);
     hipLaunchKernelGGL(dx_f32, gx, dim3(kF32Threads), 0, s, (const float*)Gc, (const float*)W,
-                       cmp_off, tiles, p.K_cap, p.h, p.d, dphi);
+                       cmp_off, tiles, p.K_cap, p.h, p.d, dphi, (const int32_t*)nullptr, 0,
+                       (const float*)nullptr, (float*)nullptr);
   }
   return hipGetLastError();
 }

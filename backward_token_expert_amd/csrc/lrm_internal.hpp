@@ -72,7 +72,7 @@ inline WsLayout ws_layout(const lrm_problem& p) {
   w.inv = off;
   off = align_up(off + (size_t)P * 4, 256);
   w.dwslots = off;
-  if (p.dtype == LRM_BF16) off = align_up(off + (size_t)kMaxDwSlots * p.h * p.d * 4, 256);
+  off = align_up(off + (size_t)kMaxDwSlots * p.h * p.d * 4, 256);
   w.total = off;
   return w;
 }
