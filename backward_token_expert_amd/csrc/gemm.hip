@@ -880,14 +880,14 @@ __device__ __forceinline__ void fused_loop(const FusedArgs& a, volatile int* cla
 // operand's orientation), kPart 0.  Each workgroup runs its share of the dW units exactly as
 // dw_bf16 does, then claims dphi units one at a time: from its own die's contiguous range (a
 // counter per die in the workspace, reset by dx_schedule), and once that is exhausted from the
-// other dies' in turn.  A second launch of the same shape (kPart 1) follows it: for the products
-// dw_schedule flags (fused_loop's MIX: store-bound, or one round of dphi units) the first launch
-// returns at once and the
-// second runs the product; otherwise the second adds the split experts' partial slots (dw_fixup's
-// work) and returns.  Two specialised kernels instead of one with both loops keep the register
-// allocation of the common path as it is.  With solo set (no second launch) the first launch
-// runs every product the common way.  The workgroups whose dW share ends early (light groups) thus take more dphi units, and
-// dphi's last partial round is spread over whoever is free.  Each unit is computed whole by the
+// other dies' in turn.  The workgroups whose dW share ends early (light groups) thus take more
+// dphi units, and dphi's last partial round is spread over whoever is free.  A second launch of
+// the same shape (kPart 1) follows it: for the products dw_schedule flags (fused_loop's MIX:
+// store-bound, or an estimate that the dphi units should start first) the first launch returns
+// at once and the second runs the product; otherwise the second adds the split experts' partial
+// slots (dw_fixup's work) and returns.  Two specialised kernels instead of one with both loops
+// keep the register allocation of the common path as it is.  With solo set (no second launch)
+// the first launch runs every product the common way.  Each unit is computed whole by the
 // workgroup that claims it, in the same order as in dx_bf16, so results do not depend on which
 // workgroup runs it.  A claim tries every die once, so every workgroup leaves when all ranges are
 // exhausted.
@@ -1596,10 +1596,22 @@ void launch_fused_bf16(const lrm_problem& p, const void* Gc, const void* Phic, c
   static_assert(TileW_dX::BM == Tile128_dX::BM && TileW_dX::BM >= kDxTileM, "row tile");
   const int64_t max_tiles = ((int64_t)p.K_cap + TileW_dX::BM - 1) / TileW_dX::BM + p.E_loc;
   switch (pick_width(p.d)) {
-    case 0: launch_fused_t<TileW_dW, TileW_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
-    case 1: launch_fused_t<Tile256_dW, Tile256_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
-    case 2: launch_fused_t<Tile192_dW, Tile192_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
-    default: launch_fused_t<Tile128_dW, Tile128_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue, max_tiles, dW, slots, dphi, g, s); break;
+    case 0:
+      launch_fused_t<TileW_dW, TileW_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue,
+                                            max_tiles, dW, slots, dphi, g, s);
+      break;
+    case 1:
+      launch_fused_t<Tile256_dW, Tile256_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue,
+                                            max_tiles, dW, slots, dphi, g, s);
+      break;
+    case 2:
+      launch_fused_t<Tile192_dW, Tile192_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue,
+                                            max_tiles, dW, slots, dphi, g, s);
+      break;
+    default:
+      launch_fused_t<Tile128_dW, Tile128_dX, kLayer>(p, Gc, Phic, W, cmp_off, sched, tiles, queue,
+                                            max_tiles, dW, slots, dphi, g, s);
+      break;
   }
 }
 
