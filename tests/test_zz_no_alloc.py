@@ -63,10 +63,14 @@ def _check_pair(sp, P, b, inp):
 # store-bound: the workspace call runs it dphi-first with dW units claimed from one counter, the
 # allocation-free call in the common order, so the two orders are checked against each other.
 CASES = [(1, 4096, 1024, False), (0, 4096, 1024, False), (3, 8192, 2048, True),
-         (2, 1024, 512, False), (4, 4096, 1024, False)]
+         (2, 1024, 512, False), (4, 4096, 1024, False),
+         # fp32 at full retention: the workspace call splits the largest experts along K, the
+         # allocation-free one never does
+         (0, 4096, 2048, True)]
 
 
-@pytest.mark.parametrize("cfg,T1,T2,full", CASES, ids=[f"cfg{c[0]}" for c in CASES])
+@pytest.mark.parametrize("cfg,T1,T2,full", CASES,
+                         ids=[f"cfg{c[0]}{'-full' if c[3] else ''}" for c in CASES])
 def test_noalloc_equals_workspace_call_twice(cfg, T1, T2, full):
     for T in (T1, T2):
         sp, P, b, inp = _compacted(cfg, T, full)
