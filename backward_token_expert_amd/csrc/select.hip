@@ -11,13 +11,14 @@
 //   2. MSB-first radix select over bits 30..0 in digits of 12, 10 and 9 bits finds the q-th
 //      largest key T and how many keys equal to T must be kept; after the first digit the keys
 //      still in play are gathered into a short list that the later digits scan;
-//   3. each wavefront owns a contiguous run of rows: it compacts its rows with key >= T, in row
-//      order and marking the ties, into the front of its own run of the LDS stage; one barrier
-//      publishes the counts, and each wavefront then writes its kept rows (key > T, or key == T
-//      among the first `need` tied rows of the segment) from that short list with ballot prefix
-//      sums, so the stores cover consecutive lanes.
-// Segments longer than the LDS stage are read from global memory in every pass instead, and
-// their output pass counts first and then writes from the keys themselves.
+//   3. each thread owns a row of 32 consecutive keys: it counts those above T and equal to T, one
+//      scan of the packed counts places its kept rows (key > T, or key == T among the first
+//      `need` tied rows of the segment), it writes them in row order into the LDS stage, and the
+//      workgroup copies the q rows out with coalesced stores.
+// The stage is swizzled (stage_pos) so that both the strided passes and a thread's own row read
+// without bank conflicts.  Segments longer than the LDS stage are read from global memory in
+// every pass instead; their output pass gives each wavefront a contiguous run of rows, counts
+// first and then writes from the keys themselves with ballot prefix sums.
 #include "lrm_device.hpp"
 #include "lrm_internal.hpp"
 
@@ -33,6 +34,13 @@ constexpr int kMaxCand = kMaxBins - kCandBase;
 constexpr int kBatch = 8;         // keys a thread loads before using them (strided passes)
 constexpr int kStageBatch = 32;   // keys a thread loads before staging them (one pass for 32768)
 constexpr int kOutBatch = 4;      // 64-key groups a wavefront loads ahead in the output pass
+
+// Position of key i in the stage: rows of 32 keys, the column XOR-ed with the row (mod 32).  A
+// wavefront reading 64 consecutive keys touches two rows, each a permutation of one half of the
+// 64 banks; a thread reading its own row of 32 keys shares a bank with one other lane at most.
+__device__ __forceinline__ int stage_pos(int i) {
+  return (i & ~31) | ((i & 31) ^ ((i >> 5) & 31));
+}
 
 struct SelectSmem {
   uint32_t keys[kLdsKeys];
@@ -53,7 +61,9 @@ __device__ __forceinline__ void select_segment(SelectSmem& sm, const uint32_t* _
   uint32_t* sm_cand = (uint32_t*)(sm.hist + kCandBase);
   // A NaN or negative score is flagged and ranked as +0, so every key has its sign bit clear.
   auto sanitize = [](uint32_t v) -> uint32_t { return v > 0x7F800000u ? 0u : v; };
-  auto key_at = [&](int i) -> uint32_t { return kStaged ? sm.keys[i] : sanitize(src[i]); };
+  auto key_at = [&](int i) -> uint32_t {
+    return kStaged ? sm.keys[stage_pos(i)] : sanitize(src[i]);
+  };
 
   for (int i = tid; i < kMaxBins; i += kThreads) sm.hist[i] = 0;
   if (tid == 0) sm.ncand = 0;
@@ -75,7 +85,7 @@ __device__ __forceinline__ void select_segment(SelectSmem& sm, const uint32_t* _
       if (i < n) {
         bad |= v[j] > 0x7F800000u;
         const uint32_t k = sanitize(v[j]);
-        if (kStaged) sm.keys[i] = k;
+        if (kStaged) sm.keys[stage_pos(i)] = k;
         atomicAdd(&sm.hist[k >> 19], 1);
       }
     }
@@ -182,57 +192,68 @@ __device__ __forceinline__ void select_segment(SelectSmem& sm, const uint32_t* _
   const uint32_t thr = prefix;
   const int need = rank;  // keys equal to thr that are kept, first in row order
 
-  // Ordered output: wavefront w owns the contiguous rows [w*chunk, (w+1)*chunk).  After one
-  // barrier every wave knows how many rows the waves before it keep and how many tied keys they
-  // hold, and writes its kept rows in row order with ballot prefix sums (no further barriers).
+  if constexpr (kStaged) {
+    // Ordered output, thread-contiguous: thread t owns keys 32t .. 32t+31 (one row of the
+    // stage).  One scan of the packed counts (keys above thr in the high half, ties in the low
+    // half: fewer than q keys lie above thr, so the sum stays below 2^31) gives each thread the
+    // kept keys and the ties before it; it then writes its own kept rows in row order.
+    const int i0 = tid * 32;
+    uint32_t kv[32];
+    int n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const int i = i0 + c;
+      kv[c] = i < n ? sm.keys[stage_pos(i)] : 0u;
+      n_gt += (i < n && kv[c] > thr) ? 1 : 0;
+      n_eq += (i < n && kv[c] == thr) ? 1 : 0;
+    }
+    int both = 0;
+    const int before = block_exclusive_scan_1024((n_gt << 16) | n_eq, sm.wsum, &both);
+    const int eq_before = before & 0xFFFF;
+    int pos = (before >> 16) + (eq_before < need ? eq_before : need);
+    int ties = eq_before;
+    // the scan's barriers follow every read of the stage, which now holds the output
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const int i = i0 + c;
+      const bool valid = i < n;
+      const bool is_eq = valid && kv[c] == thr;
+      const bool keep = (valid && kv[c] > thr) || (is_eq && ties < need);
+      ties += is_eq ? 1 : 0;
+      if (keep) {
+        if (pos < q) sm.keys[pos] = (uint32_t)(r0 + i);
+        ++pos;
+      }
+    }
+    __syncthreads();
+    for (int j = tid; j < q; j += kThreads) sel_row[o0 + j] = (int32_t)sm.keys[j];
+    return;
+  }
+
+  // Ordered output of a segment read from global memory: wavefront w owns the contiguous rows
+  // [w*chunk, (w+1)*chunk).  It counts its kept and tied keys; after one barrier every wave knows
+  // how many rows the waves before it keep and how many tied keys they hold, and writes its kept
+  // rows in row order with ballot prefix sums (no further barriers).
   const int chunk = ((n + kWaves - 1) / kWaves + kWave - 1) / kWave * kWave;
   const int c0 = w * chunk < n ? w * chunk : n;
   const int c1 = c0 + chunk < n ? c0 + chunk : n;
   int n_eq = 0, n_gt = 0;
-  if constexpr (kStaged) {
-    // Compact the rows with key >= thr, in row order, into the front of this wave's own run of
-    // the stage: offset i, bit 31 set for a tie.  A slot rewritten lies at or before the group
-    // being read, whose keys are already in registers; later groups are untouched.
-    for (int base = c0; base < c1; base += kOutBatch * kWave) {
-      uint32_t v[kOutBatch];
+  for (int base = c0; base < c1; base += kOutBatch * kWave) {
+    uint32_t v[kOutBatch];
 #pragma unroll
-      for (int u = 0; u < kOutBatch; ++u) {
-        const int i = base + u * kWave + lane;
-        v[u] = i < c1 ? sm.keys[i] : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < kOutBatch; ++u) {
-        const int i = base + u * kWave + lane;
-        const bool valid = i < c1;
-        const bool is_eq = valid && v[u] == thr;
-        const bool cand = is_eq || (valid && v[u] > thr);
-        const uint64_t bc = ballot(cand);
-        if (cand)
-          sm.keys[c0 + n_gt + n_eq + __builtin_popcountll(bc & lt)] =
-              (uint32_t)i | (is_eq ? 0x80000000u : 0u);
-        const int ne = __builtin_popcountll(ballot(is_eq));
-        n_eq += ne;
-        n_gt += __builtin_popcountll(bc) - ne;
-      }
+    for (int u = 0; u < kOutBatch; ++u) {
+      const int i = base + u * kWave + lane;
+      v[u] = i < c1 ? key_at(i) : 0u;
     }
-  } else {
-    for (int base = c0; base < c1; base += kOutBatch * kWave) {
-      uint32_t v[kOutBatch];
 #pragma unroll
-      for (int u = 0; u < kOutBatch; ++u) {
-        const int i = base + u * kWave + lane;
-        v[u] = i < c1 ? key_at(i) : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < kOutBatch; ++u) {
-        const bool valid = base + u * kWave + lane < c1;
-        n_eq += valid && v[u] == thr;
-        n_gt += valid && v[u] > thr;
-      }
+    for (int u = 0; u < kOutBatch; ++u) {
+      const bool valid = base + u * kWave + lane < c1;
+      n_eq += valid && v[u] == thr;
+      n_gt += valid && v[u] > thr;
     }
-    n_eq = wave_sum_int(n_eq);
-    n_gt = wave_sum_int(n_gt);
   }
+  n_eq = wave_sum_int(n_eq);
+  n_gt = wave_sum_int(n_gt);
   if (lane == 0) {
     sm.weq[w] = n_eq;
     sm.wkeep[w] = n_gt;
@@ -246,46 +267,26 @@ __device__ __forceinline__ void select_segment(SelectSmem& sm, const uint32_t* _
     pos += sm.wkeep[x] + tied;
     eq_before += e_x;
   }
-  if constexpr (kStaged) {
-    // This wave keeps its first t_w ties; its list holds n_gt + n_eq entries in row order.
-    int t_w = need - eq_before;
-    t_w = t_w < 0 ? 0 : (t_w > n_eq ? n_eq : t_w);
-    const int m = n_gt + n_eq;
-    int ties = 0;
-    for (int j = 0; j < m; j += kWave) {
-      const bool valid = j + lane < m;
-      const uint32_t x = valid ? sm.keys[c0 + j + lane] : 0u;
-      const bool tie = valid && (x >> 31);
-      const uint64_t bt = ballot(tie);
-      const bool keep = valid && (!tie || ties + __builtin_popcountll(bt & lt) < t_w);
+  for (int base = c0; base < c1; base += kOutBatch * kWave) {
+    uint32_t v[kOutBatch];
+#pragma unroll
+    for (int u = 0; u < kOutBatch; ++u) {
+      const int i = base + u * kWave + lane;
+      v[u] = i < c1 ? key_at(i) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kOutBatch; ++u) {
+      const int i = base + u * kWave + lane;
+      const bool valid = i < c1;
+      const bool is_eq = valid && v[u] == thr;
+      const uint64_t beq = ballot(is_eq);
+      const bool keep =
+          (valid && v[u] > thr) || (is_eq && eq_before + __builtin_popcountll(beq & lt) < need);
       const uint64_t bk = ballot(keep);
       const int at = pos + __builtin_popcountll(bk & lt);
-      if (keep && at < q) sel_row[o0 + at] = r0 + (int)(x & 0x7FFFFFFFu);
+      if (keep && at < q) sel_row[o0 + at] = r0 + i;
       pos += __builtin_popcountll(bk);
-      ties += __builtin_popcountll(bt);
-    }
-  } else {
-    for (int base = c0; base < c1; base += kOutBatch * kWave) {
-      uint32_t v[kOutBatch];
-#pragma unroll
-      for (int u = 0; u < kOutBatch; ++u) {
-        const int i = base + u * kWave + lane;
-        v[u] = i < c1 ? key_at(i) : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < kOutBatch; ++u) {
-        const int i = base + u * kWave + lane;
-        const bool valid = i < c1;
-        const bool is_eq = valid && v[u] == thr;
-        const uint64_t beq = ballot(is_eq);
-        const bool keep =
-            (valid && v[u] > thr) || (is_eq && eq_before + __builtin_popcountll(beq & lt) < need);
-        const uint64_t bk = ballot(keep);
-        const int at = pos + __builtin_popcountll(bk & lt);
-        if (keep && at < q) sel_row[o0 + at] = r0 + i;
-        pos += __builtin_popcountll(bk);
-        eq_before += __builtin_popcountll(beq);
-      }
+      eq_before += __builtin_popcountll(beq);
     }
   }
 }
